@@ -1,0 +1,465 @@
+"""Pins for the CPU oracle: values the pages print, closed forms, brute force
+on tiny inputs, library special cases and structural invariants.
+
+Each test is chosen so that a plausible slip in the oracle (a dropped term, a
+wrong sign or index, a transposed operand, the wrong GQA grouping, a mask off
+by one, a wrong block lookup) fails at least one of them.
+"""
+import json
+import math
+import os
+import random
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ----------------------------------------------------------------------------
+# slot mapping
+# ----------------------------------------------------------------------------
+def test_slot_worked_example():
+    g = _golden("slot_example.json")
+    bt = np.array([g["block_table_row"]], dtype=np.int32)
+    # request 0 schedules one token at absolute position 25
+    s = oracle.slot_mapping(bt, [1], [g["position"]], g["block_size"])
+    assert s.dtype == np.int64
+    assert int(s[0]) == g["slot"]
+    assert int(s[0]) // g["block_size"] == g["physical_block"]
+    assert int(s[0]) % g["block_size"] == g["offset"]
+
+
+def _enumerated_slots(row, nblocks, B):
+    """Independent formulation: list every slot of the request's blocks in
+    logical order; position p is the p-th entry."""
+    out = []
+    for blk in row[:nblocks]:
+        for off in range(B):
+            out.append(int(blk) * B + off)
+    return out
+
+
+@pytest.mark.parametrize("B", [1, 2, 4, 16])
+def test_slot_mapping_brute_force(B):
+    rng = random.Random(11 + B)
+    R = 5
+    M = 12
+    perm = list(range(R * M))
+    rng.shuffle(perm)
+    bt = np.array(perm, dtype=np.int32).reshape(R, M)
+    qlens, comp = [], []
+    for r in range(R):
+        L = rng.randint(1, M * B)
+        q = rng.randint(0, L)
+        qlens.append(q)
+        comp.append(L - q)
+    got = oracle.slot_mapping(bt, qlens, comp, B)
+    want = []
+    for r in range(R):
+        L = qlens[r] + comp[r]
+        slots = _enumerated_slots(bt[r], -(-L // B), B)
+        want.extend(slots[comp[r]:L])
+    assert got.tolist() == want
+
+
+def test_block_table_examples_map_positions():
+    g = _golden("block_table_examples.json")
+    # P5: pi = [7, 2, 9]; with B = 4 the request's positions 0..11 land in
+    # blocks 7,7,7,7,2,2,2,2,9,9,9,9
+    bt = np.array([g["p5_pi"]], dtype=np.int32)
+    s = oracle.slot_mapping(bt, [12], [0], 4)
+    assert (s // 4).tolist() == [7] * 4 + [2] * 4 + [9] * 4
+    assert (s % 4).tolist() == [0, 1, 2, 3] * 3
+    # P1: request 0 [5, 8, 12], request 1 [3, 7], B = 16, one decode token each
+    t = g["p1_tables"]
+    bt = np.array([t[0], t[1] + [-1]], dtype=np.int32)
+    s = oracle.slot_mapping(bt, [1, 1], [40, 20], 16)
+    assert s.tolist() == [12 * 16 + 8, 7 * 16 + 4]
+
+
+# ----------------------------------------------------------------------------
+# write / gather
+# ----------------------------------------------------------------------------
+def test_write_kv_bitexact_and_skip():
+    rng = np.random.default_rng(3)
+    nb, B, Hkv, D = 6, 4, 2, 8
+    kc = rng.integers(0, 65535, size=(nb, B, Hkv, D), dtype=np.uint16)
+    vc = kc.copy() ^ np.uint16(0x5555)
+    k0, v0 = kc.copy(), vc.copy()
+    key = rng.integers(0, 65535, size=(4, Hkv, D), dtype=np.uint16)
+    val = rng.integers(0, 65535, size=(4, Hkv, D), dtype=np.uint16)
+    slots = np.array([5, -1, 23, 0], dtype=np.int64)
+    oracle.write_kv(kc, vc, key, val, slots, B)
+    assert np.array_equal(kc[1, 1], key[0]) and np.array_equal(vc[1, 1], val[0])
+    assert np.array_equal(kc[5, 3], key[2]) and np.array_equal(vc[5, 3], val[2])
+    assert np.array_equal(kc[0, 0], key[3])
+    touched = np.zeros((nb, B), dtype=bool)
+    touched[1, 1] = touched[5, 3] = touched[0, 0] = True
+    assert np.array_equal(kc[~touched], k0[~touched])
+    assert np.array_equal(vc[~touched], v0[~touched])
+
+
+def test_write_kv_rejects_duplicates_and_overflow():
+    kc = np.zeros((2, 4, 1, 2), np.float32)
+    vc = kc.copy()
+    x = np.ones((2, 1, 2), np.float32)
+    with pytest.raises(ValueError):
+        oracle.write_kv(kc, vc, x, x, np.array([3, 3]), 4)
+    with pytest.raises(IndexError):
+        oracle.write_kv(kc, vc, x[:1], x[:1], np.array([8]), 4)
+
+
+def test_gather_brute_force():
+    rng = np.random.default_rng(5)
+    nb, B, Hkv, D = 9, 4, 2, 3
+    cache = rng.standard_normal((nb, B, Hkv, D)).astype(np.float32)
+    row = np.array([7, 2, 5, -1], dtype=np.int32)
+    L = 10
+    got = oracle.gather_kv(cache, row, L, B)
+    slots = _enumerated_slots(row, 3, B)
+    for p in range(L):
+        blk, off = divmod(slots[p], B)
+        assert np.array_equal(got[p], cache[blk, off])
+
+
+# ----------------------------------------------------------------------------
+# block accounting and preemption accounting
+# ----------------------------------------------------------------------------
+def _allocate_token_by_token(length, B):
+    """Brute force: append tokens one at a time, opening a new block whenever
+    the current one is full."""
+    blocks, used_in_last = 0, B
+    for _ in range(length):
+        if used_in_last == B:
+            blocks += 1
+            used_in_last = 0
+        used_in_last += 1
+    return blocks
+
+
+def test_tail_waste_table():
+    g = _golden("tail_waste.json")
+    lengths = g["lengths"]
+    for row in g["rows"]:
+        acc = oracle.block_accounting(lengths, row["block"])
+        assert acc["entries"] == row["entries"]
+        assert acc["allocated"] == row["allocated"]
+        assert acc["waste"] == row["waste"]
+        assert acc["blocks"] == [_allocate_token_by_token(t, row["block"]) for t in lengths]
+        for w in acc["tail_waste"]:
+            assert 0 <= w < row["block"]
+    assert len(lengths) * g["declared_max"] == g["contiguous_max_reservation_slots"]
+
+
+@pytest.mark.parametrize("B", [1, 3, 16, 32])
+def test_block_accounting_brute_force(B):
+    rng = random.Random(B)
+    lengths = [rng.randint(1, 500) for _ in range(20)]
+    acc = oracle.block_accounting(lengths, B)
+    assert acc["blocks"] == [_allocate_token_by_token(t, B) for t in lengths]
+    assert acc["allocated"] - sum(lengths) == acc["waste"]
+
+
+def test_preemption_accounting_golden():
+    g = _golden("preemption_accounting.json")
+    a = oracle.preemption_accounting(g["cached_tokens"], g["block_size"],
+                                     g["kv_bytes_per_token"], g["bandwidth_gbps"])
+    assert a["released_blocks"] == g["released_blocks"]
+    assert a["recompute_tokens"] == g["recompute_tokens"]
+    assert round(a["swap_roundtrip_ms"], g["swap_roundtrip_ms_digits"]) == g["swap_roundtrip_ms_approx"]
+
+
+def test_kv_bytes_per_token_matches_cache_layout():
+    # one slot of the whole-model cache [layers, 2, blocks, block_size, Hkv, D]
+    for L, Hkv, D, dt in [(32, 8, 128, np.uint16), (1, 2, 64, np.float32), (80, 8, 128, np.uint16)]:
+        slot = np.zeros((L, 2, 1, 1, Hkv, D), dtype=dt)
+        assert oracle.kv_bytes_per_token(L, Hkv, D, np.dtype(dt).itemsize) == slot.nbytes
+
+
+# ----------------------------------------------------------------------------
+# attention: brute force, library special cases, closed forms, invariants
+# ----------------------------------------------------------------------------
+def _random_step(rng, R, Hq, Hkv, D, B, maxlen, nb_extra=3, dtype="f32"):
+    lens = [int(rng.integers(1, maxlen + 1)) for _ in range(R)]
+    qlens = [int(rng.integers(1, L + 1)) for L in lens]
+    comp = [L - q for L, q in zip(lens, qlens)]
+    nblk = [-(-L // B) for L in lens]
+    nb = sum(nblk) + nb_extra
+    perm = rng.permutation(nb)
+    M = max(nblk)
+    bt = np.full((R, M), -1, dtype=np.int32)
+    pos = 0
+    for r in range(R):
+        bt[r, :nblk[r]] = perm[pos:pos + nblk[r]]
+        pos += nblk[r]
+    qsl = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    T = int(qsl[-1])
+    if dtype == "f32":
+        kc = rng.standard_normal((nb, B, Hkv, D)).astype(np.float32)
+        vc = rng.standard_normal((nb, B, Hkv, D)).astype(np.float32)
+        q = rng.standard_normal((T, Hq, D)).astype(np.float32)
+    else:
+        f = lambda shape: (rng.standard_normal(shape).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        kc, vc, q = f((nb, B, Hkv, D)), f((nb, B, Hkv, D)), f((T, Hq, D))
+    return dict(lens=lens, qlens=qlens, comp=comp, bt=bt, qsl=qsl, kc=kc, vc=vc, q=q, nb=nb)
+
+
+def _brute_attention(st, Hq, Hkv, D, B, scale, dtype):
+    """Scalar loops: position p of request r is read from block
+    bt[r][p // B] offset p % B; query head h uses kv head h // (Hq // Hkv)."""
+    G = Hq // Hkv
+    conv = (lambda x: float(x)) if dtype == "f32" else (
+        lambda x: float(np.array([int(x) << 16], dtype=np.uint32).view(np.float32)[0]))
+    T = int(st["qsl"][-1])
+    out = np.zeros((T, Hq, D))
+    for r in range(len(st["lens"])):
+        a = int(st["qsl"][r])
+        for i in range(st["qlens"][r]):
+            t = a + i
+            qpos = st["comp"][r] + i
+            for h in range(Hq):
+                g = h // G
+                scores = []
+                for j in range(qpos + 1):
+                    blk = int(st["bt"][r][j // B])
+                    off = j % B
+                    s = 0.0
+                    for d in range(D):
+                        s += conv(st["q"][t, h, d]) * conv(st["kc"][blk, off, g, d])
+                    scores.append(s * scale)
+                mx = max(scores)
+                ws = [math.exp(s - mx) for s in scores]
+                tot = sum(ws)
+                for d in range(D):
+                    acc = 0.0
+                    for j in range(qpos + 1):
+                        blk = int(st["bt"][r][j // B])
+                        acc += ws[j] * conv(st["vc"][blk, j % B, g, d])
+                    out[t, h, d] = acc / tot
+    return out
+
+
+@pytest.mark.parametrize("B,dtype", [(1, "f32"), (2, "bf16"), (4, "f32"), (16, "bf16")])
+def test_attention_brute_force(B, dtype):
+    rng = np.random.default_rng(100 + B)
+    Hq, Hkv, D = 4, 2, 5
+    st = _random_step(rng, 3, Hq, Hkv, D, B, 40 if B > 1 else 20, dtype=dtype)
+    scale = 1 / math.sqrt(D)
+    got, _ = oracle.attention(st["q"], st["kc"], st["vc"], st["bt"], st["qsl"], st["lens"],
+                              st["comp"], scale, B, dtype)
+    want = _brute_attention(st, Hq, Hkv, D, B, scale, dtype)
+    assert np.max(np.abs(got - want)) <= 1e-12
+
+
+def _sdpa_reference(qf, kf, vf, c):
+    """torch CPU fp64 scaled_dot_product_attention with a lower-right causal
+    bias (query i of n at absolute position c + i sees keys 0..c+i) and torch's
+    own GQA head grouping."""
+    import torch
+    import torch.nn.functional as F
+    from torch.nn.attention.bias import causal_lower_right
+    q = torch.from_numpy(qf).permute(1, 0, 2)[None]        # [1, Hq, n, D]
+    k = torch.from_numpy(kf).permute(1, 0, 2)[None]
+    v = torch.from_numpy(vf).permute(1, 0, 2)[None]
+    n, L = qf.shape[0], kf.shape[0]
+    assert L == c + n
+    mask = causal_lower_right(n, L)
+    o = F.scaled_dot_product_attention(q, k, v, attn_mask=mask, enable_gqa=True)
+    return o[0].permute(1, 0, 2).numpy()
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 2), (8, 1), (6, 3)])
+def test_attention_matches_torch_sdpa(Hq, Hkv):
+    rng = np.random.default_rng(Hq * 10 + Hkv)
+    D, B = 16, 4
+    st = _random_step(rng, 4, Hq, Hkv, D, B, 37)
+    scale = 1 / math.sqrt(D)
+    got, _ = oracle.attention(st["q"], st["kc"], st["vc"], st["bt"], st["qsl"], st["lens"],
+                              st["comp"], scale, B, "f32")
+    for r in range(4):
+        a, b = st["qsl"][r], st["qsl"][r + 1]
+        K = oracle.gather_kv(st["kc"], st["bt"][r], st["lens"][r], B).astype(np.float64)
+        V = oracle.gather_kv(st["vc"], st["bt"][r], st["lens"][r], B).astype(np.float64)
+        ref = _sdpa_reference(st["q"][a:b].astype(np.float64), K, V, st["comp"][r])
+        assert np.allclose(got[a:b], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_chunked_trace_and_equivalence():
+    g = _golden("chunk_trace.json")
+    rng = np.random.default_rng(127)
+    shape = tuple(g["shape"])
+    q = rng.standard_normal(shape)
+    k = rng.standard_normal(shape)
+    v = rng.standard_normal(shape)
+    scale = 1 / math.sqrt(shape[-1])
+    full = oracle.dense_causal(q, k, v, scale)
+    ch, trace = oracle.chunked_causal(q, k, v, g["chunk"], scale)
+    assert [[a, b, list(shp)] for a, b, shp in trace] == g["trace"]
+    assert np.allclose(ch, full, rtol=g["rtol"], atol=g["atol"])
+    for chunk in [1, 2, 5, 7, 50]:
+        ch, _ = oracle.chunked_causal(q, k, v, chunk, scale)
+        assert np.max(np.abs(ch - full)) < 1e-13
+
+
+def test_chunked_prefill_through_paged_cache_equals_full():
+    """A prompt run as chunks (each chunk a step with num_computed = chunk
+    start) through the paged cache equals the one-shot prefill."""
+    rng = np.random.default_rng(9)
+    Hq, Hkv, D, B, T = 4, 2, 8, 4, 23
+    nb = 8
+    perm = rng.permutation(nb)
+    bt = perm[: -(-T // B)][None].astype(np.int32)
+    kc = np.full((nb, B, Hkv, D), np.nan, np.float32)
+    vc = kc.copy()
+    q = rng.standard_normal((T, Hq, D)).astype(np.float32)
+    k = rng.standard_normal((T, Hkv, D)).astype(np.float32)
+    v = rng.standard_normal((T, Hkv, D)).astype(np.float32)
+    scale = 0.3
+    kc1, vc1 = kc.copy(), vc.copy()
+    oracle.write_kv(kc1, vc1, k, v, oracle.slot_mapping(bt, [T], [0], B), B)
+    full, _ = oracle.attention(q, kc1, vc1, bt, [0, T], [T], [0], scale, B, "f32")
+    outs = []
+    for a in range(0, T, 5):
+        b = min(a + 5, T)
+        oracle.write_kv(kc, vc, k[a:b], v[a:b], oracle.slot_mapping(bt, [b - a], [a], B), B)
+        o, _ = oracle.attention(q[a:b], kc, vc, bt, [0, b - a], [b], [a], scale, B, "f32")
+        outs.append(o)
+    assert np.max(np.abs(np.concatenate(outs) - full)) < 1e-13
+
+
+def test_special_cases_closed_form():
+    rng = np.random.default_rng(4)
+    Hq, Hkv, D, B = 4, 2, 6, 4
+    # L = 1: the only visible key is position 0, softmax weight 1 -> out = v0
+    kc = rng.standard_normal((3, B, Hkv, D)).astype(np.float32)
+    vc = rng.standard_normal((3, B, Hkv, D)).astype(np.float32)
+    bt = np.array([[2]], dtype=np.int32)
+    q = rng.standard_normal((1, Hq, D)).astype(np.float32)
+    out, lse = oracle.attention(q, kc, vc, bt, [0, 1], [1], [0], 0.7, B, "f32")
+    for h in range(Hq):
+        assert np.array_equal(out[0, h], vc[2, 0, h // 2].astype(np.float64))
+        s = 0.7 * float(q[0, h].astype(np.float64) @ kc[2, 0, h // 2].astype(np.float64))
+        assert abs(lse[0, h] - s) < 1e-12
+    # all keys equal -> uniform weights -> mean of the visible V rows
+    kc[:] = kc[0, 0]
+    out, lse = oracle.attention(q, kc, vc, np.array([[1, 0, 2]], np.int32), [0, 1], [10], [9],
+                                1.0, B, "f32")
+    vis = np.concatenate([vc[1], vc[0], vc[2]])[:10].astype(np.float64)
+    for h in range(Hq):
+        assert np.allclose(out[0, h], vis[:, h // 2].mean(axis=0), atol=1e-12)
+    # GQA grouping: V of kv head g is the constant g -> query head h returns h // G
+    vc2 = np.zeros_like(vc)
+    for g in range(Hkv):
+        vc2[:, :, g, :] = g
+    out, _ = oracle.attention(q, kc, vc2, np.array([[1, 0, 2]], np.int32), [0, 1], [10], [9],
+                              1.0, B, "f32")
+    for h in range(Hq):
+        assert np.all(out[0, h] == h // 2)
+    # one dominant score -> output is (almost exactly) that key's V row
+    kc3 = np.zeros_like(kc)
+    qd = np.zeros((1, Hq, D), np.float32)
+    qd[0, :, 0] = 1.0
+    kc3[0, 2, :, 0] = 1000.0     # block 0 is logical block 1: position 4 + 2 = 6
+    out, _ = oracle.attention(qd, kc3, vc, np.array([[1, 0, 2]], np.int32), [0, 1], [10], [9],
+                              1.0, B, "f32")
+    for h in range(Hq):
+        assert np.allclose(out[0, h], vc[0, 2, h // 2], atol=1e-12)
+
+
+def test_mask_is_causal_at_absolute_positions():
+    """Changing a key beyond a query's absolute position leaves that query's
+    output unchanged; changing one at or before it changes it."""
+    rng = np.random.default_rng(8)
+    Hq, Hkv, D, B = 2, 1, 4, 4
+    st = _random_step(rng, 1, Hq, Hkv, D, B, 20, nb_extra=0)
+    L, c = st["lens"][0], st["comp"][0]
+    if st["qlens"][0] < 2:
+        st["qlens"][0] = 2
+        c = L - 2
+        st["comp"][0] = c
+        st["qsl"] = np.array([0, 2], np.int32)
+        st["q"] = rng.standard_normal((2, Hq, D)).astype(np.float32)
+    base, _ = oracle.attention(st["q"], st["kc"], st["vc"], st["bt"], st["qsl"], st["lens"],
+                               st["comp"], 0.5, B, "f32")
+    # key at position c + 1 is visible to row 1 only
+    p = c + 1
+    blk, off = int(st["bt"][0][p // B]), p % B
+    kc = st["kc"].copy()
+    kc[blk, off] += 3.0
+    alt, _ = oracle.attention(st["q"], kc, st["vc"], st["bt"], st["qsl"], st["lens"],
+                              st["comp"], 0.5, B, "f32")
+    assert np.array_equal(alt[0], base[0])
+    assert not np.allclose(alt[1], base[1])
+
+
+def test_invariances_block_permutation_request_order_poison():
+    rng = np.random.default_rng(21)
+    Hq, Hkv, D, B = 4, 2, 8, 4
+    st = _random_step(rng, 4, Hq, Hkv, D, B, 30, nb_extra=5)
+    args = (0.35, B, "f32")
+    base, _ = oracle.attention(st["q"], st["kc"], st["vc"], st["bt"], st["qsl"], st["lens"],
+                               st["comp"], *args)
+    # 1) relabel physical blocks, moving their data with them
+    nb = st["nb"]
+    perm = rng.permutation(nb)               # old id -> new id
+    kc2 = np.empty_like(st["kc"])
+    vc2 = np.empty_like(st["vc"])
+    kc2[perm] = st["kc"]
+    vc2[perm] = st["vc"]
+    bt2 = np.where(st["bt"] >= 0, perm[np.maximum(st["bt"], 0)], -1).astype(np.int32)
+    o2, _ = oracle.attention(st["q"], kc2, vc2, bt2, st["qsl"], st["lens"], st["comp"], *args)
+    assert np.array_equal(o2, base)
+    # 2) poison every slot no request may read (unused blocks, tail slots)
+    kc3, vc3 = st["kc"].copy(), st["vc"].copy()
+    readable = np.zeros((nb, B), dtype=bool)
+    for r, L in enumerate(st["lens"]):
+        for p in range(L):
+            readable[st["bt"][r][p // B], p % B] = True
+    kc3[~readable] = np.nan
+    vc3[~readable] = np.nan
+    o3, _ = oracle.attention(st["q"], kc3, vc3, st["bt"], st["qsl"], st["lens"], st["comp"], *args)
+    assert np.array_equal(o3, base)
+    # 3) reverse the request order in the flattened batch
+    order = list(range(4))[::-1]
+    q_parts = [st["q"][st["qsl"][r]:st["qsl"][r + 1]] for r in order]
+    qsl4 = np.concatenate([[0], np.cumsum([st["qlens"][r] for r in order])]).astype(np.int32)
+    o4, _ = oracle.attention(np.concatenate(q_parts), st["kc"], st["vc"], st["bt"][order], qsl4,
+                             [st["lens"][r] for r in order], [st["comp"][r] for r in order], *args)
+    for i, r in enumerate(order):
+        assert np.array_equal(o4[qsl4[i]:qsl4[i + 1]], base[st["qsl"][r]:st["qsl"][r + 1]])
+
+
+def test_merge_partials_equals_full_softmax():
+    """Log-sum-exp merge of partial results over disjoint key ranges equals the
+    softmax over all keys (scalar brute force for the partials)."""
+    rng = np.random.default_rng(12)
+    L, D = 37, 5
+    s = rng.standard_normal(L) * 3
+    v = rng.standard_normal((L, D))
+    full = (np.exp(s - s.max())[:, None] * v).sum(0) / np.exp(s - s.max()).sum()
+    for cuts in [[0, 37], [0, 10, 37], [0, 1, 2, 30, 37], list(range(0, 38, 4)) + [37]]:
+        cuts = sorted(set(cuts))
+        ms, ls, os_ = [], [], []
+        for a, b in zip(cuts[:-1], cuts[1:]):
+            m = max(s[a:b])
+            ms.append(m)
+            ls.append(sum(math.exp(x - m) for x in s[a:b]))
+            os_.append(sum(math.exp(s[j] - m) * v[j] for j in range(a, b)))
+        got = oracle.merge_partials(np.array(ms), np.array(ls), np.array(os_))
+        assert np.allclose(got, full, atol=1e-13)
+
+
+def test_bf16_widening_exact():
+    # patterns of exactly representable values
+    vals = np.array([1.0, -2.5, 0.0, 3.140625, -0.0078125, 65280.0], dtype=np.float32)
+    bits = (vals.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(oracle.bf16_bits_to_f64(bits), vals.astype(np.float64))
+    assert np.isnan(oracle.bf16_bits_to_f64(np.array([0x7FC0], np.uint16)))[0]
