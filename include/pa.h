@@ -1,0 +1,210 @@
+/*
+ * pa.h -- C ABI of the paged-KV attention step for AMD Instinct MI355X (gfx950).
+ *
+ * One continuous-batching step of a decoder layer, as the pages describe it:
+ *   1. the new tokens' K/V are scattered into a block pool through a slot
+ *      mapping (slot = physical_block * block_size + offset), and
+ *   2. GQA attention runs over a flattened, padding-free batch that mixes
+ *      decode tokens and prefill chunks, reading history through a per-request
+ *      block table with the causal mask at absolute positions.
+ *
+ * Sources (web pages; section names as printed):
+ *   [P1] "AI Infra入门干货总结：大模型是如何高效推理的" (joto.ai): sections
+ *        "连续批处理 (Continuous Batching)", "Paged Attention",
+ *        "Attention Module (以标准GQA + RoPE为例)", "总结".
+ *   [P4] "Chunked Prefill 与 Preemption" (llm-glossary.tokens-kit.com):
+ *        section "Chunked Prefill：改变调度粒度，不改变 causal 结果", equation M_{i,j}.
+ *   [P5] "显存与调度" (aaai.latere.ai, chapter 32): sections "从保留词元到物理块",
+ *        "块表消除连续内存要求".
+ *
+ * Conventions for every entry point
+ *   - The caller owns every buffer.  The library keeps no pointer after a call
+ *     returns and allocates no device memory; pa_attention takes a
+ *     caller-provided workspace.
+ *   - "device" pointers are HIP device memory of the current device; "host"
+ *     pointers are ordinary host memory, read before the call returns.
+ *   - Calls taking a stream enqueue work on it (NULL = the null stream) and
+ *     return without synchronising.  pa_write_kv for a layer must be enqueued
+ *     before pa_attention of that layer: attention reads the step's own K/V
+ *     back from the cache ([P1] "Attention Module": the prompt's K/V are first
+ *     written by the cache-write kernel, then read through the block table).
+ *   - Every argument that can be checked on the host is checked before any
+ *     work is enqueued; a failing check returns a status, sets
+ *     pa_last_error() and enqueues nothing.  Nothing aborts or throws across
+ *     the ABI.  Index values that live only in device memory (block ids, slot
+ *     values) are not checked on the fast path: the kernels clamp every block
+ *     id into the pool, so bad indices give wrong numbers but no out-of-bounds
+ *     access; pa_validate_metadata checks host copies of them exactly.
+ *   - Tensors are dense and row-major with the shapes given below.
+ *   - Support matrix: head_dim in {64, 128}; block_size a positive multiple of
+ *     16; num_heads % num_kv_heads == 0 with num_heads / num_kv_heads in
+ *     {1, 2, 4, 8}; dtype PA_F32 or PA_BF16, shared by query, key, value,
+ *     caches and output.  Anything else returns PA_ERR_UNSUPPORTED.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL_PTR = 1,
+  PA_ERR_BAD_SHAPE = 2,
+  PA_ERR_BAD_DTYPE = 3,
+  PA_ERR_UNSUPPORTED = 4,
+  PA_ERR_OUT_OF_RANGE = 5,
+  PA_ERR_DUPLICATE_SLOT = 6,
+  PA_ERR_INCONSISTENT_METADATA = 7,
+  PA_ERR_WORKSPACE_TOO_SMALL = 8,
+  PA_ERR_HIP = 9
+} pa_status;
+
+typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* ABI version of the loaded library (PA_ABI_VERSION it was built with). */
+int pa_abi_version(void);
+
+/* Static, never-NULL name of a status code ("PA_OK", ...; "PA_UNKNOWN" for
+ * values outside the enum). */
+const char* pa_status_str(int status);
+
+/* Detail of the last failing call on the calling thread ("" if none).  The
+ * string stays valid until the next library call on this thread. */
+const char* pa_last_error(void);
+
+/*
+ * pa_build_step_metadata -- host-side step metadata for a flattened batch.
+ *
+ * [P1] "连续批处理": a step schedules, per request, the tokens between
+ * num_computed_tokens and its current length, and all scheduled tokens form
+ * one flattened batch; [P1] "Attention Module" ("特别注意"): cumulative
+ * sequence lengths isolate requests inside that batch; [P1] "Paged
+ * Attention": token position p of request r is stored at
+ * block_table[r][p / block_size] * block_size + p % block_size.
+ *
+ *   h_query_lens        host int32 [R]   tokens scheduled for request r (>= 0)
+ *   h_num_computed      host int32 [R]   tokens of r already in the cache (>= 0)
+ *   h_block_table       host int32 [R, max_blocks_per_req] physical block ids;
+ *                       entry j must be valid for j < ceil(seq_len / block_size)
+ *   h_query_start_loc   host int32 [R + 1] out: exclusive prefix sum of query_lens
+ *   h_seq_lens          host int32 [R]     out: num_computed + query_lens
+ *   h_slot_mapping      host int64 [slot_capacity] out: flat slot of every
+ *                       scheduled token, in flattened order
+ * Returns PA_ERR_OUT_OF_RANGE if a needed block-table entry is outside
+ * [0, num_blocks) or a sequence needs more than max_blocks_per_req blocks,
+ * PA_ERR_BAD_SHAPE if the tokens exceed slot_capacity or a count is negative.
+ * Outputs are unspecified on error.
+ */
+pa_status pa_build_step_metadata(const int32_t* h_query_lens, const int32_t* h_num_computed,
+                                 int32_t R, const int32_t* h_block_table,
+                                 int32_t max_blocks_per_req, int32_t block_size,
+                                 int32_t num_blocks, int32_t* h_query_start_loc,
+                                 int32_t* h_seq_lens, int64_t* h_slot_mapping,
+                                 int64_t slot_capacity);
+
+/*
+ * pa_write_kv -- scatter the step's new K/V rows into the paged cache.
+ *
+ * [P1] "Paged Attention" (slot_idx = block_idx * block_size + block_offset;
+ * block = slot / block_size, offset = slot % block_size) and "Attention
+ * Module" (the new K/V are scattered into the paged cache by slot mapping).
+ *
+ *   key, value          device [T, num_kv_heads, head_dim]
+ *   key_cache,
+ *   value_cache         device [num_blocks, block_size, num_kv_heads, head_dim],
+ *                       written in place: row t goes to
+ *                       cache[slot / block_size][slot % block_size]
+ *   slot_mapping        device int64 [T]; a negative slot writes nothing
+ * The copy is exact (bit-for-bit).  Slots must be distinct and below
+ * num_blocks * block_size; a slot at or past the end of the pool is skipped on
+ * the fast path (pa_validate_metadata reports it).  T == 0 is a no-op.
+ */
+pa_status pa_write_kv(const void* key, const void* value, void* key_cache, void* value_cache,
+                      const int64_t* slot_mapping, int64_t T, int32_t num_blocks,
+                      int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                      pa_dtype dtype, void* stream);
+
+/*
+ * pa_attention_workspace_size -- bytes of device workspace pa_attention needs
+ * for this step (plan tables plus split-K partial results).  Takes the same
+ * host mirrors pa_attention plans from; returns 0 and sets pa_last_error() if
+ * they are invalid.  The size depends only on these arguments.
+ */
+size_t pa_attention_workspace_size(const int32_t* h_query_start_loc, const int32_t* h_seq_lens,
+                                   int32_t R, int32_t num_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, pa_dtype dtype);
+
+/*
+ * pa_attention -- GQA attention of one step over the paged cache.
+ *
+ * Definition ([P1] "Attention Module"; [P4] equation M_{i,j}; [P5]
+ * "块表消除连续内存要求"): for request r with n_r = query_start_loc[r+1] -
+ * query_start_loc[r] query rows, seq_len L_r and num_computed c_r, query row
+ * i (flattened index query_start_loc[r] + i) sits at absolute position c_r + i;
+ * query head h uses kv head h / (num_heads / num_kv_heads); its output is
+ *   softmax_j(scale * <q, K_r[j]>) . V_r[j]  over keys j = 0 .. c_r + i,
+ * where K_r/V_r are the request's first L_r positions gathered through
+ * block_table[r].  A request with n_r == 1 is a decode row (it sees all L_r
+ * keys); n_r > 1 is a prefill chunk.  Requests never interact.
+ *
+ *   out                 device [T, num_heads, head_dim] (written; rows of
+ *                       requests with n_r == 0 do not exist)
+ *   query               device [T, num_heads, head_dim]
+ *   key_cache,
+ *   value_cache         device [num_blocks, block_size, num_kv_heads, head_dim]
+ *   block_table         device int32 [R, max_blocks_per_req]
+ *   query_start_loc     device int32 [R + 1]
+ *   seq_lens            device int32 [R]
+ *   num_computed_tokens device int32 [R] (must equal seq_lens - query lens)
+ *   h_query_start_loc,
+ *   h_seq_lens          host copies of the two arrays above; used only to size
+ *                       the launch and check the workspace, never to compute
+ *                       results.  They must equal the device arrays.
+ *   scale               softmax scale (1/sqrt(head_dim) for standard attention)
+ *   workspace           device buffer of at least
+ *                       pa_attention_workspace_size(...) bytes, 256-byte
+ *                       aligned; contents on entry are ignored
+ * Requirements checked on the host: query_start_loc[0] == 0, non-decreasing,
+ * query_start_loc[R] == T; 0 <= n_r <= L_r; L_r <= max_blocks_per_req *
+ * block_size.  The result does not depend on request order or on which
+ * physical blocks hold the data.
+ */
+pa_status pa_attention(void* out, const void* query, const void* key_cache,
+                       const void* value_cache, const int32_t* block_table,
+                       int32_t max_blocks_per_req, const int32_t* query_start_loc,
+                       const int32_t* seq_lens, const int32_t* num_computed_tokens,
+                       const int32_t* h_query_start_loc, const int32_t* h_seq_lens, int32_t R,
+                       int64_t T, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t num_blocks, int32_t block_size, float scale, pa_dtype dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_validate_metadata -- exact host-side check of a step's metadata (for
+ * tests and debugging; O(R * max_blocks + T)).
+ *
+ * Checks, in order: pointers and sizes; query_start_loc[0] == 0, monotone,
+ * query_start_loc[R] == T; seq_lens[r] == num_computed[r] + n_r; every
+ * sequence fits its block-table row; every block-table entry a sequence needs
+ * lies in [0, num_blocks); when h_slot_mapping is not NULL, every slot is
+ * negative or below num_blocks * block_size (else PA_ERR_OUT_OF_RANGE),
+ * every non-negative slot equals the block-table formula for its token
+ * (else PA_ERR_INCONSISTENT_METADATA) and no two tokens share a slot
+ * (else PA_ERR_DUPLICATE_SLOT).
+ */
+pa_status pa_validate_metadata(const int32_t* h_query_start_loc, const int32_t* h_seq_lens,
+                               const int32_t* h_num_computed, const int32_t* h_block_table,
+                               int32_t max_blocks_per_req, const int64_t* h_slot_mapping,
+                               int32_t R, int64_t T, int32_t num_blocks, int32_t block_size);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,11 @@
+"""Paged-KV attention step for AMD Instinct MI355X (gfx950).
+
+The work happens in libpa.so (HIP kernels behind the C ABI of include/pa.h);
+this package only marshals arguments.  Importing it does not load the
+library; the first call does, and raises if it has not been built.
+"""
+from ._lib import (  # noqa: F401
+    EXPORTS, LIB_PATH, PA_BF16, PA_F32, PAError, Workspace, abi_version, attention,
+    attention_workspace_size, build_step_metadata, last_error, lib, status_str,
+    validate_metadata, write_kv,
+)

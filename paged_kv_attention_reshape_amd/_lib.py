@@ -1,0 +1,226 @@
+"""Thin ctypes binding of libpa.so (include/pa.h).
+
+Argument marshalling only: every step of the attention path runs in the HIP
+library.  Torch tensors are used for device memory and streams; their data
+pointers and the current HIP stream are passed straight through.  If the
+library is not built, every call raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+PA_F32 = 0
+PA_BF16 = 1
+
+STATUS = {
+    0: "PA_OK", 1: "PA_ERR_NULL_PTR", 2: "PA_ERR_BAD_SHAPE", 3: "PA_ERR_BAD_DTYPE",
+    4: "PA_ERR_UNSUPPORTED", 5: "PA_ERR_OUT_OF_RANGE", 6: "PA_ERR_DUPLICATE_SLOT",
+    7: "PA_ERR_INCONSISTENT_METADATA", 8: "PA_ERR_WORKSPACE_TOO_SMALL", 9: "PA_ERR_HIP",
+}
+
+EXPORTS = [
+    "pa_abi_version", "pa_status_str", "pa_last_error", "pa_build_step_metadata",
+    "pa_write_kv", "pa_attention_workspace_size", "pa_attention", "pa_validate_metadata",
+]
+
+
+class PAError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        self.status_name = STATUS.get(status, "PA_UNKNOWN")
+        super().__init__(f"{where}: {self.status_name}: {detail}")
+
+
+_lib = None
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_vp = ctypes.c_void_p
+
+
+def lib():
+    """Load libpa.so (raises if it is missing)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m paged_kv_attention_reshape_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    L.pa_abi_version.restype = ctypes.c_int
+    L.pa_status_str.restype = ctypes.c_char_p
+    L.pa_status_str.argtypes = [ctypes.c_int]
+    L.pa_last_error.restype = ctypes.c_char_p
+    L.pa_build_step_metadata.restype = ctypes.c_int
+    L.pa_build_step_metadata.argtypes = [_i32p, _i32p, ctypes.c_int32, _i32p, ctypes.c_int32,
+                                         ctypes.c_int32, ctypes.c_int32, _i32p, _i32p, _i64p,
+                                         ctypes.c_int64]
+    L.pa_write_kv.restype = ctypes.c_int
+    L.pa_write_kv.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int64, ctypes.c_int32,
+                              ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int, _vp]
+    L.pa_attention_workspace_size.restype = ctypes.c_size_t
+    L.pa_attention_workspace_size.argtypes = [_i32p, _i32p, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_int]
+    L.pa_attention.restype = ctypes.c_int
+    L.pa_attention.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp, _i32p,
+                               _i32p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                               ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                               ctypes.c_float, ctypes.c_int, _vp, ctypes.c_size_t, _vp]
+    L.pa_validate_metadata.restype = ctypes.c_int
+    L.pa_validate_metadata.argtypes = [_i32p, _i32p, _i32p, _i32p, ctypes.c_int32, _i64p,
+                                       ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                       ctypes.c_int32]
+    _lib = L
+    return L
+
+
+def abi_version() -> int:
+    return lib().pa_abi_version()
+
+
+def status_str(s: int) -> str:
+    return lib().pa_status_str(s).decode()
+
+
+def last_error() -> str:
+    return lib().pa_last_error().decode()
+
+
+def _check(rc: int, where: str):
+    if rc != 0:
+        raise PAError(rc, where, last_error())
+
+
+def _np_i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _p32(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(_i32p)
+
+
+def _p64(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(_i64p)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    if t.dtype == torch.float32:
+        return PA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+# ----------------------------------------------------------------------------
+def build_step_metadata(query_lens, num_computed, block_table, block_size: int, num_blocks: int):
+    """Host metadata of a step: (query_start_loc [R+1], seq_lens [R],
+    slot_mapping [T] int64), from per-request query lengths, computed-token
+    counts and the block table [R, max_blocks_per_req]."""
+    ql = _np_i32(query_lens)
+    nc = _np_i32(num_computed)
+    bt = _np_i32(block_table)
+    R = len(ql)
+    if bt.ndim != 2 or bt.shape[0] < R:
+        raise ValueError("block_table must be [R, max_blocks_per_req]")
+    T = int(ql.sum())
+    qsl = np.zeros(R + 1, np.int32)
+    sl = np.zeros(max(R, 1), np.int32)
+    sm = np.zeros(max(T, 1), np.int64)
+    _check(lib().pa_build_step_metadata(_p32(ql), _p32(nc), R, _p32(bt), bt.shape[1], block_size,
+                                        num_blocks, _p32(qsl), _p32(sl), _p64(sm), T),
+           "pa_build_step_metadata")
+    return qsl, sl[:R], sm[:T]
+
+
+def validate_metadata(query_start_loc, seq_lens, num_computed, block_table, slot_mapping,
+                      num_blocks: int, block_size: int) -> None:
+    qsl = _np_i32(query_start_loc)
+    sl = _np_i32(seq_lens)
+    nc = _np_i32(num_computed)
+    bt = _np_i32(block_table)
+    sm = None if slot_mapping is None else np.ascontiguousarray(np.asarray(slot_mapping, np.int64))
+    R = len(sl)
+    T = int(qsl[-1]) if len(qsl) else 0
+    _check(lib().pa_validate_metadata(_p32(qsl), _p32(sl), _p32(nc), _p32(bt),
+                                      bt.shape[1] if bt.ndim == 2 else 0, _p64(sm), R, T,
+                                      num_blocks, block_size), "pa_validate_metadata")
+
+
+def write_kv(key, value, key_cache, value_cache, slot_mapping, stream=None) -> None:
+    """key/value [T, Hkv, D]; caches [N, B, Hkv, D]; slot_mapping int64 [T]
+    (device tensors, same dtype)."""
+    T = key.shape[0]
+    N, B, Hkv, D = key_cache.shape
+    _check(lib().pa_write_kv(_ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
+                             _ptr(slot_mapping), T, N, B, Hkv, D, _dtype_code(key),
+                             ctypes.c_void_p(_stream(stream))), "pa_write_kv")
+
+
+def attention_workspace_size(h_query_start_loc, h_seq_lens, num_heads: int, num_kv_heads: int,
+                             head_dim: int, block_size: int, dtype_code: int) -> int:
+    qsl = _np_i32(h_query_start_loc)
+    sl = _np_i32(h_seq_lens)
+    n = lib().pa_attention_workspace_size(_p32(qsl), _p32(sl), len(sl), num_heads, num_kv_heads,
+                                          head_dim, block_size, dtype_code)
+    if n == 0 and last_error():
+        raise PAError(2, "pa_attention_workspace_size", last_error())
+    return int(n)
+
+
+class Workspace:
+    """Reusable device workspace (grows on demand, 256-byte aligned)."""
+
+    def __init__(self, device="cuda"):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes: int):
+        import torch
+        nbytes = max(int(nbytes), 256)
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
+def attention(out, query, key_cache, value_cache, block_table, query_start_loc, seq_lens,
+              num_computed, h_query_start_loc, h_seq_lens, scale: float, workspace=None,
+              stream=None) -> None:
+    """out/query [T, Hq, D]; caches [N, B, Hkv, D]; block_table [R, M] int32;
+    query_start_loc [R+1], seq_lens [R], num_computed [R] int32 device tensors;
+    h_query_start_loc / h_seq_lens host mirrors (numpy)."""
+    T, Hq, D = query.shape
+    N, B, Hkv, _ = key_cache.shape
+    R = int(seq_lens.shape[0])
+    qsl = _np_i32(h_query_start_loc)
+    sl = _np_i32(h_seq_lens)
+    dt = _dtype_code(query)
+    need = attention_workspace_size(qsl, sl, Hq, Hkv, D, B, dt)
+    if workspace is None:
+        workspace = Workspace(query.device)
+    buf = workspace.get(need) if isinstance(workspace, Workspace) else workspace
+    M = block_table.shape[1] if block_table.dim() == 2 else 1
+    _check(lib().pa_attention(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
+                              _ptr(block_table), M, _ptr(query_start_loc), _ptr(seq_lens),
+                              _ptr(num_computed), _p32(qsl), _p32(sl), R, T, Hq, Hkv, D, N, B,
+                              float(scale), dt, _ptr(buf), buf.numel(),
+                              ctypes.c_void_p(_stream(stream))), "pa_attention")

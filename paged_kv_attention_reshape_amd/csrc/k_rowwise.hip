@@ -1,0 +1,410 @@
+// Split-K row-wise attention (decode rows) and the partition merge pass.
+//
+// Method: "AI Infra入门干货总结：大模型是如何高效推理的", section "Attention
+// Module": attention reads each request's history through the block table and
+// fuses q.k, softmax and the product with V using online softmax (a running
+// max and running sum, rescaled when a new tile raises the max); section
+// "总结": Flash-Decoding splits decode attention along the KV dimension and
+// normalises the partitions with log-sum-exp.  The causal limit of a row at
+// absolute position p is key p ("Chunked Prefill 与 Preemption", equation
+// M_{i,j}); the plan gives each item its key range [kb, ke).
+//
+// MI355X design (one wavefront per item x kv head; no atomics, so results are
+// deterministic):
+//   * the G query heads that share kv head g are processed together, so every
+//     K/V byte is read from HBM exactly once per item;
+//   * q.k: lanes are (token j, quarter c) pairs, 16 tokens per sub-tile; each
+//     lane dots a quarter of the head dimension for all G heads with
+//     v_dot2_f32_bf16 (two bf16 products per instruction, fp32 accumulate),
+//     and two DPP quad permutations finish the sums.  K rows are loaded as
+//     16-byte chunks, four lanes covering 64 contiguous bytes of a row;
+//   * softmax: each lane owns one head of its token, so one v_exp covers 16
+//     tokens x 4 heads; the max over tokens uses DPP row rotations and two
+//     cross-row shuffles; the running sum stays per lane until the end;
+//   * p.v: probabilities go through LDS as bf16 pairs of two tokens, V rows
+//     are read with 16 lanes covering one 256-byte row (fully coalesced), and
+//     v_dot2_f32_bf16 accumulates two tokens per instruction into fp32;
+//   * the next sub-tile's K and V are loaded before the current one is used.
+// fp32 caches use the same structure with plain FMAs.
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kRowRor4 = 0x124;  // row_ror:4
+constexpr int kRowRor8 = 0x128;  // row_ror:8
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float shfl_xor(float x, int m) { return __shfl_xor(x, m, 64); }
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+__device__ __forceinline__ uint32_t comp(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+template <bool BF16, int D, int G>
+struct Geo {
+  static constexpr int E = BF16 ? 2 : 4;        // bytes per element
+  static constexpr int ROWB = D * E;            // bytes of one head row
+  static constexpr int LPR = 4;                 // q.k lanes per token
+  static constexpr int NL = ROWB / (16 * LPR);  // 16-byte K loads per lane
+  static constexpr int EPC = 16 / E;            // elements per 16-byte chunk
+  static constexpr int LPRV = ROWB / 16;        // p.v lanes per V row
+  static constexpr int RPI = 64 / LPRV;         // V rows per wave instruction
+  static constexpr int RPL = 16 / RPI;          // V rows per lane per sub-tile
+  static constexpr int HPL = (G + 3) / 4;       // softmax heads per lane
+  static_assert(NL >= 1 && RPL >= 2 && RPL % 2 == 0, "unsupported geometry");
+};
+
+template <bool BF16, int D, int G>
+__global__ void __launch_bounds__(64) rowwise_kernel(AttnArgs a) {
+  using Gm = Geo<BF16, D, G>;
+  constexpr int ROWB = Gm::ROWB, LPR = Gm::LPR, NL = Gm::NL, EPC = Gm::EPC;
+  constexpr int LPRV = Gm::LPRV, RPI = Gm::RPI, RPL = Gm::RPL, HPL = Gm::HPL;
+
+  __shared__ float p_lds[16 * G];   // bf16: 8 token pairs x G dwords; fp32: 16 x G
+  __shared__ float a_lds[G];        // per-head rescale factor of this sub-tile
+  __shared__ float m_lds[G];
+  __shared__ float l_lds[G];
+
+  const int lane = threadIdx.x;
+  const int4 it = a.items_rw[blockIdx.x];
+  const int r = it.x;
+  if (r < 0 || r >= a.R) return;
+  const int g = blockIdx.y;
+  const int t = it.y;
+  const int kb = it.z;
+  const int ke = it.w & 0x7FFFFFFF;
+  const bool direct = (it.w & kDirect) != 0;
+
+  const int j = lane >> 2;           // token of the sub-tile (q.k layout)
+  const int c = lane & 3;            // quarter of the head dimension
+  const int rsub = lane / LPRV;      // first V row of this lane (p.v layout)
+  const int cv = lane % LPRV;        // 16-byte chunk of the V row
+
+  // query rows of the G heads, in the q.k lane layout
+  uint4 qv[G][NL];
+  {
+    const char* qb = static_cast<const char*>(a.query) + ((int64_t)t * a.Hq + g * G) * ROWB;
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int i = 0; i < NL; ++i)
+        qv[h][i] = *reinterpret_cast<const uint4*>(qb + h * ROWB + (i * LPR + c) * 16);
+  }
+
+  // physical block ids of the partition: lane i holds block kb/B + i
+  const int blk0 = kb / a.B;
+  const int nblk = (ke - 1) / a.B - blk0 + 1;
+  int myblk = 0;
+  if (lane < nblk) {
+    myblk = a.block_table[(int64_t)r * a.M + blk0 + lane];
+    myblk = myblk < 0 ? 0 : (myblk >= a.num_blocks ? a.num_blocks - 1 : myblk);
+  }
+
+  const char* kcache = static_cast<const char*>(a.kcache);
+  const char* vcache = static_cast<const char*>(a.vcache);
+  const int64_t slot_stride = (int64_t)a.Hkv * ROWB;
+
+  auto load_tile = [&](int start, uint4 (&kr)[NL], uint4 (&vr)[RPL]) {
+    const int blk = __builtin_amdgcn_readlane(myblk, start / a.B - blk0);
+    const int64_t slot0 = (int64_t)blk * a.B + (start % a.B);
+    const char* kbp = kcache + (slot0 + j) * slot_stride + (int64_t)g * ROWB;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) kr[i] = *reinterpret_cast<const uint4*>(kbp + (i * LPR + c) * 16);
+    const char* vbp = vcache + slot0 * slot_stride + (int64_t)g * ROWB + cv * 16;
+#pragma unroll
+    for (int k = 0; k < RPL; ++k)
+      vr[k] = *reinterpret_cast<const uint4*>(vbp + (int64_t)(rsub + RPI * k) * slot_stride);
+  };
+
+  float m_run[HPL], l_run[HPL];
+#pragma unroll
+  for (int k = 0; k < HPL; ++k) { m_run[k] = kNegInf; l_run[k] = 0.f; }
+  float o[G][EPC];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) o[h][e] = 0.f;
+
+  const int n_tiles = (ke - kb + 15) >> 4;
+  uint4 kc[NL], vc[RPL];
+  load_tile(kb, kc, vc);
+
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    const int start = kb + (tile << 4);
+    uint4 kn[NL], vn[RPL];
+    if (tile + 1 < n_tiles) load_tile(start + 16, kn, vn);
+
+    // ---- q.k for the G heads ----------------------------------------------
+    float s[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < NL; ++i)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          if constexpr (BF16) {
+            acc = dot2(comp(kc[i], w), comp(qv[h][i], w), acc);
+          } else {
+            acc = __builtin_fmaf(__uint_as_float(comp(kc[i], w)), __uint_as_float(comp(qv[h][i], w)), acc);
+          }
+        }
+      acc += dpp<kQuadXor1>(acc);
+      acc += dpp<kQuadXor2>(acc);
+      s[h] = acc;
+    }
+
+    // ---- online softmax: each lane owns heads c, c+4 of token j ------------
+    const bool tok_ok = start + j < ke;
+    bool rescale = false;
+#pragma unroll
+    for (int k = 0; k < HPL; ++k) {
+      const int h = c + 4 * k;
+      const bool hv = h < G;
+      float sv = s[0];
+#pragma unroll
+      for (int hh = 1; hh < G; ++hh) sv = (h == hh) ? s[hh] : sv;
+      const float s2 = (hv && tok_ok) ? sv * a.scale_log2 : kNegInf;
+      float mx = s2;
+      mx = fmaxf(mx, dpp<kRowRor4>(mx));
+      mx = fmaxf(mx, dpp<kRowRor8>(mx));
+      mx = fmaxf(mx, shfl_xor(mx, 16));
+      mx = fmaxf(mx, shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run[k], mx);
+      const bool live = m_new != kNegInf;
+      const float alpha = live ? __builtin_amdgcn_exp2f(m_run[k] - m_new) : 1.f;
+      const float p = live ? __builtin_amdgcn_exp2f(s2 - m_new) : 0.f;
+      l_run[k] = l_run[k] * alpha + p;
+      m_run[k] = m_new;
+      rescale |= alpha != 1.f;
+      if (hv) {
+        if constexpr (BF16) {
+          const int rs = j % RPI, kk = j / RPI;
+          const int pi = (kk >> 1) * RPI + rs;
+          reinterpret_cast<uint16_t*>(p_lds)[(pi * G + h) * 2 + (kk & 1)] = to_bf16(p);
+        } else {
+          p_lds[j * G + h] = p;
+        }
+        if (j == 0) a_lds[h] = alpha;
+      }
+    }
+    const bool any_rescale = __builtin_amdgcn_ballot_w64(rescale) != 0;
+    __syncthreads();
+
+    // ---- p.v ----------------------------------------------------------------
+    if (start + 16 > ke) {  // tail sub-tile: rows past the key range may hold NaN
+#pragma unroll
+      for (int k = 0; k < RPL; ++k)
+        if (start + rsub + RPI * k >= ke) vc[k] = make_uint4(0, 0, 0, 0);
+    }
+    if (any_rescale) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float al = a_lds[h];
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) o[h][e] *= al;
+      }
+    }
+    if constexpr (BF16) {
+#pragma unroll
+      for (int kk = 0; kk < RPL / 2; ++kk) {
+        const uint32_t* pp = reinterpret_cast<const uint32_t*>(p_lds) + (kk * RPI + rsub) * G;
+        uint32_t pr[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) pr[h] = pp[h];
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+          const uint32_t lo = comp(vc[2 * kk], e >> 1);
+          const uint32_t hi = comp(vc[2 * kk + 1], e >> 1);
+          const uint32_t vp = __builtin_amdgcn_perm(hi, lo, (e & 1) ? 0x07060302u : 0x05040100u);
+#pragma unroll
+          for (int h = 0; h < G; ++h) o[h][e] = dot2(vp, pr[h], o[h][e]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < RPL; ++k) {
+        const int row = rsub + RPI * k;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float p = p_lds[row * G + h];
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) o[h][e] = __builtin_fmaf(p, __uint_as_float(comp(vc[k], e)), o[h][e]);
+        }
+      }
+    }
+    __syncthreads();
+
+    if (tile + 1 < n_tiles) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) kc[i] = kn[i];
+#pragma unroll
+      for (int k = 0; k < RPL; ++k) vc[k] = vn[k];
+    }
+  }
+
+  // ---- finish: sums over tokens and over V-row groups ----------------------
+#pragma unroll
+  for (int k = 0; k < HPL; ++k) {
+    float l = l_run[k];
+    l += dpp<kRowRor4>(l);
+    l += dpp<kRowRor8>(l);
+    l += shfl_xor(l, 16);
+    l += shfl_xor(l, 32);
+    const int h = c + 4 * k;
+    if (j == 0 && h < G) {
+      m_lds[h] = m_run[k];
+      l_lds[h] = l;
+    }
+  }
+#pragma unroll
+  for (int off = LPRV; off < 64; off <<= 1)
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) o[h][e] += shfl_xor(o[h][e], off);
+  __syncthreads();
+
+  if (rsub == 0) {
+    const int hq0 = g * G;
+    if (direct) {
+      char* ob = static_cast<char*>(a.out) + ((int64_t)t * a.Hq + hq0) * ROWB + cv * 16;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float inv = 1.f / l_lds[h];
+        if constexpr (BF16) {
+          uint32_t w[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            w[e] = (uint32_t)to_bf16(o[h][2 * e] * inv) | ((uint32_t)to_bf16(o[h][2 * e + 1] * inv) << 16);
+          *reinterpret_cast<uint4*>(ob + h * ROWB) = make_uint4(w[0], w[1], w[2], w[3]);
+        } else {
+          *reinterpret_cast<float4*>(ob + h * ROWB) =
+              make_float4(o[h][0] * inv, o[h][1] * inv, o[h][2] * inv, o[h][3] * inv);
+        }
+      }
+    } else {
+      float* op = a.o_part + ((int64_t)blockIdx.x * a.Hq + hq0) * D + cv * EPC;
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < EPC; e += 4)
+          *reinterpret_cast<float4*>(op + h * D + e) = make_float4(o[h][e], o[h][e + 1], o[h][e + 2], o[h][e + 3]);
+    }
+  }
+  if (!direct && lane < G) {
+    float* mp = a.ml_part + ((int64_t)blockIdx.x * a.Hq + g * G + lane) * 2;
+    mp[0] = m_lds[lane];
+    mp[1] = l_lds[lane];
+  }
+}
+
+// Merge pass: combine the partial (m, l, o) of one query row's partitions,
+// rescaling each to the global max (log-sum-exp normalisation).
+template <bool BF16, int D, int G>
+__global__ void __launch_bounds__(64) merge_kernel(AttnArgs a) {
+  constexpr int E = BF16 ? 2 : 4;
+  constexpr int PER = D / 64;  // elements per lane
+  const int4 mr = a.merge[blockIdx.x];
+  const int t = mr.x;
+  if (t < 0) return;
+  const int first = mr.y, n = mr.z, stride = mr.w;
+  const int g = blockIdx.y;
+  const int lane = threadIdx.x;
+#pragma unroll 1
+  for (int h = 0; h < G; ++h) {
+    const int hq = g * G + h;
+    float M = kNegInf;
+    for (int p = 0; p < n; ++p) {
+      const int64_t part = first + (int64_t)p * stride;
+      M = fmaxf(M, a.ml_part[(part * a.Hq + hq) * 2]);
+    }
+    float num[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) num[e] = 0.f;
+    float den = 0.f;
+    for (int p = 0; p < n; ++p) {
+      const int64_t part = first + (int64_t)p * stride;
+      const float* ml = a.ml_part + (part * a.Hq + hq) * 2;
+      const float w = __builtin_amdgcn_exp2f(ml[0] - M);
+      den += w * ml[1];
+      const float* op = a.o_part + (part * a.Hq + hq) * D + lane * PER;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) num[e] += w * op[e];
+    }
+    const float inv = 1.f / den;
+    char* ob = static_cast<char*>(a.out) + (((int64_t)t * a.Hq + hq) * D + lane * PER) * E;
+    if constexpr (BF16) {
+      if constexpr (PER == 2) {
+        *reinterpret_cast<uint32_t*>(ob) =
+            (uint32_t)to_bf16(num[0] * inv) | ((uint32_t)to_bf16(num[1] * inv) << 16);
+      } else {
+        *reinterpret_cast<uint16_t*>(ob) = to_bf16(num[0] * inv);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < PER; ++e) reinterpret_cast<float*>(ob)[e] = num[e] * inv;
+    }
+  }
+}
+
+#define PA_DISPATCH_GD(FN, BF, DD)                                    \
+  switch (a.Hq / a.Hkv) {                                             \
+    case 1: kern = (const void*)FN<BF, DD, 1>; break;                 \
+    case 2: kern = (const void*)FN<BF, DD, 2>; break;                 \
+    case 4: kern = (const void*)FN<BF, DD, 4>; break;                 \
+    case 8: kern = (const void*)FN<BF, DD, 8>; break;                 \
+    default: return hipErrorInvalidValue;                             \
+  }
+
+#define PA_SELECT(FN)                                                 \
+  const void* kern = nullptr;                                         \
+  if (a.bf16) {                                                       \
+    if (a.D == 64) { PA_DISPATCH_GD(FN, true, 64) }                   \
+    else if (a.D == 128) { PA_DISPATCH_GD(FN, true, 128) }            \
+    else return hipErrorInvalidValue;                                 \
+  } else {                                                            \
+    if (a.D == 64) { PA_DISPATCH_GD(FN, false, 64) }                  \
+    else if (a.D == 128) { PA_DISPATCH_GD(FN, false, 128) }           \
+    else return hipErrorInvalidValue;                                 \
+  }
+
+}  // namespace
+
+hipError_t launch_rowwise(const AttnArgs& a, hipStream_t s) {
+  if (a.ps.n_rw == 0) return hipSuccess;
+  PA_SELECT(rowwise_kernel)
+  AttnArgs args = a;
+  void* params[] = {&args};
+  return hipLaunchKernel(kern, dim3(a.ps.n_rw, a.Hkv), dim3(64), params, 0, s);
+}
+
+hipError_t launch_merge(const AttnArgs& a, hipStream_t s) {
+  if (a.ps.n_mg == 0) return hipSuccess;
+  PA_SELECT(merge_kernel)
+  AttnArgs args = a;
+  void* params[] = {&args};
+  return hipLaunchKernel(kern, dim3(a.ps.n_mg, a.Hkv), dim3(64), params, 0, s);
+}
+
+}  // namespace pa

@@ -1,0 +1,62 @@
+// Cache-write kernel: scatter the step's new K/V rows into the paged pool.
+//
+// "AI Infra入门干货总结：大模型是如何高效推理的", section "Paged Attention":
+// the slot of a token is block * block_size + offset, and the cache of a
+// layer is [num_blocks, block_size, num_kv_heads, head_dim], so one token's
+// K (or V) for all kv heads is one contiguous row of num_kv_heads * head_dim
+// elements at row index `slot` of the pool viewed as [num_blocks*block_size,
+// row].  The write is therefore a row gather-scatter: every 16-byte chunk of
+// the source row goes to the same offset of the destination row.
+//
+// MI355X mapping: consecutive lanes move consecutive 16-byte chunks of the
+// same row, so each wavefront issues fully coalesced 1 KiB loads and stores;
+// K and V of a token are handled by the same workgroup (second half of the
+// block), which keeps the slot value in one cache line for both.  The kernel
+// is bandwidth- and latency-bound and touches each byte exactly once.
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ void __launch_bounds__(kThreads)
+write_kv_kernel(const uint4* __restrict__ key, const uint4* __restrict__ value,
+                uint4* __restrict__ key_cache, uint4* __restrict__ value_cache,
+                const int64_t* __restrict__ slots, int64_t T, int64_t num_slots,
+                int32_t chunks_per_row) {
+  // one block handles `tokens_per_block` tokens; threads [0, half) copy K,
+  // [half, 2*half) copy V of the same tokens
+  const int32_t half = kThreads / 2;
+  const bool is_v = threadIdx.x >= half;
+  const int32_t lt = is_v ? threadIdx.x - half : threadIdx.x;
+  const int64_t total = T * (int64_t)chunks_per_row;
+  const uint4* __restrict__ src = is_v ? value : key;
+  uint4* __restrict__ dst = is_v ? value_cache : key_cache;
+  for (int64_t idx = (int64_t)blockIdx.x * half + lt; idx < total;
+       idx += (int64_t)gridDim.x * half) {
+    const int64_t t = idx / chunks_per_row;
+    const int64_t c = idx - t * chunks_per_row;
+    const int64_t slot = slots[t];
+    if (slot < 0 || slot >= num_slots) continue;
+    dst[slot * chunks_per_row + c] = src[t * chunks_per_row + c];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_write_kv(const void* key, const void* value, void* key_cache, void* value_cache,
+                           const int64_t* slots, int64_t T, int64_t num_slots, int32_t row_bytes,
+                           hipStream_t s) {
+  const int32_t cpr = row_bytes / 16;
+  const int64_t total = T * (int64_t)cpr;
+  int64_t blocks = (total + kThreads / 2 - 1) / (kThreads / 2);
+  if (blocks > 1 << 20) blocks = 1 << 20;
+  hipLaunchKernelGGL(write_kv_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s,
+                     static_cast<const uint4*>(key), static_cast<const uint4*>(value),
+                     static_cast<uint4*>(key_cache), static_cast<uint4*>(value_cache), slots, T,
+                     num_slots, cpr);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,363 @@
+// C-ABI entry points of the paged-KV attention library (declared in pa.h).
+//
+// Host side only: argument checks, the step-metadata builder, the launch
+// plan sizing and the kernel launch sequence
+//   pa_write_kv:  write_kv
+//   pa_attention: plan -> row-wise split-K -> chunk (matrix cores) -> merge
+// all on the caller's stream.
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "pa_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+pa_status fail(pa_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+pa_status hip_fail(hipError_t e, const char* what) {
+  return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  if (v == nullptr || *v == 0) return dflt;
+  return atoi(v);
+}
+
+pa_status check_geometry(int32_t Hq, int32_t Hkv, int32_t D, int32_t B, int32_t num_blocks,
+                         int dtype) {
+  if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_BAD_DTYPE, "dtype %d is not PA_F32 or PA_BF16", dtype);
+  if (Hq <= 0 || Hkv <= 0 || D <= 0 || B <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_BAD_SHAPE, "sizes must be positive (Hq=%d Hkv=%d D=%d B=%d num_blocks=%d)", Hq, Hkv, D, B, num_blocks);
+  if (D != 64 && D != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", D);
+  if (B % 16 != 0) return fail(PA_ERR_UNSUPPORTED, "block_size %d is not a multiple of 16", B);
+  if (Hq % Hkv != 0) return fail(PA_ERR_UNSUPPORTED, "num_heads %d is not a multiple of num_kv_heads %d", Hq, Hkv);
+  const int G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(PA_ERR_UNSUPPORTED, "GQA group %d not in {1, 2, 4, 8}", G);
+  return PA_OK;
+}
+
+int64_t gcd64(int64_t a, int64_t b) { return b == 0 ? a : gcd64(b, a % b); }
+
+// Row-wise partition length: a power-of-two multiple of lcm(64, B), at most
+// 64 blocks (one block id per lane of the wavefront), chosen so that the
+// grid holds roughly 16 wavefronts per compute unit.
+int32_t choose_split(int64_t rowwise_keys, int32_t Hkv, int32_t B) {
+  const int64_t unit = 64 / gcd64(64, B) * B;
+  const int64_t cap = std::max<int64_t>(unit, (int64_t)64 * B);
+  const int forced = env_int("PA_SPLIT_TOKENS", 0);
+  if (forced > 0) {
+    int64_t s = (forced + unit - 1) / unit * unit;
+    return (int32_t)std::min(s, cap / unit * unit);
+  }
+  const int64_t target_waves = 256 * 16;
+  const int64_t want = rowwise_keys * Hkv / target_waves;
+  int64_t s = unit;
+  while (s < want && s * 2 <= cap && s * 2 <= 1024) s *= 2;
+  return (int32_t)s;
+}
+
+// Validates the host mirrors and fills the plan shape (exact table sizes).
+pa_status make_plan(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R, int64_t T,
+                    int32_t M, int32_t Hq, int32_t Hkv, int32_t D, int32_t B, bool bf16,
+                    pa::PlanShape* out) {
+  if (R < 0) return fail(PA_ERR_BAD_SHAPE, "R=%d < 0", R);
+  if (R > 0 && (h_qsl == nullptr || h_seq_lens == nullptr))
+    return fail(PA_ERR_NULL_PTR, "host query_start_loc / seq_lens mirrors are required");
+  if (T < 0 || T > INT32_MAX) return fail(PA_ERR_BAD_SHAPE, "T=%lld out of range", (long long)T);
+  if (R > 0 && h_qsl[0] != 0) return fail(PA_ERR_INCONSISTENT_METADATA, "query_start_loc[0]=%d != 0", h_qsl[0]);
+  if (R > 0 && h_qsl[R] != T)
+    return fail(PA_ERR_INCONSISTENT_METADATA, "query_start_loc[R]=%d != T=%lld", h_qsl[R], (long long)T);
+  const int64_t cap_tokens = (int64_t)M * B;
+  int64_t rowwise_keys = 0;
+  const int G = Hq / Hkv;
+  pa::PlanShape ps{};
+  ps.R = R;
+  ps.T = (int32_t)T;
+  ps.M = M;
+  ps.B = B;
+  ps.rowwise_all = pa::chunk_kernel_supports(bf16, D, G) && env_int("PA_FORCE_ROWWISE", 0) == 0 ? 0 : 1;
+  ps.TQ = pa::chunk_tile_tokens(G);
+  ps.SEG = 1 << 30;
+  for (int32_t r = 0; r < R; ++r) {
+    const int32_t q = h_qsl[r + 1] - h_qsl[r];
+    const int32_t L = h_seq_lens[r];
+    if (q < 0) return fail(PA_ERR_INCONSISTENT_METADATA, "query_start_loc decreases at request %d", r);
+    if (L < q) return fail(PA_ERR_INCONSISTENT_METADATA, "seq_lens[%d]=%d < query length %d", r, L, q);
+    if ((int64_t)L > cap_tokens)
+      return fail(PA_ERR_OUT_OF_RANGE, "seq_lens[%d]=%d exceeds max_blocks_per_req*block_size=%lld", r, L, (long long)cap_tokens);
+    if (q > 0 && pa::goes_rowwise(q, ps)) {
+      const int64_t c = L - q;
+      rowwise_keys += q * (c + 1) + (int64_t)q * (q - 1) / 2;
+    }
+  }
+  ps.S = choose_split(rowwise_keys, Hkv, B);
+  const int seg = env_int("PA_CHUNK_SEG", 0);
+  if (seg > 0) ps.SEG = (seg + 63) / 64 * 64;
+  int64_t n_rw = 0, n_ck = 0, n_mg = 0, n_parts = 0;
+  for (int32_t r = 0; r < R; ++r) {
+    int32_t q = h_qsl[r + 1] - h_qsl[r];
+    int32_t L = h_seq_lens[r];
+    pa::sanitize(q, L, M, B);
+    const pa::ReqCounts n = pa::request_counts(q, L, ps);
+    n_rw += n.rw;
+    n_ck += n.ck;
+    n_mg += n.mg;
+    n_parts += n.ck_parts;
+  }
+  if (n_rw + n_parts > INT32_MAX / 2 || n_ck > INT32_MAX / 2 || n_mg > INT32_MAX / 2)
+    return fail(PA_ERR_BAD_SHAPE, "step too large for one call");
+  ps.n_rw = (int32_t)n_rw;
+  ps.n_ck = (int32_t)n_ck;
+  ps.n_mg = (int32_t)n_mg;
+  ps.n_ck_parts = (int32_t)n_parts;
+  *out = ps;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_abi_version(void) { return PA_ABI_VERSION; }
+
+const char* pa_status_str(int status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_NULL_PTR: return "PA_ERR_NULL_PTR";
+    case PA_ERR_BAD_SHAPE: return "PA_ERR_BAD_SHAPE";
+    case PA_ERR_BAD_DTYPE: return "PA_ERR_BAD_DTYPE";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+    case PA_ERR_OUT_OF_RANGE: return "PA_ERR_OUT_OF_RANGE";
+    case PA_ERR_DUPLICATE_SLOT: return "PA_ERR_DUPLICATE_SLOT";
+    case PA_ERR_INCONSISTENT_METADATA: return "PA_ERR_INCONSISTENT_METADATA";
+    case PA_ERR_WORKSPACE_TOO_SMALL: return "PA_ERR_WORKSPACE_TOO_SMALL";
+    case PA_ERR_HIP: return "PA_ERR_HIP";
+    default: return "PA_UNKNOWN";
+  }
+}
+
+const char* pa_last_error(void) { return g_err.c_str(); }
+
+pa_status pa_build_step_metadata(const int32_t* h_query_lens, const int32_t* h_num_computed,
+                                 int32_t R, const int32_t* h_block_table,
+                                 int32_t max_blocks_per_req, int32_t block_size,
+                                 int32_t num_blocks, int32_t* h_query_start_loc,
+                                 int32_t* h_seq_lens, int64_t* h_slot_mapping,
+                                 int64_t slot_capacity) {
+  g_err.clear();
+  if (R < 0 || max_blocks_per_req < 0 || block_size <= 0 || num_blocks <= 0 || slot_capacity < 0)
+    return fail(PA_ERR_BAD_SHAPE, "negative or zero size argument");
+  if (h_query_start_loc == nullptr) return fail(PA_ERR_NULL_PTR, "h_query_start_loc is NULL");
+  if (R > 0 && (h_query_lens == nullptr || h_num_computed == nullptr || h_seq_lens == nullptr))
+    return fail(PA_ERR_NULL_PTR, "NULL per-request array");
+  int64_t t = 0;
+  h_query_start_loc[0] = 0;
+  for (int32_t r = 0; r < R; ++r) {
+    const int32_t q = h_query_lens[r], c = h_num_computed[r];
+    if (q < 0 || c < 0) return fail(PA_ERR_BAD_SHAPE, "negative count for request %d", r);
+    const int64_t L = (int64_t)q + c;
+    if (L > INT32_MAX) return fail(PA_ERR_BAD_SHAPE, "sequence %d too long", r);
+    const int64_t need = (L + block_size - 1) / block_size;
+    if (need > max_blocks_per_req)
+      return fail(PA_ERR_OUT_OF_RANGE, "request %d needs %lld blocks > %d", r, (long long)need, max_blocks_per_req);
+    if (t + q > slot_capacity || t + q > INT32_MAX)
+      return fail(PA_ERR_BAD_SHAPE, "scheduled tokens exceed slot_capacity %lld", (long long)slot_capacity);
+    if (q > 0 && (h_block_table == nullptr || h_slot_mapping == nullptr))
+      return fail(PA_ERR_NULL_PTR, "NULL block table or slot mapping");
+    const int32_t* row = h_block_table + (int64_t)r * max_blocks_per_req;
+    for (int32_t i = 0; i < q; ++i) {
+      const int64_t p = (int64_t)c + i;
+      const int32_t blk = row[p / block_size];
+      if (blk < 0 || blk >= num_blocks)
+        return fail(PA_ERR_OUT_OF_RANGE, "block_table[%d][%lld]=%d outside [0, %d)", r, (long long)(p / block_size), blk, num_blocks);
+      h_slot_mapping[t + i] = (int64_t)blk * block_size + p % block_size;
+    }
+    t += q;
+    h_query_start_loc[r + 1] = (int32_t)t;
+    h_seq_lens[r] = (int32_t)L;
+  }
+  return PA_OK;
+}
+
+pa_status pa_write_kv(const void* key, const void* value, void* key_cache, void* value_cache,
+                      const int64_t* slot_mapping, int64_t T, int32_t num_blocks,
+                      int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                      pa_dtype dtype, void* stream) {
+  g_err.clear();
+  pa_status st = check_geometry(num_kv_heads, num_kv_heads, head_dim, block_size, num_blocks, dtype);
+  if (st != PA_OK) return st;
+  if (T < 0) return fail(PA_ERR_BAD_SHAPE, "T=%lld < 0", (long long)T);
+  if (T == 0) return PA_OK;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping)
+    return fail(PA_ERR_NULL_PTR, "NULL tensor pointer");
+  const int32_t row_bytes = num_kv_heads * head_dim * (dtype == PA_BF16 ? 2 : 4);
+  const uintptr_t mis = (uintptr_t)key | (uintptr_t)value | (uintptr_t)key_cache | (uintptr_t)value_cache;
+  if (mis & 15) return fail(PA_ERR_BAD_SHAPE, "tensors must be 16-byte aligned");
+  hipError_t e = pa::launch_write_kv(key, value, key_cache, value_cache, slot_mapping, T,
+                                     (int64_t)num_blocks * block_size, row_bytes,
+                                     reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "write_kv launch");
+  return PA_OK;
+}
+
+size_t pa_attention_workspace_size(const int32_t* h_query_start_loc, const int32_t* h_seq_lens,
+                                   int32_t R, int32_t num_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, pa_dtype dtype) {
+  g_err.clear();
+  if (check_geometry(num_heads, num_kv_heads, head_dim, block_size, 1, dtype) != PA_OK) return 0;
+  if (R < 0 || (R > 0 && (h_query_start_loc == nullptr || h_seq_lens == nullptr))) {
+    fail(PA_ERR_NULL_PTR, "host mirrors are required");
+    return 0;
+  }
+  // M does not change the plan as long as every sequence fits its row
+  int32_t maxL = 0;
+  for (int32_t r = 0; r < R; ++r) maxL = std::max(maxL, h_seq_lens[r]);
+  const int32_t M = std::max(1, (maxL + block_size - 1) / block_size);
+  pa::PlanShape ps;
+  const int64_t T = R > 0 ? h_query_start_loc[R] : 0;
+  if (make_plan(h_query_start_loc, h_seq_lens, R, T, M, num_heads, num_kv_heads, head_dim,
+                block_size, dtype == PA_BF16, &ps) != PA_OK)
+    return 0;
+  return pa::workspace_layout(ps, num_heads, head_dim).total;
+}
+
+pa_status pa_attention(void* out, const void* query, const void* key_cache,
+                       const void* value_cache, const int32_t* block_table,
+                       int32_t max_blocks_per_req, const int32_t* query_start_loc,
+                       const int32_t* seq_lens, const int32_t* num_computed_tokens,
+                       const int32_t* h_query_start_loc, const int32_t* h_seq_lens, int32_t R,
+                       int64_t T, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t num_blocks, int32_t block_size, float scale, pa_dtype dtype,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  pa_status st = check_geometry(num_heads, num_kv_heads, head_dim, block_size, num_blocks, dtype);
+  if (st != PA_OK) return st;
+  if (max_blocks_per_req <= 0) return fail(PA_ERR_BAD_SHAPE, "max_blocks_per_req=%d", max_blocks_per_req);
+  const bool bf16 = dtype == PA_BF16;
+  pa::PlanShape ps;
+  st = make_plan(h_query_start_loc, h_seq_lens, R, T, max_blocks_per_req, num_heads, num_kv_heads,
+                 head_dim, block_size, bf16, &ps);
+  if (st != PA_OK) return st;
+  if (ps.n_rw == 0 && ps.n_ck == 0) return PA_OK;
+  if (!out || !query || !key_cache || !value_cache || !block_table || !query_start_loc ||
+      !seq_lens || !num_computed_tokens || !workspace)
+    return fail(PA_ERR_NULL_PTR, "NULL device pointer");
+  const uintptr_t mis = (uintptr_t)out | (uintptr_t)query | (uintptr_t)key_cache | (uintptr_t)value_cache;
+  if (mis & 15) return fail(PA_ERR_BAD_SHAPE, "tensors must be 16-byte aligned");
+  if ((uintptr_t)workspace & 255) return fail(PA_ERR_BAD_SHAPE, "workspace must be 256-byte aligned");
+  const pa::WorkspaceLayout wl = pa::workspace_layout(ps, num_heads, head_dim);
+  if (workspace_bytes < wl.total)
+    return fail(PA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < needed %zu bytes", workspace_bytes, wl.total);
+  if (!(scale > 0.f) || !(scale < 1e30f)) return fail(PA_ERR_BAD_SHAPE, "scale must be positive and finite");
+
+  char* ws = static_cast<char*>(workspace);
+  pa::AttnArgs a{};
+  a.out = out;
+  a.query = query;
+  a.kcache = key_cache;
+  a.vcache = value_cache;
+  a.block_table = block_table;
+  a.qsl = query_start_loc;
+  a.seq_lens = seq_lens;
+  a.num_computed = num_computed_tokens;
+  a.M = max_blocks_per_req;
+  a.R = R;
+  a.Hq = num_heads;
+  a.Hkv = num_kv_heads;
+  a.D = head_dim;
+  a.B = block_size;
+  a.num_blocks = num_blocks;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.bf16 = bf16;
+  a.ps = ps;
+  a.items_rw = reinterpret_cast<int4*>(ws + wl.off_rw);
+  a.items_ck = reinterpret_cast<int4*>(ws + wl.off_ck);
+  a.merge = reinterpret_cast<int4*>(ws + wl.off_mg);
+  a.ml_part = reinterpret_cast<float*>(ws + wl.off_ml);
+  a.o_part = reinterpret_cast<float*>(ws + wl.off_o);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+  hipError_t e = pa::launch_plan(query_start_loc, seq_lens, ps, a.items_rw, a.items_ck, a.merge, s);
+  if (e != hipSuccess) return hip_fail(e, "plan launch");
+  e = pa::launch_rowwise(a, s);
+  if (e != hipSuccess) return hip_fail(e, "row-wise attention launch");
+  e = pa::launch_chunk(a, s);
+  if (e != hipSuccess) return hip_fail(e, "chunk attention launch");
+  e = pa::launch_merge(a, s);
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return PA_OK;
+}
+
+pa_status pa_validate_metadata(const int32_t* h_query_start_loc, const int32_t* h_seq_lens,
+                               const int32_t* h_num_computed, const int32_t* h_block_table,
+                               int32_t max_blocks_per_req, const int64_t* h_slot_mapping,
+                               int32_t R, int64_t T, int32_t num_blocks, int32_t block_size) {
+  g_err.clear();
+  if (R < 0 || T < 0 || num_blocks <= 0 || block_size <= 0 || max_blocks_per_req < 0)
+    return fail(PA_ERR_BAD_SHAPE, "bad sizes");
+  if (h_query_start_loc == nullptr) return fail(PA_ERR_NULL_PTR, "query_start_loc is NULL");
+  if (R > 0 && (h_seq_lens == nullptr || h_num_computed == nullptr || h_block_table == nullptr))
+    return fail(PA_ERR_NULL_PTR, "NULL metadata array");
+  if (h_query_start_loc[0] != 0) return fail(PA_ERR_INCONSISTENT_METADATA, "query_start_loc[0] != 0");
+  for (int32_t r = 0; r < R; ++r) {
+    const int32_t q = h_query_start_loc[r + 1] - h_query_start_loc[r];
+    if (q < 0) return fail(PA_ERR_INCONSISTENT_METADATA, "query_start_loc decreases at %d", r);
+    if ((int64_t)h_num_computed[r] + q != h_seq_lens[r] || h_num_computed[r] < 0)
+      return fail(PA_ERR_INCONSISTENT_METADATA, "seq_lens[%d]=%d != num_computed %d + query length %d", r,
+                  h_seq_lens[r], h_num_computed[r], q);
+    const int64_t need = ((int64_t)h_seq_lens[r] + block_size - 1) / block_size;
+    if (need > max_blocks_per_req)
+      return fail(PA_ERR_OUT_OF_RANGE, "request %d needs %lld blocks > %d", r, (long long)need, max_blocks_per_req);
+    for (int64_t j = 0; j < need; ++j) {
+      const int32_t b = h_block_table[(int64_t)r * max_blocks_per_req + j];
+      if (b < 0 || b >= num_blocks)
+        return fail(PA_ERR_OUT_OF_RANGE, "block_table[%d][%lld]=%d outside [0, %d)", r, (long long)j, b, num_blocks);
+    }
+  }
+  if (h_query_start_loc[R] != T) return fail(PA_ERR_INCONSISTENT_METADATA, "query_start_loc[R] != T");
+  if (h_slot_mapping != nullptr && T > 0) {
+    const int64_t nslots = (int64_t)num_blocks * block_size;
+    for (int64_t t = 0; t < T; ++t) {
+      const int64_t s = h_slot_mapping[t];
+      if (s >= nslots) return fail(PA_ERR_OUT_OF_RANGE, "slot_mapping[%lld]=%lld >= %lld", (long long)t, (long long)s, (long long)nslots);
+    }
+    for (int32_t r = 0; r < R; ++r) {
+      const int32_t c = h_num_computed[r];
+      for (int32_t i = h_query_start_loc[r]; i < h_query_start_loc[r + 1]; ++i) {
+        const int64_t s = h_slot_mapping[i];
+        if (s < 0) continue;
+        const int64_t p = (int64_t)c + (i - h_query_start_loc[r]);
+        const int64_t want = (int64_t)h_block_table[(int64_t)r * max_blocks_per_req + p / block_size] * block_size + p % block_size;
+        if (s != want)
+          return fail(PA_ERR_INCONSISTENT_METADATA, "slot_mapping[%d]=%lld but the block table gives %lld", i, (long long)s, (long long)want);
+      }
+    }
+    std::vector<int64_t> live;
+    live.reserve((size_t)T);
+    for (int64_t t = 0; t < T; ++t)
+      if (h_slot_mapping[t] >= 0) live.push_back(h_slot_mapping[t]);
+    std::sort(live.begin(), live.end());
+    for (size_t i = 1; i < live.size(); ++i)
+      if (live[i] == live[i - 1]) return fail(PA_ERR_DUPLICATE_SLOT, "slot %lld written twice", (long long)live[i]);
+  }
+  return PA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,162 @@
+// Internal declarations shared by the host entry points and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa.h"
+
+namespace pa {
+
+// ---------------------------------------------------------------------------
+// Work plan.
+//
+// pa_attention splits the step's query rows into two kinds of work:
+//   * row-wise split-K items (decode rows, and every row of a multi-token
+//     request when the chunk kernel does not handle its dtype): one item is
+//     one query row x one key partition [kb, ke) x one kv head (grid y);
+//   * chunk items (multi-token requests in bf16, matrix-core kernel): one
+//     item is one query tile of TQ tokens x one key segment x one kv head.
+// A query row whose keys were split over several items gets a merge row that
+// combines the partial results by log-sum-exp ("AI Infra入门干货总结…",
+// section "总结": Flash-Decoding splits the KV dimension and normalises the
+// partitions with log-sum-exp).
+//
+// The plan is computed on the device by plan_kernel from query_start_loc and
+// seq_lens, so no host-to-device copy sits on the step's critical path; the
+// host evaluates the same per-request counts (request_counts below, one
+// definition for both sides) from its mirrors to size the launches.
+// ---------------------------------------------------------------------------
+
+// Records (int4):
+//   row-wise item  {r, t, kb, ke | kDirect}   t = flattened query row
+//   chunk item     {r, qt, seg, part_base}    part_base < 0: single segment
+//   merge row      {t, first_part, n_parts, stride}
+// Unused trailing records hold r = -1 / t = -1.
+constexpr int32_t kDirect = (int32_t)0x80000000;
+
+// Number of query tokens per chunk-kernel tile as a function of the GQA group:
+// a tile is always 128 (token, head) rows of one kv head.
+__host__ __device__ inline int32_t chunk_tile_tokens(int32_t G) { return 128 / G; }
+
+struct PlanShape {
+  int32_t R;
+  int32_t T;             // flattened query rows
+  int32_t M;             // block-table row length
+  int32_t B;             // block size
+  int32_t S;             // row-wise partition length (keys), multiple of 16 and of B
+  int32_t rowwise_all;   // 1: multi-token requests go row-wise too
+  int32_t TQ;            // chunk tile tokens
+  int32_t SEG;           // chunk key-segment length, multiple of 64
+  // exact totals for this step (host mirrors); capacities of the tables
+  int32_t n_rw;          // row-wise items (= row-wise partial slots)
+  int32_t n_ck;          // chunk items
+  int32_t n_mg;          // merge rows
+  int32_t n_ck_parts;    // chunk partial slots (after the n_rw row-wise ones)
+};
+
+struct ReqCounts {
+  int32_t rw;
+  int32_t ck;
+  int32_t mg;
+  int32_t ck_parts;
+};
+
+__host__ __device__ inline int32_t cdiv(int32_t a, int32_t b) { return (a + b - 1) / b; }
+
+// Sanitised view of one request: L clamped into the block-table row, q into
+// [0, L].  On the host the same values have already been validated, so the
+// clamps change nothing there; on the device they keep every access inside
+// the caller's buffers even if device metadata disagrees with the mirrors.
+__host__ __device__ inline void sanitize(int32_t& q, int32_t& L, int32_t M, int32_t B) {
+  const int64_t cap = (int64_t)M * B;
+  if (L < 0) L = 0;
+  if ((int64_t)L > cap) L = (int32_t)cap;
+  if (q < 0) q = 0;
+  if (q > L) q = L;
+}
+
+__host__ __device__ inline bool goes_rowwise(int32_t q, const PlanShape& ps) {
+  return q == 1 || (q > 1 && ps.rowwise_all);
+}
+
+__host__ __device__ inline ReqCounts request_counts(int32_t q, int32_t L, const PlanShape& ps) {
+  ReqCounts n{0, 0, 0, 0};
+  if (q <= 0) return n;
+  const int32_t c = L - q;
+  if (goes_rowwise(q, ps)) {
+    for (int32_t i = 0; i < q; ++i) {
+      const int32_t parts = cdiv(c + i + 1, ps.S);
+      n.rw += parts;
+      if (parts > 1) n.mg += 1;
+    }
+  } else {
+    const int32_t nqt = cdiv(q, ps.TQ);
+    for (int32_t qt = 0; qt < nqt; ++qt) {
+      const int32_t tok_end = (qt + 1) * ps.TQ < q ? (qt + 1) * ps.TQ : q;
+      const int32_t nseg = cdiv(c + tok_end, ps.SEG);
+      n.ck += nseg;
+      if (nseg > 1) {
+        n.ck_parts += nseg * ps.TQ;
+        n.mg += tok_end - qt * ps.TQ;
+      }
+    }
+  }
+  return n;
+}
+
+struct WorkspaceLayout {
+  size_t off_rw, off_ck, off_mg, off_ml, off_o, total;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+inline WorkspaceLayout workspace_layout(const PlanShape& ps, int32_t Hq, int32_t D) {
+  WorkspaceLayout w;
+  size_t o = 0;
+  w.off_rw = o; o = align256(o + sizeof(int4) * (size_t)ps.n_rw);
+  w.off_ck = o; o = align256(o + sizeof(int4) * (size_t)ps.n_ck);
+  w.off_mg = o; o = align256(o + sizeof(int4) * (size_t)ps.n_mg);
+  const size_t parts = (size_t)ps.n_rw + (size_t)ps.n_ck_parts;
+  w.off_ml = o; o = align256(o + sizeof(float) * 2 * parts * Hq);
+  w.off_o = o;  o = align256(o + sizeof(float) * parts * Hq * D);
+  w.total = o;
+  return w;
+}
+
+// ---------------------------------------------------------------------------
+// launchers (each returns the launch's hipError_t)
+// ---------------------------------------------------------------------------
+hipError_t launch_write_kv(const void* key, const void* value, void* key_cache, void* value_cache,
+                           const int64_t* slots, int64_t T, int64_t num_slots, int32_t row_bytes,
+                           hipStream_t s);
+
+hipError_t launch_plan(const int32_t* qsl, const int32_t* seq_lens, const PlanShape& ps,
+                       int4* items_rw, int4* items_ck, int4* merge, hipStream_t s);
+
+struct AttnArgs {
+  void* out;
+  const void* query;
+  const void* kcache;
+  const void* vcache;
+  const int32_t* block_table;
+  const int32_t* qsl;
+  const int32_t* seq_lens;
+  const int32_t* num_computed;
+  int32_t M, R, Hq, Hkv, D, B, num_blocks;
+  float scale_log2;   // scale * log2(e): softmax runs in base 2
+  bool bf16;
+  PlanShape ps;
+  int4* items_rw;
+  int4* items_ck;
+  int4* merge;
+  float* ml_part;     // [parts, Hq, 2] (running max in log2 units, sum)
+  float* o_part;      // [parts, Hq, D] unnormalised
+};
+
+hipError_t launch_rowwise(const AttnArgs& a, hipStream_t s);
+hipError_t launch_chunk(const AttnArgs& a, hipStream_t s);
+hipError_t launch_merge(const AttnArgs& a, hipStream_t s);
+bool chunk_kernel_supports(bool bf16, int32_t D, int32_t G);
+
+}  // namespace pa

@@ -1,0 +1,258 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Cache writes and slot mappings must match bit for bit; attention outputs
+within atol = rtol = 1e-5 (fp32) or 1e-2 (bf16), elementwise.  Inputs are the
+seeded synthetic steps of workloads.configs; large steps are checked on
+sampled requests (every cache block those requests own, and sampled query
+rows), which the oracle computes one request at a time.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from helpers import (assert_close, bits, check_requests, oracle_request, run_step,
+                     sample_requests, say, storage_np)
+from workloads import configs, rng
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import paged_kv_attention_reshape_amd as pa  # noqa: E402
+from workloads import _lib as wl  # noqa: E402
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    say(f"\n[gpu-test] {request.node.name}")
+    yield
+    torch.cuda.synchronize()
+
+
+def test_library_is_the_hip_build():
+    assert os.path.exists(pa.LIB_PATH)
+    assert pa.abi_version() == 1
+
+
+def test_generator_device_matches_host_mirror():
+    for dtype, tdt in (("f32", torch.float32), ("bf16", torch.bfloat16)):
+        t = torch.empty((37, 3, 64), dtype=tdt, device="cuda")
+        keys = rng.base_row_keys(rng.key(5, 9), np.arange(37))
+        wl.fill_rows(t, dtype, row_keys=torch.from_numpy(keys.view(np.int64)).cuda())
+        want = rng.row_values(keys, 3 * 64, dtype).reshape(37, 3, 64)
+        assert np.array_equal(bits(storage_np(t)), bits(want))
+        pool = torch.empty((5, 16, 2, 64), dtype=tdt, device="cuda")
+        valid = np.array([0, 16, 3, 9, 1], np.int32)
+        wl.fill_pool(pool, dtype, 1234, torch.from_numpy(valid).cuda(), 16)
+        rows = np.arange(5 * 16)
+        hv = rng.row_values(rng.base_row_keys(1234, rows), 128, dtype).reshape(5, 16, 2, 64)
+        bad = np.arange(16)[None, :] >= valid[:, None]
+        hv[bad] = rng.storage_nan(dtype)
+        assert np.array_equal(bits(storage_np(pool)), bits(hv))
+
+
+def test_c1_tiny_mixed_fp32_full():
+    spec = configs.c1()
+    d, out, sm = run_step(spec, pa)
+    torch.cuda.synchronize()
+    # slot mapping: library (host C++) vs oracle, bit-exact
+    want_sm = oracle.slot_mapping(spec.block_table, spec.query_lens, spec.num_computed, spec.B)
+    assert np.array_equal(sm, want_sm)
+    # whole pool after the write, bit-exact
+    kp = spec.host_pool_blocks("k", np.arange(spec.num_blocks))
+    vp = spec.host_pool_blocks("v", np.arange(spec.num_blocks))
+    rows = np.arange(spec.T)
+    oracle.write_kv(kp, vp, spec.host_rows("k", rows), spec.host_rows("v", rows), want_sm, spec.B)
+    assert np.array_equal(bits(storage_np(d["key_cache"])), bits(kp))
+    assert np.array_equal(bits(storage_np(d["value_cache"])), bits(vp))
+    # every output row
+    want, _ = oracle.attention(spec.host_rows("q", rows), kp, vp, spec.block_table,
+                               spec.query_start_loc, spec.seq_lens, spec.num_computed,
+                               spec.scale, spec.B, "f32")
+    got = storage_np(out).astype(np.float64)
+    err = assert_close(got, want, "f32", "c1")
+    say(f"c1 max abs err {err:.2e}")
+
+
+def test_c2_decode_bf16_sampled():
+    spec = configs.c2()
+    d, out, _ = run_step(spec, pa)
+    torch.cuda.synchronize()
+    longest = int(np.argmax(spec.seq_lens))
+    reqs = sample_requests(spec, 12, seed=2, must=[longest, 0, spec.R - 1])
+    err = check_requests(spec, out, d["key_cache"], d["value_cache"], reqs, what="c2")
+    say(f"c2 requests {reqs} max abs err {err:.2e}")
+
+
+def test_c3_mixed_chunked_bf16_sampled():
+    spec = configs.c3()
+    d, out, _ = run_step(spec, pa)
+    torch.cuda.synchronize()
+    chunks = [int(r) for r in np.nonzero(spec.query_lens > 1)[0]]
+    longest_dec = int(np.argmax(np.where(spec.query_lens == 1, spec.seq_lens, 0)))
+    dec = sample_requests(spec, 10, seed=3, must=[longest_dec])
+    dec = [r for r in dec if spec.query_lens[r] == 1]
+    err = check_requests(spec, out, d["key_cache"], d["value_cache"], chunks, rows_per_req=20,
+                         what="c3 chunk")
+    err2 = check_requests(spec, out, d["key_cache"], d["value_cache"], dec, what="c3 decode")
+    say(f"c3 chunk reqs {chunks} offsets {spec.num_computed[chunks].tolist()} err {err:.2e}; decode err {err2:.2e}")
+
+
+def test_c4_long_decode_bf16_sampled():
+    spec = configs.c4()
+    d, out, _ = run_step(spec, pa)
+    torch.cuda.synchronize()
+    longs = [int(r) for r in np.nonzero(spec.seq_lens == 32768)[0][:3]]
+    reqs = sample_requests(spec, 10, seed=4, must=longs)
+    err = check_requests(spec, out, d["key_cache"], d["value_cache"], reqs, what="c4")
+    say(f"c4 requests {reqs} max abs err {err:.2e}")
+
+
+def test_determinism_bitwise():
+    spec = configs.c2(R=16)
+    d, out1, _ = run_step(spec, pa)
+    _, out2, _ = run_step(spec, pa, dev_inputs=d)
+    torch.cuda.synchronize()
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+
+
+def _small(dtype, Hq, Hkv, D, B, qlens, comp, seed=7, pool_factor=1.5):
+    return configs.custom(f"s{seed}", dtype, Hq, Hkv, D, B, qlens, comp, seed, pool_factor)
+
+
+def test_block_permutation_and_request_order_invariance():
+    spec = _small("bf16", 16, 4, 128, 16, [1, 1, 37, 1, 5], [700, 33, 200, 0, 1000], seed=11)
+    d, base, _ = run_step(spec, pa)
+    torch.cuda.synchronize()
+    # 1) relabel physical blocks (moving the data): outputs bitwise equal
+    g = np.random.default_rng(3)
+    perm = g.permutation(spec.num_blocks)
+    kc = torch.empty_like(d["key_cache"])
+    vc = torch.empty_like(d["value_cache"])
+    pt = torch.from_numpy(perm).cuda()
+    # pool before the write: regenerate, move, then run the step again
+    fresh = spec.device_inputs()
+    kc[pt] = fresh["key_cache"]
+    vc[pt] = fresh["value_cache"]
+    bt2 = np.where(spec.block_table >= 0, perm[np.maximum(spec.block_table, 0)], -1).astype(np.int32)
+    spec2 = configs.StepSpec(**{**spec.__dict__, "block_table": bt2})
+    fresh["key_cache"], fresh["value_cache"] = kc, vc
+    fresh["block_table"] = torch.from_numpy(bt2).cuda()
+    _, out2, _ = run_step(spec2, pa, dev_inputs=fresh)
+    torch.cuda.synchronize()
+    assert torch.equal(out2.view(torch.int16), base.view(torch.int16))
+    # 2) reverse request order: each request's rows bitwise unchanged
+    order = list(range(spec.R))[::-1]
+    qsl = spec.query_start_loc
+    rows = np.concatenate([np.arange(qsl[r], qsl[r + 1]) for r in order])
+    spec3 = configs.StepSpec(**{**spec.__dict__, "query_lens": spec.query_lens[order],
+                                "num_computed": spec.num_computed[order],
+                                "block_table": spec.block_table[order],
+                                "q_row_keys": spec.row_keys("q", rows),
+                                "k_row_keys": spec.row_keys("k", rows),
+                                "v_row_keys": spec.row_keys("v", rows)})
+    _, out3, _ = run_step(spec3, pa)
+    torch.cuda.synchronize()
+    q3 = spec3.query_start_loc
+    for i, r in enumerate(order):
+        assert torch.equal(out3[q3[i]:q3[i + 1]].view(torch.int16),
+                           base[qsl[r]:qsl[r + 1]].view(torch.int16))
+
+
+EDGE = [
+    # dtype, Hq, Hkv, D, B, query lens, computed
+    ("bf16", 8, 8, 128, 16, [1, 1, 1], [0, 15, 16]),          # G=1, L=1, 16, 17
+    ("bf16", 16, 8, 64, 32, [1, 3, 1], [31, 40, 63]),         # G=2, D=64, B=32
+    ("bf16", 64, 8, 128, 32, [1, 2, 1], [5000, 77, 1]),        # G=8
+    ("f32", 32, 8, 128, 16, [1, 9, 1], [300, 50, 2]),          # fp32, D=128
+    ("f32", 8, 1, 64, 48, [1, 20], [100, 13]),                 # G=8 fp32, B=48
+    ("bf16", 32, 8, 128, 16, [0, 1, 0, 4], [10, 99, 0, 2]),    # requests with no rows
+    ("bf16", 32, 8, 128, 64, [1, 1], [4095, 2047]),            # B=64
+]
+
+
+@pytest.mark.parametrize("idx", range(len(EDGE)), ids=[f"edge{i}" for i in range(len(EDGE))])
+def test_edge_shapes(idx):
+    case = EDGE[idx]
+    dtype, Hq, Hkv, D, B, ql, cp = case
+    spec = _small(dtype, Hq, Hkv, D, B, ql, cp, seed=100 + idx)
+    d, out, _ = run_step(spec, pa)
+    torch.cuda.synchronize()
+    err = check_requests(spec, out, d["key_cache"], d["value_cache"], range(spec.R), what=str(case))
+    say(f"{case} err {err:.2e}")
+
+
+@pytest.mark.parametrize("split", [64, 128, 1024])
+def test_forced_partition_sizes(split, monkeypatch):
+    monkeypatch.setenv("PA_SPLIT_TOKENS", str(split))
+    spec = _small("bf16", 32, 8, 128, 16, [1, 1, 1, 7], [3000, 64, 63, 700], seed=split)
+    d, out, _ = run_step(spec, pa)
+    torch.cuda.synchronize()
+    err = check_requests(spec, out, d["key_cache"], d["value_cache"], range(spec.R), what=f"split{split}")
+    say(f"split {split} err {err:.2e}")
+
+
+def test_chunked_prefill_equals_full_prefill_on_gpu():
+    """A 300-token prompt run as five chunks of 64 (each chunk a step that
+    reads the cache the earlier chunks wrote) matches the one-shot prefill."""
+    P, CH, Hq, Hkv, D, B = 300, 64, 32, 8, 128, 16
+    seed = 21
+    full = _small("bf16", Hq, Hkv, D, B, [P], [0], seed=seed)
+    bt = full.block_table
+    pos_keys = {w: rng.base_row_keys(rng.key(seed, tag, 0), np.arange(P))
+                for w, tag in (("q", rng.TAG_Q), ("k", rng.TAG_K), ("v", rng.TAG_V))}
+    full = configs.StepSpec(**{**full.__dict__, "q_row_keys": pos_keys["q"],
+                               "k_row_keys": pos_keys["k"], "v_row_keys": pos_keys["v"]})
+    d, out_full, _ = run_step(full, pa)
+    pools = full.device_inputs()   # fresh NaN pool for the chunked run
+    outs = []
+    for a in range(0, P, CH):
+        b = min(a + CH, P)
+        st = configs.StepSpec(**{**full.__dict__, "query_lens": np.array([b - a], np.int32),
+                                 "num_computed": np.array([a], np.int32),
+                                 "q_row_keys": pos_keys["q"][a:b], "k_row_keys": pos_keys["k"][a:b],
+                                 "v_row_keys": pos_keys["v"][a:b]})
+        di = st.device_inputs(pools=False)
+        di["key_cache"], di["value_cache"] = pools["key_cache"], pools["value_cache"]
+        _, o, _ = run_step(st, pa, dev_inputs=di)
+        outs.append(o)
+    torch.cuda.synchronize()
+    chunked = torch.cat(outs)
+    g_full = oracle.as_f64(storage_np(out_full), "bf16")
+    g_ch = oracle.as_f64(storage_np(chunked), "bf16")
+    want, _, _, _, _, _ = oracle_request(full, 0)
+    assert_close(g_full, want, "bf16", "full prefill")
+    assert_close(g_ch, want, "bf16", "chunked prefill")
+    assert np.max(np.abs(g_full - g_ch)) < 2e-2
+
+
+def test_empty_and_noop_steps():
+    kc = torch.zeros((4, 16, 2, 64), dtype=torch.bfloat16, device="cuda")
+    e = torch.empty((0, 2, 64), dtype=torch.bfloat16, device="cuda")
+    pa.write_kv(e, e, kc, kc.clone(), torch.empty(0, dtype=torch.int64, device="cuda"))
+    out = torch.empty((0, 8, 64), dtype=torch.bfloat16, device="cuda")
+    z = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pa.attention(out, out, kc, kc, torch.zeros((1, 1), dtype=torch.int32, device="cuda"), z,
+                 z[:0], z[:0], np.zeros(1, np.int32), np.zeros(0, np.int32), 0.125)
+
+
+def test_write_kv_skips_negative_slots():
+    spec = _small("bf16", 8, 2, 64, 16, [3, 2], [5, 0], seed=5)
+    d = spec.device_inputs()
+    before_k = storage_np(d["key_cache"]).copy()
+    sm = torch.tensor([-1, 6 + int(spec.block_table[0, 0]) * 16, -1, -5, 1 + int(spec.block_table[1, 0]) * 16],
+                      dtype=torch.int64, device="cuda")
+    pa.write_kv(d["key"], d["value"], d["key_cache"], d["value_cache"], sm)
+    torch.cuda.synchronize()
+    after_k = storage_np(d["key_cache"])
+    changed = np.argwhere(np.any(bits(after_k) != bits(before_k), axis=(2, 3)))
+    b0, b1 = int(spec.block_table[0, 0]), int(spec.block_table[1, 0])
+    assert sorted(map(tuple, changed.tolist())) == sorted([(b0, 6), (b1, 1)])
+    kn = storage_np(d["key"])
+    assert np.array_equal(bits(after_k[b0, 6]), bits(kn[1]))
+    assert np.array_equal(bits(after_k[b1, 1]), bits(kn[4]))
