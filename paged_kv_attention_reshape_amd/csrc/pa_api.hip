@@ -73,6 +73,34 @@ int32_t choose_split(int64_t rowwise_keys, int32_t Hkv, int32_t B) {
   return (int32_t)s;
 }
 
+// Key-segment length of the chunk kernel: a multiple of 64 keys between 512
+// and the kernel's limit, sized so the chunk work spreads over about eight
+// workgroups per compute unit (long histories are cut into segments that the
+// merge pass recombines).
+int32_t choose_segment(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R, int32_t M,
+                       int32_t B, int32_t Hkv, const pa::PlanShape& ps) {
+  const int64_t limit = pa::chunk_max_segment(B) / 64 * 64;
+  const int forced = env_int("PA_CHUNK_SEG", 0);
+  if (forced > 0) return (int32_t)std::min<int64_t>(limit, (forced + 63) / 64 * 64);
+  int64_t tiles = 0;  // 64-key tiles of all chunk work items, one kv head
+  for (int32_t r = 0; r < R; ++r) {
+    int32_t q = h_qsl[r + 1] - h_qsl[r];
+    int32_t L = h_seq_lens[r];
+    pa::sanitize(q, L, M, B);
+    if (q <= 1 || pa::goes_rowwise(q, ps)) continue;
+    const int32_t c = L - q;
+    for (int32_t t0 = 0; t0 < q; t0 += ps.TQ) {
+      const int32_t kmax = c + std::min(t0 + ps.TQ, q);
+      tiles += (kmax + 63) / 64;
+    }
+  }
+  const int64_t target_items = 256 * 8;
+  const int64_t per_item = std::max<int64_t>(1, tiles * Hkv / target_items);
+  int64_t seg = 512;
+  while (seg < per_item * 64 && seg * 2 <= limit) seg *= 2;
+  return (int32_t)std::min(seg, limit);
+}
+
 // Validates the host mirrors and fills the plan shape (exact table sizes).
 pa_status make_plan(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R, int64_t T,
                     int32_t M, int32_t Hq, int32_t Hkv, int32_t D, int32_t B, bool bf16,
@@ -108,8 +136,7 @@ pa_status make_plan(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R, 
     }
   }
   ps.S = choose_split(rowwise_keys, Hkv, B);
-  const int seg = env_int("PA_CHUNK_SEG", 0);
-  if (seg > 0) ps.SEG = (seg + 63) / 64 * 64;
+  ps.SEG = choose_segment(h_qsl, h_seq_lens, R, M, B, Hkv, ps);
   int64_t n_rw = 0, n_ck = 0, n_mg = 0, n_parts = 0;
   for (int32_t r = 0; r < R; ++r) {
     int32_t q = h_qsl[r + 1] - h_qsl[r];

@@ -158,5 +158,7 @@ hipError_t launch_rowwise(const AttnArgs& a, hipStream_t s);
 hipError_t launch_chunk(const AttnArgs& a, hipStream_t s);
 hipError_t launch_merge(const AttnArgs& a, hipStream_t s);
 bool chunk_kernel_supports(bool bf16, int32_t D, int32_t G);
+// Longest key segment one chunk work item may cover (its block ids live in LDS).
+int32_t chunk_max_segment(int32_t B);
 
 }  // namespace pa

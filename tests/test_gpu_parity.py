@@ -256,3 +256,39 @@ def test_write_kv_skips_negative_slots():
     kn = storage_np(d["key"])
     assert np.array_equal(bits(after_k[b0, 6]), bits(kn[1]))
     assert np.array_equal(bits(after_k[b1, 1]), bits(kn[4]))
+
+
+CHUNK_CASES = [
+    # Hq, Hkv, D, B, query lens, computed, forced key segment (0 = planner's choice)
+    (32, 8, 128, 16, [100, 1, 300], [0, 500, 1000], 0),
+    (32, 8, 128, 16, [100, 1, 300], [0, 500, 1000], 512),
+    (8, 8, 64, 32, [77, 128], [33, 1000], 512),          # G=1, D=64
+    (16, 8, 128, 48, [65, 3], [700, 2], 512),            # G=2, B=48
+    (64, 8, 128, 32, [17, 40], [4000, 0], 1024),         # G=8
+    (32, 8, 128, 64, [512], [2500], 512),                # B=64
+    (32, 8, 64, 16, [2, 33, 64], [0, 31, 4095], 0),      # tiny chunks, D=64
+]
+
+
+@pytest.mark.parametrize("idx", range(len(CHUNK_CASES)), ids=[f"chunk{i}" for i in range(len(CHUNK_CASES))])
+def test_chunk_kernel_shapes(idx, monkeypatch):
+    Hq, Hkv, D, B, ql, cp, seg = CHUNK_CASES[idx]
+    if seg:
+        monkeypatch.setenv("PA_CHUNK_SEG", str(seg))
+    spec = _small("bf16", Hq, Hkv, D, B, ql, cp, seed=300 + idx)
+    d, out, _ = run_step(spec, pa)
+    torch.cuda.synchronize()
+    err = check_requests(spec, out, d["key_cache"], d["value_cache"], range(spec.R), what=f"chunk{idx}")
+    say(f"chunk case {idx} err {err:.2e}")
+
+
+def test_chunk_kernel_agrees_with_rowwise_path(monkeypatch):
+    spec = _small("bf16", 32, 8, 128, 16, [200, 1, 64], [300, 40, 0], seed=77)
+    d, out_ck, _ = run_step(spec, pa)
+    monkeypatch.setenv("PA_FORCE_ROWWISE", "1")
+    fresh = spec.device_inputs()
+    _, out_rw, _ = run_step(spec, pa, dev_inputs=fresh)
+    torch.cuda.synchronize()
+    a = oracle.as_f64(storage_np(out_ck), "bf16")
+    b = oracle.as_f64(storage_np(out_rw), "bf16")
+    assert np.max(np.abs(a - b)) < 2e-2
