@@ -110,6 +110,27 @@ pa_status pa_build_step_metadata(const int32_t* h_query_lens, const int32_t* h_n
                                  int64_t slot_capacity);
 
 /*
+ * pa_compute_slot_mapping -- the same slot mapping, computed on the device.
+ *
+ * [P1] "Paged Attention": token i of request r (flattened index
+ * query_start_loc[r] + i) is at position p = num_computed_tokens[r] + i and
+ * goes to slot block_table[r][p / block_size] * block_size + p % block_size.
+ *
+ *   slot_mapping        device int64 [T] (written)
+ *   block_table         device int32 [R, max_blocks_per_req]
+ *   query_start_loc     device int32 [R + 1]
+ *   num_computed_tokens device int32 [R]
+ * A token whose block-table entry lies outside [0, num_blocks), or whose
+ * position is past the end of its block-table row, gets slot -1 (pa_write_kv
+ * then writes nothing for it; pa_validate_metadata reports the cause).
+ * Tokens outside every request's range are left untouched.
+ */
+pa_status pa_compute_slot_mapping(int64_t* slot_mapping, const int32_t* block_table,
+                                  int32_t max_blocks_per_req, const int32_t* query_start_loc,
+                                  const int32_t* num_computed_tokens, int32_t R, int64_t T,
+                                  int32_t num_blocks, int32_t block_size, void* stream);
+
+/*
  * pa_write_kv -- scatter the step's new K/V rows into the paged cache.
  *
  * [P1] "Paged Attention" (slot_idx = block_idx * block_size + block_offset;
@@ -184,6 +205,19 @@ pa_status pa_attention(void* out, const void* query, const void* key_cache,
                        int64_t T, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                        int32_t num_blocks, int32_t block_size, float scale, pa_dtype dtype,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_set_profiling_events -- optional per-kernel timing hook (tests and
+ * benchmarks).
+ *
+ * events: host array of n_events == 5 hipEvent_t handles created by the
+ * caller on the current device, or NULL / n_events == 0 to disable.  While set
+ * on the calling thread, every pa_attention call records, on its stream,
+ * events[0] before its first launch and events[1], [2], [3], [4] after the
+ * plan, row-wise split-K, chunk and merge launches.  The library copies the
+ * handles; the caller keeps ownership of the events.
+ */
+pa_status pa_set_profiling_events(void* const* events, int32_t n_events);
 
 /*
  * pa_validate_metadata -- exact host-side check of a step's metadata (for

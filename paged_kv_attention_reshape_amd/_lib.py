@@ -27,7 +27,8 @@ STATUS = {
 
 EXPORTS = [
     "pa_abi_version", "pa_status_str", "pa_last_error", "pa_build_step_metadata",
-    "pa_write_kv", "pa_attention_workspace_size", "pa_attention", "pa_validate_metadata",
+    "pa_compute_slot_mapping", "pa_write_kv", "pa_attention_workspace_size", "pa_attention",
+    "pa_set_profiling_events", "pa_validate_metadata",
 ]
 
 
@@ -62,6 +63,11 @@ def lib():
     L.pa_build_step_metadata.argtypes = [_i32p, _i32p, ctypes.c_int32, _i32p, ctypes.c_int32,
                                          ctypes.c_int32, ctypes.c_int32, _i32p, _i32p, _i64p,
                                          ctypes.c_int64]
+    L.pa_compute_slot_mapping.restype = ctypes.c_int
+    L.pa_compute_slot_mapping.argtypes = [_vp, _vp, ctypes.c_int32, _vp, _vp, ctypes.c_int32,
+                                          ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _vp]
+    L.pa_set_profiling_events.restype = ctypes.c_int
+    L.pa_set_profiling_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]
     L.pa_write_kv.restype = ctypes.c_int
     L.pa_write_kv.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int64, ctypes.c_int32,
                               ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int, _vp]
@@ -164,6 +170,28 @@ def validate_metadata(query_start_loc, seq_lens, num_computed, block_table, slot
     _check(lib().pa_validate_metadata(_p32(qsl), _p32(sl), _p32(nc), _p32(bt),
                                       bt.shape[1] if bt.ndim == 2 else 0, _p64(sm), R, T,
                                       num_blocks, block_size), "pa_validate_metadata")
+
+
+def compute_slot_mapping(slot_mapping, block_table, query_start_loc, num_computed,
+                         num_blocks: int, block_size: int, stream=None) -> None:
+    """Device slot mapping: slot_mapping int64 [T] (written) from block_table
+    [R, M], query_start_loc [R+1] and num_computed [R] (device tensors)."""
+    R = int(num_computed.shape[0])
+    T = int(slot_mapping.shape[0])
+    M = block_table.shape[1] if block_table.dim() == 2 else 1
+    _check(lib().pa_compute_slot_mapping(_ptr(slot_mapping), _ptr(block_table), M,
+                                         _ptr(query_start_loc), _ptr(num_computed), R, T,
+                                         num_blocks, block_size, ctypes.c_void_p(_stream(stream))),
+           "pa_compute_slot_mapping")
+
+
+def set_profiling_events(events) -> None:
+    """events: 5 torch.cuda.Event (enable_timing=True) or None to disable."""
+    if not events:
+        _check(lib().pa_set_profiling_events(None, 0), "pa_set_profiling_events")
+        return
+    arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    _check(lib().pa_set_profiling_events(arr, len(events)), "pa_set_profiling_events")
 
 
 def write_kv(key, value, key_cache, value_cache, slot_mapping, stream=None) -> None:

@@ -43,7 +43,39 @@ write_kv_kernel(const uint4* __restrict__ key, const uint4* __restrict__ value,
   }
 }
 
+// Slot mapping on the device: one workgroup per request, threads over its
+// tokens.  Position p of request r maps to block_table[r][p / B] * B + p % B.
+__global__ void __launch_bounds__(kThreads)
+slot_mapping_kernel(int64_t* __restrict__ slots, const int32_t* __restrict__ block_table,
+                    int32_t M, const int32_t* __restrict__ qsl, const int32_t* __restrict__ num_computed,
+                    int64_t T, int32_t num_blocks, int32_t B) {
+  const int r = blockIdx.x;
+  const int64_t t0 = qsl[r];
+  int64_t q = (int64_t)qsl[r + 1] - t0;
+  if (t0 < 0 || t0 > T) return;
+  if (q > T - t0) q = T - t0;
+  const int64_t c = num_computed[r];
+  for (int64_t i = threadIdx.x; i < q; i += blockDim.x) {
+    const int64_t p = c + i;
+    const int64_t j = p / B;
+    int64_t s = -1;
+    if (p >= 0 && j < M) {
+      const int32_t blk = block_table[(int64_t)r * M + j];
+      if (blk >= 0 && blk < num_blocks) s = (int64_t)blk * B + p % B;
+    }
+    slots[t0 + i] = s;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_slot_mapping(int64_t* slots, const int32_t* block_table, int32_t M,
+                               const int32_t* qsl, const int32_t* num_computed, int32_t R,
+                               int64_t T, int32_t num_blocks, int32_t B, hipStream_t s) {
+  hipLaunchKernelGGL(slot_mapping_kernel, dim3(R), dim3(kThreads), 0, s, slots, block_table, M,
+                     qsl, num_computed, T, num_blocks, B);
+  return hipGetLastError();
+}
 
 hipError_t launch_write_kv(const void* key, const void* value, void* key_cache, void* value_cache,
                            const int64_t* slots, int64_t T, int64_t num_slots, int32_t row_bytes,

@@ -18,6 +18,12 @@
 namespace {
 
 thread_local std::string g_err;
+thread_local hipEvent_t g_prof[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
+thread_local bool g_prof_on = false;
+
+void prof_mark(int i, hipStream_t s) {
+  if (g_prof_on) (void)hipEventRecord(g_prof[i], s);
+}
 
 pa_status fail(pa_status s, const char* fmt, ...) {
   char buf[512];
@@ -223,6 +229,38 @@ pa_status pa_build_step_metadata(const int32_t* h_query_lens, const int32_t* h_n
   return PA_OK;
 }
 
+pa_status pa_compute_slot_mapping(int64_t* slot_mapping, const int32_t* block_table,
+                                  int32_t max_blocks_per_req, const int32_t* query_start_loc,
+                                  const int32_t* num_computed_tokens, int32_t R, int64_t T,
+                                  int32_t num_blocks, int32_t block_size, void* stream) {
+  g_err.clear();
+  if (R < 0 || T < 0 || max_blocks_per_req < 0 || num_blocks <= 0 || block_size <= 0)
+    return fail(PA_ERR_BAD_SHAPE, "bad sizes");
+  if (R == 0 || T == 0) return PA_OK;
+  if (!slot_mapping || !block_table || !query_start_loc || !num_computed_tokens)
+    return fail(PA_ERR_NULL_PTR, "NULL device pointer");
+  hipError_t e = pa::launch_slot_mapping(slot_mapping, block_table, max_blocks_per_req,
+                                         query_start_loc, num_computed_tokens, R, T, num_blocks,
+                                         block_size, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "slot mapping launch");
+  return PA_OK;
+}
+
+pa_status pa_set_profiling_events(void* const* events, int32_t n_events) {
+  g_err.clear();
+  if (events == nullptr || n_events == 0) {
+    g_prof_on = false;
+    return PA_OK;
+  }
+  if (n_events != 5) return fail(PA_ERR_BAD_SHAPE, "n_events must be 5 (or 0)");
+  for (int i = 0; i < 5; ++i) {
+    if (events[i] == nullptr) return fail(PA_ERR_NULL_PTR, "event %d is NULL", i);
+    g_prof[i] = reinterpret_cast<hipEvent_t>(events[i]);
+  }
+  g_prof_on = true;
+  return PA_OK;
+}
+
 pa_status pa_write_kv(const void* key, const void* value, void* key_cache, void* value_cache,
                       const int64_t* slot_mapping, int64_t T, int32_t num_blocks,
                       int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
@@ -321,14 +359,19 @@ pa_status pa_attention(void* out, const void* query, const void* key_cache,
   a.o_part = reinterpret_cast<float*>(ws + wl.off_o);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
+  prof_mark(0, s);
   hipError_t e = pa::launch_plan(query_start_loc, seq_lens, ps, a.items_rw, a.items_ck, a.merge, s);
   if (e != hipSuccess) return hip_fail(e, "plan launch");
+  prof_mark(1, s);
   e = pa::launch_rowwise(a, s);
   if (e != hipSuccess) return hip_fail(e, "row-wise attention launch");
+  prof_mark(2, s);
   e = pa::launch_chunk(a, s);
   if (e != hipSuccess) return hip_fail(e, "chunk attention launch");
+  prof_mark(3, s);
   e = pa::launch_merge(a, s);
   if (e != hipSuccess) return hip_fail(e, "merge launch");
+  prof_mark(4, s);
   return PA_OK;
 }
 

@@ -131,6 +131,10 @@ hipError_t launch_write_kv(const void* key, const void* value, void* key_cache, 
                            const int64_t* slots, int64_t T, int64_t num_slots, int32_t row_bytes,
                            hipStream_t s);
 
+hipError_t launch_slot_mapping(int64_t* slots, const int32_t* block_table, int32_t M,
+                               const int32_t* qsl, const int32_t* num_computed, int32_t R,
+                               int64_t T, int32_t num_blocks, int32_t B, hipStream_t s);
+
 hipError_t launch_plan(const int32_t* qsl, const int32_t* seq_lens, const PlanShape& ps,
                        int4* items_rw, int4* items_ck, int4* merge, hipStream_t s);
 

@@ -292,3 +292,39 @@ def test_chunk_kernel_agrees_with_rowwise_path(monkeypatch):
     a = oracle.as_f64(storage_np(out_ck), "bf16")
     b = oracle.as_f64(storage_np(out_rw), "bf16")
     assert np.max(np.abs(a - b)) < 2e-2
+
+
+def test_device_slot_mapping_matches_oracle():
+    for spec in (configs.c1(), configs.c3()):
+        d = spec.device_inputs(pools=False)
+        sm = torch.full((spec.T,), -7, dtype=torch.int64, device="cuda")
+        pa.compute_slot_mapping(sm, d["block_table"], d["query_start_loc"], d["num_computed"],
+                                spec.num_blocks, spec.B)
+        torch.cuda.synchronize()
+        want = oracle.slot_mapping(spec.block_table, spec.query_lens, spec.num_computed, spec.B)
+        assert np.array_equal(sm.cpu().numpy(), want)
+    # an out-of-range block id gives slot -1 (nothing is written for that token)
+    spec = _small("bf16", 8, 2, 64, 16, [2, 1], [14, 3], seed=9)
+    bt = spec.block_table.copy()
+    bt[0, 1] = spec.num_blocks + 5
+    d = spec.device_inputs(pools=False)
+    sm = torch.empty((spec.T,), dtype=torch.int64, device="cuda")
+    pa.compute_slot_mapping(sm, torch.from_numpy(bt).cuda(), d["query_start_loc"], d["num_computed"],
+                            spec.num_blocks, spec.B)
+    torch.cuda.synchronize()
+    got = sm.cpu().numpy()
+    assert got[1] == -1 and got[0] == bt[0, 0] * 16 + 14 and got[2] == bt[1, 0] * 16 + 3
+
+
+def test_profiling_events_bracket_the_kernels():
+    spec = configs.c2(R=32)
+    d = spec.device_inputs()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    pa.set_profiling_events(ev)
+    try:
+        run_step(spec, pa, dev_inputs=d)
+    finally:
+        pa.set_profiling_events(None)
+    torch.cuda.synchronize()
+    ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(4)]
+    assert all(m >= 0 for m in ms) and ms[1] > 0
