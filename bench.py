@@ -1,0 +1,285 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-KV attention step on one MI355X.
+
+One step = the whole hot path over one synthetic batch, all on the device:
+  slot mapping -> write_kv -> attention (plan, split-K decode rows, bf16 MFMA
+  prefill chunks, log-sum-exp merge).
+Default workload: the mixed chunked-prefill step (3 prefill chunks of 512
+tokens at seeded offsets into 16384-token prompts + 512 decode requests with
+lognormal contexts, median 2048; Llama-3-8B heads: 32 q, 8 kv, head_dim 128,
+block 16, bf16), i.e. the configuration that exercises every part of the step.
+
+Prints ONE JSON line.  `value` is the decode KV-read bandwidth (algorithmic
+bytes of the decode rows / time of the split-K and merge kernels in the timed
+steps); chunk TFLOP/s, per-kernel times, the roofline of the dominant kernel
+and a CPU-oracle baseline ride along.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode KV-read GB/s (% HBM peak) + prefill-chunk TFLOP/s (% MFMA) per step"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak, published
+KERNEL_SOURCES = {
+    "rowwise": "paged_kv_attention_reshape_amd/csrc/k_rowwise.hip",
+    "chunk": "paged_kv_attention_reshape_amd/csrc/k_chunk.hip",
+}
+
+
+def source_hash(rel: str) -> str:
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="c3", choices=["c2", "c3", "c4"])
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="budget of oracle work for the CPU baseline (0 disables it)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="instead of the step, run a plain 1 GiB device copy a few times "
+                        "(reference for scaling the FETCH_SIZE / WRITE_SIZE counters)")
+    return p.parse_args()
+
+
+def copy_calibration():
+    """A plain device-to-device copy of exactly 1 GiB, three times: the HBM
+    byte counters of a profiling run of this mode give the counter-to-bytes
+    scale (2^30 bytes read and 2^30 bytes written per copy)."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
+
+
+def cpu_baseline(spec, d, budget_s):
+    """Time the fp64 oracle on a bounded sample of the same step: the decode
+    requests in flattened order until the time budget is spent.  The oracle
+    gets the generator's pre-write pool blocks and the step's query / new K/V
+    rows (copied from the device generator before any step ran) and does its
+    own slot mapping, write, gather and attention."""
+    import numpy as np
+    import torch
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    def host(t):
+        t = t.detach().cpu()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+    qsl = spec.query_start_loc
+    dec = [r for r in range(spec.R) if spec.query_lens[r] == 1]
+    spent = 0.0
+    bytes_done = 0
+    n = 0
+    for r in dec:
+        if spent >= budget_s:
+            break
+        L = int(spec.seq_lens[r])
+        nblk = -(-L // spec.B)
+        ids = torch.from_numpy(spec.block_table[r, :nblk].astype(np.int64)).to(d["key_cache"].device)
+        kp = host(d["key_cache"].index_select(0, ids))
+        vp = host(d["value_cache"].index_select(0, ids))
+        t = int(qsl[r])
+        qrow = host(d["query"][t:t + 1])
+        knew = host(d["key"][t:t + 1])
+        vnew = host(d["value"][t:t + 1])
+        mini = np.arange(nblk, dtype=np.int32)[None]
+        t0 = time.perf_counter()
+        sm = oracle.slot_mapping(mini, [1], [L - 1], spec.B)
+        oracle.write_kv(kp, vp, knew, vnew, sm, spec.B)
+        K = oracle.gather_kv(kp, mini[0], L, spec.B)
+        V = oracle.gather_kv(vp, mini[0], L, spec.B)
+        oracle.attention_rows(qrow, K, V, [L - 1], spec.scale, spec.dtype)
+        spent += time.perf_counter() - t0
+        bytes_done += L * spec.Hkv * spec.D * 2 * spec.esize + 2 * spec.Hq * spec.D * spec.esize \
+            + 4 * nblk + 12
+        n += 1
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {
+        "value": round(bytes_done / spent / 1e9, 4) if spent > 0 else None,
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{n} of {len(dec)} decode requests of the same step (fp64 numpy oracle: "
+                  f"slot mapping, write, gather, attention), {spent:.1f} s of oracle time",
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def load_traffic(kernel: str):
+    """HBM traffic per launch measured by rocprofv3 counters (FETCH_SIZE,
+    WRITE_SIZE), scaled by the copy-kernel calibration, if a summary exists for
+    the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_c3_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        js = json.load(f)
+    if js.get("source_hash") != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return js.get("traffic_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the step shards by request or kv head with no exchange; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import numpy as np
+    import torch
+
+    import paged_kv_attention_reshape_amd as pa
+    from workloads import configs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pa.lib()  # fail loudly if the HIP library is missing
+
+    spec = configs.BUILDERS[args.workload]()
+    d = spec.device_inputs(device=dev)
+    torch.cuda.synchronize()
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(spec, d, args.cpu_seconds)
+
+    qsl_h, sl_h = spec.query_start_loc, spec.seq_lens
+    out = torch.empty_like(d["query"])
+    slot_mapping = torch.empty((spec.T,), dtype=torch.int64, device=dev)
+    ws = pa.Workspace(dev)
+    ws.get(pa.attention_workspace_size(qsl_h, sl_h, spec.Hq, spec.Hkv, spec.D, spec.B,
+                                       pa.PA_BF16 if spec.dtype == "bf16" else pa.PA_F32))
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        if events is not None:
+            events[0].record(stream)
+        pa.compute_slot_mapping(slot_mapping, d["block_table"], d["query_start_loc"],
+                                d["num_computed"], spec.num_blocks, spec.B)
+        if events is not None:
+            events[1].record(stream)
+        pa.write_kv(d["key"], d["value"], d["key_cache"], d["value_cache"], slot_mapping)
+        if events is not None:
+            events[2].record(stream)
+            pa.set_profiling_events(events[3:8])
+        pa.attention(out, d["query"], d["key_cache"], d["value_cache"], d["block_table"],
+                     d["query_start_loc"], d["seq_lens"], d["num_computed"], qsl_h, sl_h,
+                     spec.scale, workspace=ws)
+        if events is not None:
+            pa.set_profiling_events(None)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_begin.record(stream)
+    for i in range(args.steps):
+        step(ev[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_begin.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+
+    names = ["slot_mapping", "write_kv", "launch_gap", "plan", "rowwise", "chunk", "merge"]
+    acc = {k: 0.0 for k in names}
+    for e in ev:
+        for k, (a, b) in zip(names, [(0, 1), (1, 2), (2, 3), (3, 4), (4, 5), (5, 6), (6, 7)]):
+            acc[k] += e[a].elapsed_time(e[b])
+    us = {k: 1e3 * v / args.steps for k, v in acc.items()}
+
+    dec_bytes = spec.decode_bytes()
+    chunk_fl = spec.chunk_flops()
+    dec_s = (us["rowwise"] + us["merge"]) * 1e-6
+    value = dec_bytes / dec_s / 1e9 if dec_s > 0 else 0.0
+    rw_gbs = dec_bytes / (us["rowwise"] * 1e-6) / 1e9 if us["rowwise"] > 0 else 0.0
+    chunk_tf = chunk_fl / (us["chunk"] * 1e-6) / 1e12 if us["chunk"] > 0 and chunk_fl else 0.0
+    traffic = load_traffic("rowwise")
+
+    n_dec = int(np.sum(spec.query_lens == 1))
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": configs.WORKLOADS[args.workload],
+            "requests": spec.R, "tokens": spec.T, "decode_rows": n_dec,
+            "chunk_rows": int(spec.T - n_dec), "num_heads": spec.Hq, "num_kv_heads": spec.Hkv,
+            "head_dim": spec.D, "block_size": spec.B, "num_blocks": spec.num_blocks,
+            "seed": spec.seed,
+        },
+        "decode_frac_hbm": round(value / HBM_PEAK_GBS, 4),
+        "chunk_tflops": round(chunk_tf, 2),
+        "chunk_frac_mfma": round(chunk_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+        "tokens_per_s": round(spec.T / (ms_step * 1e-3), 1),
+        "kernel_us": {k: round(v, 2) for k, v in us.items()},
+        "decode_bytes_per_step": dec_bytes,
+        "chunk_flops_per_step": chunk_fl,
+        "write_kv_gbs": round(spec.write_bytes() / (us["write_kv"] * 1e-6) / 1e9, 1) if us["write_kv"] > 0 else None,
+        "wall_s_timed": round(wall, 4),
+        "roofline": {
+            "kernel": "rowwise split-K decode",
+            "bound": "hbm",
+            "achieved": round(rw_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(rw_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+        },
+        "chunk_roofline": {
+            "kernel": "bf16 MFMA prefill chunk",
+            "bound": "mfma",
+            "achieved": round(chunk_tf, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(chunk_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
