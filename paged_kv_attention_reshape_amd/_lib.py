@@ -190,6 +190,9 @@ def set_profiling_events(events) -> None:
     if not events:
         _check(lib().pa_set_profiling_events(None, 0), "pa_set_profiling_events")
         return
+    for e in events:           # torch creates the event handle on first record
+        if not e.cuda_event:
+            e.record()
     arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
     _check(lib().pa_set_profiling_events(arr, len(events)), "pa_set_profiling_events")
 

@@ -304,7 +304,7 @@ def test_device_slot_mapping_matches_oracle():
         want = oracle.slot_mapping(spec.block_table, spec.query_lens, spec.num_computed, spec.B)
         assert np.array_equal(sm.cpu().numpy(), want)
     # an out-of-range block id gives slot -1 (nothing is written for that token)
-    spec = _small("bf16", 8, 2, 64, 16, [2, 1], [14, 3], seed=9)
+    spec = _small("bf16", 8, 2, 64, 16, [2, 1], [15, 3], seed=9)   # request 0 spans 2 blocks
     bt = spec.block_table.copy()
     bt[0, 1] = spec.num_blocks + 5
     d = spec.device_inputs(pools=False)
@@ -313,7 +313,7 @@ def test_device_slot_mapping_matches_oracle():
                             spec.num_blocks, spec.B)
     torch.cuda.synchronize()
     got = sm.cpu().numpy()
-    assert got[1] == -1 and got[0] == bt[0, 0] * 16 + 14 and got[2] == bt[1, 0] * 16 + 3
+    assert got[1] == -1 and got[0] == bt[0, 0] * 16 + 15 and got[2] == bt[1, 0] * 16 + 3
 
 
 def test_profiling_events_bracket_the_kernels():
