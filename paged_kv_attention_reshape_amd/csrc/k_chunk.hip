@@ -36,6 +36,8 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 constexpr int kThreads = 256;  // 4 waves
@@ -43,9 +45,23 @@ constexpr int KT = 64;         // keys per tile
 constexpr int kMaxSegBlocks = 512;
 constexpr float kNegInf = -__builtin_huge_valf();
 
+template <int V>
+struct __integral_constant {
+  static constexpr int value = V;
+  constexpr operator int() const { return V; }
+};
+
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) |
          ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+}
+
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (N > 0) {
+    static_for<N - 1>(f);
+    f(__integral_constant<N - 1>());
+  }
 }
 
 __device__ __forceinline__ float xor32(float x) {
@@ -93,7 +109,7 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(AttnArgs a) {
 
   // block ids of the segment into LDS
   const int blk_first = k0 / a.B;
-  const int nblk = (k1 - 1) / a.B - blk_first + 1;
+  const int nblk = (k1 - 1) / a.B - blk_first + 1;   // (one-time divisions)
   for (int i = tid; i < nblk && i < kMaxSegBlocks; i += kThreads) {
     int b = a.block_table[(int64_t)r * a.M + blk_first + i];
     bt_lds[i] = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
@@ -113,15 +129,13 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(AttnArgs a) {
   const int w_qpos_hi = c + min(tok0 + w_tau_hi, q - 1);
 
   // Q fragment (B operand of S^T = K Q^T): lane holds d = 16kk + 8(lane/32) .. +8
-  bf16x8_t qf[KSTEPS];
+  u32x4_t qf[KSTEPS];
   {
     const char* qrow = static_cast<const char*>(a.query) +
                        ((int64_t)(t0 + tok0 + tau) * a.Hq + hq) * ROWB + (lane >> 5) * 16;
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-      uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qrow + kk * 32) : make_uint4(0, 0, 0, 0);
-      qf[kk] = __builtin_bit_cast(bf16x8_t, v);
-    }
+    for (int kk = 0; kk < KSTEPS; ++kk)
+      qf[kk] = row_ok ? *reinterpret_cast<const u32x4_t*>(qrow + kk * 32) : u32x4_t{0, 0, 0, 0};
   }
   __syncthreads();  // bt_lds ready
 
@@ -129,34 +143,38 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(AttnArgs a) {
   const char* vcache = static_cast<const char*>(a.vcache);
   const int64_t slot_stride = (int64_t)a.Hkv * ROWB;
   const int64_t head_off = (int64_t)g * ROWB;
+  const int lb = 31 - __builtin_clz(a.B);   // block size is a power of two here
+  const int bmask = a.B - 1;
 
-  // global -> register staging of one tile (K and V), 16-byte chunks
-  uint4 kst[LOADS], vst[LOADS];
-  auto load_tile = [&](int kt) {
+  // This thread's 16-byte chunks of every tile: chunk i is key row
+  // (i * kThreads + tid) / CPR of the tile, physical column pchunk, holding
+  // logical column pchunk ^ (key % CPR) (XOR swizzle against LDS conflicts).
+  int ld_key[LOADS], ld_lds[LOADS], ld_col[LOADS];
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int id = i * kThreads + tid;
-      const int key = id / CPR;
-      const int pchunk = id % CPR;
-      const int lchunk = pchunk ^ (key % CPR);
-      int kabs = kt + key;
-      kabs = kabs < k1 ? kabs : k1 - 1;        // rows past the segment: re-read a valid row
-      const int blk = bt_lds[kabs / a.B - blk_first];
-      const int64_t off = ((int64_t)blk * a.B + kabs % a.B) * slot_stride + head_off + lchunk * 16;
-      kst[i] = *reinterpret_cast<const uint4*>(kcache + off);
-      vst[i] = *reinterpret_cast<const uint4*>(vcache + off);
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int id = i * kThreads + tid;
-      const int key = id / CPR;
-      const int pchunk = id % CPR;
-      *reinterpret_cast<uint4*>(k_lds + buf * TILE_BYTES + key * ROWB + pchunk * 16) = kst[i];
-      *reinterpret_cast<uint4*>(v_lds + buf * TILE_BYTES + key * ROWB + pchunk * 16) = vst[i];
-    }
-  };
+  for (int i = 0; i < LOADS; ++i) {
+    const int id = i * kThreads + tid;
+    ld_key[i] = id / CPR;
+    const int pchunk = id % CPR;
+    ld_lds[i] = ld_key[i] * ROWB + pchunk * 16;
+    ld_col[i] = (pchunk ^ (ld_key[i] % CPR)) * 16;
+  }
+  u32x4_t kst[LOADS], vst[LOADS];
+#define PA_CK_LOAD(KT0)                                                                   \
+  static_for<LOADS>([&](auto I) {                                                         \
+    constexpr int i = I;                                                                  \
+    int kabs = (KT0) + ld_key[i];                                                         \
+    kabs = kabs < k1 ? kabs : k1 - 1;                                                     \
+    const int blk = bt_lds[(kabs >> lb) - blk_first];                                     \
+    const int64_t off = (((int64_t)blk << lb) + (kabs & bmask)) * slot_stride + head_off + ld_col[i]; \
+    kst[i] = *reinterpret_cast<const u32x4_t*>(kcache + off);                             \
+    vst[i] = *reinterpret_cast<const u32x4_t*>(vcache + off);                             \
+  });
+#define PA_CK_STORE(BUF)                                                                  \
+  static_for<LOADS>([&](auto I) {                                                         \
+    constexpr int i = I;                                                                  \
+    *reinterpret_cast<u32x4_t*>(k_lds + (BUF) * TILE_BYTES + ld_lds[i]) = kst[i];         \
+    *reinterpret_cast<u32x4_t*>(v_lds + (BUF) * TILE_BYTES + ld_lds[i]) = vst[i];         \
+  });
 
   f32x16_t o[DB];
 #pragma unroll
@@ -171,13 +189,13 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(AttnArgs a) {
   const int li = lane & 15;        // lane within the 16-lane group
 
   const int n_tiles = (k1 - k0 + KT - 1) / KT;
-  load_tile(k0);
-  store_tile(0);
+  PA_CK_LOAD(k0)
+  PA_CK_STORE(0)
 
   for (int ti = 0; ti < n_tiles; ++ti) {
     const int kt = k0 + ti * KT;
     const int buf = ti & 1;
-    if (ti + 1 < n_tiles) load_tile(kt + KT);
+    if (ti + 1 < n_tiles) { PA_CK_LOAD(kt + KT) }
     __syncthreads();
 
     if (kt <= w_qpos_hi) {  // some row of this wave sees part of the tile
@@ -193,8 +211,9 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(AttnArgs a) {
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
           const int ch = (2 * kk + grp) ^ (key % CPR);
-          const uint4 kv = *reinterpret_cast<const uint4*>(kb + key * ROWB + ch * 16);
-          s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kv), qf[kk],
+          const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(kb + key * ROWB + ch * 16);
+          s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kv),
+                                                           __builtin_bit_cast(bf16x8_t, qf[kk]),
                                                            s[sub], 0, 0, 0);
         }
       }
@@ -207,7 +226,7 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(AttnArgs a) {
         for (int e = 0; e < 16; ++e) {
           if (need_mask) {
             const int key = kt + sub * 32 + 8 * (e >> 2) + 4 * grp + (e & 3);
-            if (key > qpos || key >= k1) s[sub][e] = kNegInf;
+            s[sub][e] = (key > qpos || key >= k1) ? kNegInf : s[sub][e];
           }
           mx = fmaxf(mx, s[sub][e]);
         }
@@ -239,7 +258,7 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(AttnArgs a) {
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const uint4 pw = make_uint4(pk[sub][4 * h], pk[sub][4 * h + 1], pk[sub][4 * h + 2], pk[sub][4 * h + 3]);
+          const u32x4_t pw = {pk[sub][4 * h], pk[sub][4 * h + 1], pk[sub][4 * h + 2], pk[sub][4 * h + 3]};
           const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
           const int kbase = sub * 32 + 16 * h + 4 * grp + (li >> 2);  // row m = li / 4
 #pragma unroll
@@ -254,14 +273,16 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(AttnArgs a) {
                 (__attribute__((address_space(3))) const char*)(vb + key2 * ROWB + c2 * 16 + in_chunk));
             const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_s16x4_t*>(p1));
             const s16x4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_s16x4_t*>(p2));
-            short vv[8] = {v1[0], v1[1], v1[2], v1[3], v2[0], v2[1], v2[2], v2[3]};
+            const s16x8_t vv = __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
             const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, vv);
             o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[db], 0, 0, 0);
           }
         }
     }
-    if (ti + 1 < n_tiles) store_tile(buf ^ 1);
+    if (ti + 1 < n_tiles) { PA_CK_STORE(buf ^ 1) }
   }
+#undef PA_CK_LOAD
+#undef PA_CK_STORE
 
   // ---- epilogue ---------------------------------------------------------------
   const float l_tot = l_run + xor32(l_run);
@@ -305,8 +326,9 @@ size_t chunk_smem() {
 
 }  // namespace
 
-bool chunk_kernel_supports(bool bf16, int32_t D, int32_t G) {
-  return bf16 && (D == 64 || D == 128) && (G == 1 || G == 2 || G == 4 || G == 8);
+bool chunk_kernel_supports(bool bf16, int32_t D, int32_t G, int32_t B) {
+  return bf16 && (D == 64 || D == 128) && (G == 1 || G == 2 || G == 4 || G == 8) &&
+         (B & (B - 1)) == 0;
 }
 
 int32_t chunk_max_segment(int32_t B) { return kMaxSegBlocks * B - B; }

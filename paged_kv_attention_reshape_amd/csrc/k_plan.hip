@@ -60,7 +60,7 @@ plan_kernel(const int32_t* __restrict__ qsl, const int32_t* __restrict__ seq_len
           const int32_t keys = c + i + 1;
           const int32_t parts = cdiv(keys, ps.S);
           if (parts > 1) {
-            if (k_mg < ps.n_mg) merge[k_mg] = make_int4(t0 + i, k_rw, parts, 1);
+            if (k_mg < ps.n_mg) merge[k_mg] = make_int4(t0 + i, k_rw, parts, (1 << 8) | 1);
             ++k_mg;
           }
           for (int32_t p = 0; p < parts; ++p) {
@@ -82,13 +82,11 @@ plan_kernel(const int32_t* __restrict__ qsl, const int32_t* __restrict__ seq_len
             ++k_ck;
           }
           if (nseg > 1) {
-            for (int32_t tau = qt * ps.TQ; tau < tok_end; ++tau) {
-              if (k_mg < ps.n_mg && split)
-                merge[k_mg] = make_int4(t0 + tau, pb + (tau - qt * ps.TQ), nseg, ps.TQ);
-              else if (k_mg < ps.n_mg)
-                merge[k_mg] = make_int4(-1, 0, 0, 0);
-              ++k_mg;
-            }
+            if (k_mg < ps.n_mg)
+              merge[k_mg] = split ? make_int4(t0 + qt * ps.TQ, pb, nseg,
+                                              ((tok_end - qt * ps.TQ) << 8) | ps.TQ)
+                                  : make_int4(-1, 0, 0, 0);
+            ++k_mg;
             pb += nseg * ps.TQ;
           }
         }

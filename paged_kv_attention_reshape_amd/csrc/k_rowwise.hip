@@ -320,40 +320,69 @@ __global__ void __launch_bounds__(64) rowwise_kernel(AttnArgs a) {
 }
 
 // Merge pass: combine the partial (m, l, o) of one query row's partitions,
-// rescaling each to the global max (log-sum-exp normalisation).
+// rescaling each to the global max (log-sum-exp normalisation).  One
+// workgroup per merge record; its waves take the record's (token, head)
+// pairs in turn.  For a pair, lane p loads partition p's (m, l) so the max
+// and the weighted sum of l are wave reductions, then every lane accumulates
+// its slice of the head dimension over the partitions.
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x = fmaxf(x, shfl_xor(x, m));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x += shfl_xor(x, m);
+  return x;
+}
+
 template <bool BF16, int D, int G>
-__global__ void __launch_bounds__(64) merge_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(256) merge_kernel(AttnArgs a) {
   constexpr int E = BF16 ? 2 : 4;
   constexpr int PER = D / 64;  // elements per lane
   const int4 mr = a.merge[blockIdx.x];
-  const int t = mr.x;
-  if (t < 0) return;
-  const int first = mr.y, n = mr.z, stride = mr.w;
+  const int t_first = mr.x;
+  if (t_first < 0) return;
+  const int first = mr.y, n = mr.z, n_tok = mr.w >> 8, stride = mr.w & 0xFF;
   const int g = blockIdx.y;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
 #pragma unroll 1
-  for (int h = 0; h < G; ++h) {
-    const int hq = g * G + h;
+  for (int pair = wave; pair < n_tok * G; pair += 4) {
+    const int tau = pair / G;
+    const int hq = g * G + pair % G;
+    const int64_t p0 = first + tau;
+    // max over partitions
     float M = kNegInf;
-    for (int p = 0; p < n; ++p) {
-      const int64_t part = first + (int64_t)p * stride;
-      M = fmaxf(M, a.ml_part[(part * a.Hq + hq) * 2]);
+    for (int pb = 0; pb < n; pb += 64) {
+      const int p = pb + lane;
+      const float m = p < n ? a.ml_part[((p0 + (int64_t)p * stride) * a.Hq + hq) * 2] : kNegInf;
+      M = fmaxf(M, m);
     }
+    M = wave_max(M);
     float num[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) num[e] = 0.f;
     float den = 0.f;
-    for (int p = 0; p < n; ++p) {
-      const int64_t part = first + (int64_t)p * stride;
-      const float* ml = a.ml_part + (part * a.Hq + hq) * 2;
-      const float w = __builtin_amdgcn_exp2f(ml[0] - M);
-      den += w * ml[1];
-      const float* op = a.o_part + (part * a.Hq + hq) * D + lane * PER;
+    for (int pb = 0; pb < n; pb += 64) {
+      const int p = pb + lane;
+      float w = 0.f;
+      if (p < n) {
+        const float* ml = a.ml_part + ((p0 + (int64_t)p * stride) * a.Hq + hq) * 2;
+        w = __builtin_amdgcn_exp2f(ml[0] - M);
+        den += w * ml[1];
+      }
+      const int cnt = min(64, n - pb);
+      for (int j = 0; j < cnt; ++j) {
+        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));
+        const float* op = a.o_part + ((p0 + (int64_t)(pb + j) * stride) * a.Hq + hq) * D + lane * PER;
 #pragma unroll
-      for (int e = 0; e < PER; ++e) num[e] += w * op[e];
+        for (int e = 0; e < PER; ++e) num[e] += wj * op[e];
+      }
     }
+    den = wave_sum(den);
     const float inv = 1.f / den;
-    char* ob = static_cast<char*>(a.out) + (((int64_t)t * a.Hq + hq) * D + lane * PER) * E;
+    char* ob = static_cast<char*>(a.out) + (((int64_t)(t_first + tau) * a.Hq + hq) * D + lane * PER) * E;
     if constexpr (BF16) {
       if constexpr (PER == 2) {
         *reinterpret_cast<uint32_t*>(ob) =
@@ -404,7 +433,7 @@ hipError_t launch_merge(const AttnArgs& a, hipStream_t s) {
   PA_SELECT(merge_kernel)
   AttnArgs args = a;
   void* params[] = {&args};
-  return hipLaunchKernel(kern, dim3(a.ps.n_mg, a.Hkv), dim3(64), params, 0, s);
+  return hipLaunchKernel(kern, dim3(a.ps.n_mg, a.Hkv), dim3(256), params, 0, s);
 }
 
 }  // namespace pa

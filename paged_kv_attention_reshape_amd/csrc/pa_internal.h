@@ -31,7 +31,11 @@ namespace pa {
 // Records (int4):
 //   row-wise item  {r, t, kb, ke | kDirect}   t = flattened query row
 //   chunk item     {r, qt, seg, part_base}    part_base < 0: single segment
-//   merge row      {t, first_part, n_parts, stride}
+//   merge record   {t_first, first_part, n_parts, (n_tok << 8) | stride}:
+//                  tokens t_first + tau (tau < n_tok); token tau's partials
+//                  are first_part + tau + p * stride, p < n_parts.  One record
+//                  per split decode row (n_tok 1, stride 1) or per split chunk
+//                  tile (n_tok <= TQ, stride TQ).
 // Unused trailing records hold r = -1 / t = -1.
 constexpr int32_t kDirect = (int32_t)0x80000000;
 
@@ -98,7 +102,7 @@ __host__ __device__ inline ReqCounts request_counts(int32_t q, int32_t L, const 
       n.ck += nseg;
       if (nseg > 1) {
         n.ck_parts += nseg * ps.TQ;
-        n.mg += tok_end - qt * ps.TQ;
+        n.mg += 1;
       }
     }
   }
@@ -161,7 +165,7 @@ struct AttnArgs {
 hipError_t launch_rowwise(const AttnArgs& a, hipStream_t s);
 hipError_t launch_chunk(const AttnArgs& a, hipStream_t s);
 hipError_t launch_merge(const AttnArgs& a, hipStream_t s);
-bool chunk_kernel_supports(bool bf16, int32_t D, int32_t G);
+bool chunk_kernel_supports(bool bf16, int32_t D, int32_t G, int32_t B);
 // Longest key segment one chunk work item may cover (its block ids live in LDS).
 int32_t chunk_max_segment(int32_t B);
 
