@@ -1,13 +1,15 @@
 // Plan kernel: turns query_start_loc / seq_lens into the step's work tables
-// (row-wise split-K items, chunk items, merge rows) on the device.
+// (row-wise split-K items, chunk items, merge records) on the device.
 //
-// One workgroup of 1024 threads walks the requests 1024 at a time; each
-// thread counts its request's work with request_counts() (the same function
-// the host uses to size the tables), a block-wide scan turns the counts into
-// table offsets, and each thread writes its records.  Every write is bounded
-// by the table capacities the host computed, and unused trailing records are
-// filled with sentinels, so a mismatch between device metadata and the host
-// mirrors can give wrong numbers but never an out-of-bounds access.
+// One workgroup of 1024 threads walks the requests 1024 at a time.  Phase 1:
+// each thread counts its request's records with request_counts() (the same
+// function the host uses to size the tables) and a block-wide scan turns the
+// counts into offsets.  Phase 2: the threads emit the records in parallel,
+// record index idx going to the request whose scanned range contains idx
+// (binary search in LDS), so a request with many records does not serialise
+// the kernel.  Every write is bounded by the capacities the host computed and
+// unused trailing records get sentinels: device metadata that disagrees with
+// the host mirrors gives wrong numbers, never an out-of-bounds access.
 #include "pa_internal.h"
 
 namespace pa {
@@ -15,16 +17,111 @@ namespace {
 
 constexpr int kPlanThreads = 1024;
 
+struct ReqView {
+  int32_t r, q, L, c, t0;
+};
+
+// first position in the inclusive scan whose value exceeds idx
+__device__ __forceinline__ int upper_bound(const int32_t* inc, int n, int32_t idx) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (inc[mid] > idx) hi = mid; else lo = mid + 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ int32_t min32(int32_t a, int32_t b) { return a < b ? a : b; }
+
+// j-th row-wise item of a request; item index k (also its partial slot)
+__device__ void emit_rowwise(const ReqView& v, int32_t j, int32_t k, const PlanShape& ps,
+                             int4* items_rw) {
+  int32_t i = 0;
+  int32_t parts = cdiv(v.c + 1, ps.S);
+  while (j >= parts && i + 1 < v.q) {  // multi-token requests only (fp32 chunks)
+    j -= parts;
+    ++i;
+    parts = cdiv(v.c + i + 1, ps.S);
+  }
+  const int32_t keys = v.c + i + 1;
+  const int32_t kb = j * ps.S;
+  const int32_t ke = min32(kb + ps.S, keys);
+  if (k < ps.n_rw) items_rw[k] = make_int4(v.r, v.t0 + i, kb, ke | (parts == 1 ? kDirect : 0));
+}
+
+// j-th merge record of a row-wise request whose first item is k_first
+__device__ void emit_merge_rowwise(const ReqView& v, int32_t j, int32_t k_first, int32_t m,
+                                   const PlanShape& ps, int4* merge) {
+  int32_t item = k_first;
+  for (int32_t i = 0; i < v.q; ++i) {
+    const int32_t parts = cdiv(v.c + i + 1, ps.S);
+    if (parts > 1) {
+      if (j == 0) {
+        if (m < ps.n_mg)
+          merge[m] = item + parts <= ps.n_rw ? make_int4(v.t0 + i, item, parts, (1 << 8) | 1)
+                                             : make_int4(-1, 0, 0, 0);
+        return;
+      }
+      --j;
+    }
+    item += parts;
+  }
+}
+
+// j-th chunk item of a chunk request whose partial slots start at pbase
+__device__ void emit_chunk(const ReqView& v, int32_t j, int32_t k, int32_t pbase,
+                           const PlanShape& ps, int4* items_ck) {
+  const int32_t nqt = cdiv(v.q, ps.TQ);
+  for (int32_t qt = 0; qt < nqt; ++qt) {
+    const int32_t tok_end = min32((qt + 1) * ps.TQ, v.q);
+    const int32_t nseg = cdiv(v.c + tok_end, ps.SEG);
+    if (j < nseg) {
+      const bool split = nseg > 1 && pbase + nseg * ps.TQ <= ps.n_rw + ps.n_ck_parts;
+      if (k < ps.n_ck) items_ck[k] = make_int4(v.r, qt, j, split ? pbase : -1);
+      return;
+    }
+    j -= nseg;
+    if (nseg > 1) pbase += nseg * ps.TQ;
+  }
+}
+
+// j-th merge record of a chunk request (groups of MT tokens of split tiles)
+__device__ void emit_merge_chunk(const ReqView& v, int32_t j, int32_t m, int32_t pbase,
+                                 const PlanShape& ps, int4* merge) {
+  const int32_t nqt = cdiv(v.q, ps.TQ);
+  for (int32_t qt = 0; qt < nqt; ++qt) {
+    const int32_t tok_end = min32((qt + 1) * ps.TQ, v.q);
+    const int32_t nseg = cdiv(v.c + tok_end, ps.SEG);
+    if (nseg > 1) {
+      const int32_t ntok = tok_end - qt * ps.TQ;
+      const int32_t ngrp = cdiv(ntok, ps.MT);
+      if (j < ngrp) {
+        const int32_t tau0 = j * ps.MT;
+        const int32_t n = min32(ps.MT, ntok - tau0);
+        const bool split = pbase + nseg * ps.TQ <= ps.n_rw + ps.n_ck_parts;
+        if (m < ps.n_mg)
+          merge[m] = split ? make_int4(v.t0 + qt * ps.TQ + tau0, pbase + tau0, nseg, (n << 8) | ps.TQ)
+                           : make_int4(-1, 0, 0, 0);
+        return;
+      }
+      j -= ngrp;
+      pbase += nseg * ps.TQ;
+    }
+  }
+}
+
 __global__ void __launch_bounds__(kPlanThreads)
 plan_kernel(const int32_t* __restrict__ qsl, const int32_t* __restrict__ seq_lens, PlanShape ps,
             int4* __restrict__ items_rw, int4* __restrict__ items_ck, int4* __restrict__ merge) {
-  __shared__ int32_t scan[4][kPlanThreads];
+  __shared__ int32_t scan[4][kPlanThreads];   // inclusive scans of the 4 counts
+  __shared__ int32_t s_q[kPlanThreads], s_L[kPlanThreads], s_t0[kPlanThreads];
   __shared__ int32_t carry[4];
   const int tid = threadIdx.x;
   if (tid < 4) carry[tid] = 0;
   __syncthreads();
   for (int32_t base = 0; base < ps.R; base += kPlanThreads) {
     const int32_t r = base + tid;
+    const int n_here = min32(kPlanThreads, ps.R - base);
     int32_t q = 0, L = 0, t0 = 0;
     if (r < ps.R) {
       t0 = qsl[r];
@@ -33,6 +130,9 @@ plan_kernel(const int32_t* __restrict__ qsl, const int32_t* __restrict__ seq_len
       sanitize(q, L, ps.M, ps.B);
       if (t0 < 0 || (int64_t)t0 + q > (int64_t)ps.T) q = 0;
     }
+    s_q[tid] = q;
+    s_L[tid] = L;
+    s_t0[tid] = t0;
     const ReqCounts n = request_counts(q, L, ps);
     scan[0][tid] = n.rw;
     scan[1][tid] = n.ck;
@@ -48,54 +148,40 @@ plan_kernel(const int32_t* __restrict__ qsl, const int32_t* __restrict__ seq_len
       for (int k = 0; k < 4; ++k) scan[k][tid] += v[k];
       __syncthreads();
     }
-    int32_t k_rw = carry[0] + scan[0][tid] - n.rw;
-    int32_t k_ck = carry[1] + scan[1][tid] - n.ck;
-    int32_t k_mg = carry[2] + scan[2][tid] - n.mg;
-    int32_t pb = ps.n_rw + carry[3] + scan[3][tid] - n.ck_parts;
-    const int32_t pb_end = ps.n_rw + ps.n_ck_parts;
-    if (q > 0) {
-      const int32_t c = L - q;
-      if (goes_rowwise(q, ps)) {
-        for (int32_t i = 0; i < q; ++i) {
-          const int32_t keys = c + i + 1;
-          const int32_t parts = cdiv(keys, ps.S);
-          if (parts > 1) {
-            if (k_mg < ps.n_mg) merge[k_mg] = make_int4(t0 + i, k_rw, parts, (1 << 8) | 1);
-            ++k_mg;
-          }
-          for (int32_t p = 0; p < parts; ++p) {
-            const int32_t kb = p * ps.S;
-            const int32_t ke = kb + ps.S < keys ? kb + ps.S : keys;
-            if (k_rw < ps.n_rw)
-              items_rw[k_rw] = make_int4(r, t0 + i, kb, ke | (parts == 1 ? kDirect : 0));
-            ++k_rw;
-          }
-        }
-      } else {
-        const int32_t nqt = cdiv(q, ps.TQ);
-        for (int32_t qt = 0; qt < nqt; ++qt) {
-          const int32_t tok_end = (qt + 1) * ps.TQ < q ? (qt + 1) * ps.TQ : q;
-          const int32_t nseg = cdiv(c + tok_end, ps.SEG);
-          const bool split = nseg > 1 && pb + nseg * ps.TQ <= pb_end;
-          for (int32_t sg = 0; sg < nseg; ++sg) {
-            if (k_ck < ps.n_ck) items_ck[k_ck] = make_int4(r, qt, sg, split ? pb : -1);
-            ++k_ck;
-          }
-          if (nseg > 1) {
-            if (k_mg < ps.n_mg)
-              merge[k_mg] = split ? make_int4(t0 + qt * ps.TQ, pb, nseg,
-                                              ((tok_end - qt * ps.TQ) << 8) | ps.TQ)
-                                  : make_int4(-1, 0, 0, 0);
-            ++k_mg;
-            pb += nseg * ps.TQ;
-          }
-        }
-      }
+    auto view = [&](int rl) {
+      ReqView v;
+      v.r = base + rl;
+      v.q = s_q[rl];
+      v.L = s_L[rl];
+      v.c = v.L - v.q;
+      v.t0 = s_t0[rl];
+      return v;
+    };
+    auto excl = [&](int k, int rl) { return rl > 0 ? scan[k][rl - 1] : 0; };
+    // row-wise items
+    for (int32_t idx = tid; idx < scan[0][n_here - 1]; idx += kPlanThreads) {
+      const int rl = upper_bound(scan[0], n_here, idx);
+      emit_rowwise(view(rl), idx - excl(0, rl), carry[0] + idx, ps, items_rw);
+    }
+    // chunk items
+    for (int32_t idx = tid; idx < scan[1][n_here - 1]; idx += kPlanThreads) {
+      const int rl = upper_bound(scan[1], n_here, idx);
+      const int32_t pbase = ps.n_rw + carry[3] + excl(3, rl);
+      emit_chunk(view(rl), idx - excl(1, rl), carry[1] + idx, pbase, ps, items_ck);
+    }
+    // merge records
+    for (int32_t idx = tid; idx < scan[2][n_here - 1]; idx += kPlanThreads) {
+      const int rl = upper_bound(scan[2], n_here, idx);
+      const ReqView v = view(rl);
+      if (goes_rowwise(v.q, ps))
+        emit_merge_rowwise(v, idx - excl(2, rl), carry[0] + excl(0, rl), carry[2] + idx, ps, merge);
+      else
+        emit_merge_chunk(v, idx - excl(2, rl), carry[2] + idx, ps.n_rw + carry[3] + excl(3, rl), ps, merge);
     }
     __syncthreads();
-    if (tid == kPlanThreads - 1) {
+    if (tid == 0) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) carry[k] += scan[k][tid];
+      for (int k = 0; k < 4; ++k) carry[k] += scan[k][n_here - 1];
     }
     __syncthreads();
   }

@@ -128,6 +128,7 @@ pa_status make_plan(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R, 
   ps.B = B;
   ps.rowwise_all = pa::chunk_kernel_supports(bf16, D, G, B) && env_int("PA_FORCE_ROWWISE", 0) == 0 ? 0 : 1;
   ps.TQ = pa::chunk_tile_tokens(G);
+  ps.MT = pa::chunk_merge_tokens(G);
   ps.SEG = 1 << 30;
   for (int32_t r = 0; r < R; ++r) {
     const int32_t q = h_qsl[r + 1] - h_qsl[r];

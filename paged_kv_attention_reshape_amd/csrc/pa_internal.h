@@ -34,14 +34,16 @@ namespace pa {
 //   merge record   {t_first, first_part, n_parts, (n_tok << 8) | stride}:
 //                  tokens t_first + tau (tau < n_tok); token tau's partials
 //                  are first_part + tau + p * stride, p < n_parts.  One record
-//                  per split decode row (n_tok 1, stride 1) or per split chunk
-//                  tile (n_tok <= TQ, stride TQ).
+//                  per split decode row (n_tok 1, stride 1) or per group of at
+//                  most MT = chunk_merge_tokens(G) tokens of a split chunk tile
+//                  (stride TQ), so a record is at most 16 (token, head) pairs.
 // Unused trailing records hold r = -1 / t = -1.
 constexpr int32_t kDirect = (int32_t)0x80000000;
 
 // Number of query tokens per chunk-kernel tile as a function of the GQA group:
 // a tile is always 128 (token, head) rows of one kv head.
 __host__ __device__ inline int32_t chunk_tile_tokens(int32_t G) { return 128 / G; }
+__host__ __device__ inline int32_t chunk_merge_tokens(int32_t G) { return G >= 16 ? 1 : 16 / G; }
 
 struct PlanShape {
   int32_t R;
@@ -51,6 +53,7 @@ struct PlanShape {
   int32_t S;             // row-wise partition length (keys), multiple of 16 and of B
   int32_t rowwise_all;   // 1: multi-token requests go row-wise too
   int32_t TQ;            // chunk tile tokens
+  int32_t MT;            // tokens per chunk merge record
   int32_t SEG;           // chunk key-segment length, multiple of 64
   // exact totals for this step (host mirrors); capacities of the tables
   int32_t n_rw;          // row-wise items (= row-wise partial slots)
@@ -102,7 +105,7 @@ __host__ __device__ inline ReqCounts request_counts(int32_t q, int32_t L, const 
       n.ck += nseg;
       if (nseg > 1) {
         n.ck_parts += nseg * ps.TQ;
-        n.mg += 1;
+        n.mg += cdiv(tok_end - qt * ps.TQ, ps.MT);
       }
     }
   }
