@@ -43,6 +43,7 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 constexpr int kThreads = 256;  // 4 waves
 constexpr int KT = 64;         // keys per tile
 constexpr int kMaxSegBlocks = 512;
+constexpr int kXcds = 8;       // accelerator complex dies of an MI355X
 constexpr float kNegInf = -__builtin_huge_valf();
 
 template <int V>
@@ -89,11 +90,19 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(AttnArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int4 it = a.items_ck[blockIdx.x];
+  // XCD-aware work assignment: workgroups are dispatched round-robin over the
+  // 8 XCDs (linear id % 8), so XCD x runs ids x, x+8, ...  Work unit
+  // u = g * n_ck + item (items ordered request, segment, q-tile) is given to
+  // XCD u / per_xcd, in order: every XCD gets a contiguous range of units and
+  // the q-tiles that read the same K/V segment share that XCD's L2.
+  const int per_xcd = (int)(gridDim.x / kXcds);
+  const int u = ((int)blockIdx.x % kXcds) * per_xcd + (int)blockIdx.x / kXcds;
+  if (u >= a.ps.n_ck * a.Hkv) return;
+  const int g = u / a.ps.n_ck;
+  const int4 it = a.items_ck[u - g * a.ps.n_ck];
   const int r = it.x;
   if (r < 0 || r >= a.R) return;
   const int qt = it.y, seg = it.z, part_base = it.w;
-  const int g = blockIdx.y;
 
   int q = a.qsl[r + 1] - a.qsl[r];
   int L = a.seq_lens[r];
@@ -366,7 +375,9 @@ hipError_t launch_chunk(const AttnArgs& a, hipStream_t s) {
   }
   AttnArgs args = a;
   void* params[] = {&args};
-  return hipLaunchKernel(kern, dim3(a.ps.n_ck, a.Hkv), dim3(kThreads), params, smem, s);
+  const int64_t units = (int64_t)a.ps.n_ck * a.Hkv;
+  const int64_t per_xcd = (units + kXcds - 1) / kXcds;
+  return hipLaunchKernel(kern, dim3((unsigned)(per_xcd * kXcds)), dim3(kThreads), params, smem, s);
 }
 
 }  // namespace pa

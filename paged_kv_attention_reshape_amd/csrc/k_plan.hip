@@ -68,20 +68,33 @@ __device__ void emit_merge_rowwise(const ReqView& v, int32_t j, int32_t k_first,
   }
 }
 
-// j-th chunk item of a chunk request whose partial slots start at pbase
+// j-th chunk item of a chunk request whose partial slots start at pbase.
+// Items are ordered segment-major, (seg, qt): the q-tiles that read the same
+// key segment are consecutive, so the XCD-aware launch keeps them on one L2.
+// A q-tile's segment count grows with qt, so the q-tiles that have segment s
+// form a suffix of the tile range.
 __device__ void emit_chunk(const ReqView& v, int32_t j, int32_t k, int32_t pbase,
                            const PlanShape& ps, int4* items_ck) {
   const int32_t nqt = cdiv(v.q, ps.TQ);
-  for (int32_t qt = 0; qt < nqt; ++qt) {
-    const int32_t tok_end = min32((qt + 1) * ps.TQ, v.q);
-    const int32_t nseg = cdiv(v.c + tok_end, ps.SEG);
-    if (j < nseg) {
-      const bool split = nseg > 1 && pbase + nseg * ps.TQ <= ps.n_rw + ps.n_ck_parts;
-      if (k < ps.n_ck) items_ck[k] = make_int4(v.r, qt, j, split ? pbase : -1);
+  const int32_t max_seg = cdiv(v.c + v.q, ps.SEG);
+  for (int32_t sg = 0; sg < max_seg; ++sg) {
+    int32_t first_qt = nqt;
+    for (int32_t qt = 0; qt < nqt; ++qt)
+      if (cdiv(v.c + min32((qt + 1) * ps.TQ, v.q), ps.SEG) > sg) { first_qt = qt; break; }
+    const int32_t count = nqt - first_qt;
+    if (j < count) {
+      const int32_t qt = first_qt + j;
+      const int32_t nseg = cdiv(v.c + min32((qt + 1) * ps.TQ, v.q), ps.SEG);
+      int32_t pb = pbase;  // partial slots of earlier split tiles
+      for (int32_t t = 0; t < qt; ++t) {
+        const int32_t ns = cdiv(v.c + min32((t + 1) * ps.TQ, v.q), ps.SEG);
+        if (ns > 1) pb += ns * ps.TQ;
+      }
+      const bool split = nseg > 1 && pb + nseg * ps.TQ <= ps.n_rw + ps.n_ck_parts;
+      if (k < ps.n_ck) items_ck[k] = make_int4(v.r, qt, sg, split ? pb : -1);
       return;
     }
-    j -= nseg;
-    if (nseg > 1) pbase += nseg * ps.TQ;
+    j -= count;
   }
 }
 
