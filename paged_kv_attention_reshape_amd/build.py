@@ -29,8 +29,15 @@ COMMON = [
 ]
 
 
+# Per-file extra flags.  The chunk kernel's scores never hold a NaN (masked
+# rows re-read finite cache rows), so max/min need no NaN canonicalisation;
+# infinities are still honoured (the causal mask uses -inf).
+EXTRA_FLAGS = {"k_chunk.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src: str, obj: str, includes, verbose: bool) -> None:
-    cmd = [HIPCC, *COMMON, *[f"-I{i}" for i in includes], "-c", src, "-o", obj]
+    extra = EXTRA_FLAGS.get(os.path.basename(src), [])
+    cmd = [HIPCC, *COMMON, *extra, *[f"-I{i}" for i in includes], "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

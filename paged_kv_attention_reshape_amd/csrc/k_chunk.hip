@@ -34,6 +34,7 @@ namespace pa {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x8_t __attribute__((ext_vector_type(8)));
@@ -52,9 +53,13 @@ struct __integral_constant {
   constexpr operator int() const { return V; }
 };
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+
+// two floats -> packed bf16 pair (round to nearest even; one v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+  const f32x2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v_t));
 }
 
 template <int N, typename F>
@@ -71,20 +76,132 @@ __device__ __forceinline__ float xor32(float x) {
   return __uint_as_float((threadIdx.x & 32) ? p[0] : p[1]);
 }
 
+// LDS swizzle: 16-byte chunk c of key row k is stored at chunk c ^ swz(k).
+// swz takes the key's low three bits to {0,2,4,6,1,3,5,7}: eight consecutive
+// keys read at one chunk (the K operand) hit eight different bank groups, and
+// the four rows of a transposed V read (keys differing in the low two bits,
+// two adjacent chunks each) also cover all bank groups.
+__device__ __forceinline__ int swz(int key) { return ((key & 3) << 1) | ((key >> 2) & 1); }
+
+template <int D, int G>
+struct ChunkGeo {
+  static constexpr int ROWB = D * 2;        // bytes per key row (one head)
+  static constexpr int CPR = ROWB / 16;     // 16-byte chunks per row
+  static constexpr int KSTEPS = D / 16;     // MFMA k-steps for q.k
+  static constexpr int DB = D / 32;         // 32-wide d blocks of O
+  static constexpr int TQ = 128 / G;
+  static constexpr int TILE_BYTES = KT * ROWB;
+  static constexpr int LOADS = KT * CPR / kThreads;  // 16-byte chunks per thread per tile
+};
+
+template <int D, int G>
+struct ChunkState {
+  using Gm = ChunkGeo<D, G>;
+  f32x16_t o[Gm::DB];
+  float m_run;
+  float l_run;
+};
+
+// One 64-key tile of the online-softmax loop on LDS buffer BUF.
+typedef const __attribute__((address_space(3))) char* lds_cptr;
+
+template <int D, int G, int BUF>
+__device__ __forceinline__ void chunk_tile(ChunkState<D, G>& st,
+                                           const u32x4_t (&qf)[ChunkGeo<D, G>::KSTEPS],
+                                           const lds_cptr (&kaddr)[ChunkGeo<D, G>::KSTEPS],
+                                           const lds_cptr (&vaddr)[ChunkGeo<D, G>::DB], int kt,
+                                           int qpos, int k1, int w_qpos_lo, float sl, int lane) {
+  using Gm = ChunkGeo<D, G>;
+  constexpr int ROWB = Gm::ROWB, KSTEPS = Gm::KSTEPS, DB = Gm::DB, TILE_BYTES = Gm::TILE_BYTES;
+  const int grp = lane >> 5;
+  // ---- S^T = K Q^T ---------------------------------------------------------
+  f32x16_t s[2];
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[sub][e] = 0.f;
+  }
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk) {
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const u32x4_t kv = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
+          kaddr[kk] + BUF * TILE_BYTES + sub * 32 * ROWB);
+      s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kv),
+                                                       __builtin_bit_cast(bf16x8_t, qf[kk]),
+                                                       s[sub], 0, 0, 0);
+    }
+  }
+  // ---- mask (diagonal / segment-end tiles only) and online softmax ----------
+  if (kt + KT - 1 > w_qpos_lo || kt + KT > k1) {
+    const int lim = min(qpos + 1, k1) - kt;   // keys < lim (relative) are visible
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = sub * 32 + 8 * (e >> 2) + 4 * grp + (e & 3);
+        s[sub][e] = key < lim ? s[sub][e] : kNegInf;
+      }
+  }
+  float mx = kNegInf;
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[sub][e], s[sub][e + 1]));
+  mx = fmaxf(mx, xor32(mx));
+  const float m_new = fmaxf(st.m_run, mx * sl);
+  const float m_use = m_new == kNegInf ? 0.f : m_new;
+  const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_use);
+  st.m_run = m_new;
+  uint32_t pk[2][8];
+  float psum = 0.f;
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][e], sl, -m_use));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][e + 1], sl, -m_use));
+      pk[sub][e >> 1] = pack_bf16(p0, p1);
+      // row sum of the bf16-rounded probabilities (the ones p.v uses)
+      psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[sub][e >> 1]),
+                                             __builtin_bit_cast(bf16x2_t, 0x3F803F80u), psum, false);
+    }
+  st.l_run = st.l_run * alpha + psum;
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) st.o[db][e] *= alpha;
+  }
+  // ---- O^T += V^T P^T ---------------------------------------------------------
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const u32x4_t pw = {pk[sub][4 * h], pk[sub][4 * h + 1], pk[sub][4 * h + 2], pk[sub][4 * h + 3]};
+      const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
+      const int rowoff = (sub * 32 + 16 * h) * ROWB;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t*)(vaddr[db] + (2 + BUF) * TILE_BYTES + rowoff));
+        const s16x4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t*)(vaddr[db] + (2 + BUF) * TILE_BYTES + rowoff + 8 * ROWB));
+        const s16x8_t vv = __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
+        st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv), pf,
+                                                           st.o[db], 0, 0, 0);
+      }
+    }
+}
+
 template <int D, int G>
 __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(AttnArgs a) {
-  constexpr int ROWB = D * 2;        // bytes per key row (one head)
-  constexpr int CPR = ROWB / 16;     // 16-byte chunks per row
-  constexpr int KSTEPS = D / 16;     // MFMA k-steps for q.k
-  constexpr int DB = D / 32;         // 32-wide d blocks of O
-  constexpr int TQ = 128 / G;
-  constexpr int TILE_BYTES = KT * ROWB;
-  constexpr int LOADS = KT * CPR / kThreads;  // 16-byte chunks per thread per tile (K or V)
+  using Gm = ChunkGeo<D, G>;
+  constexpr int ROWB = Gm::ROWB, CPR = Gm::CPR, KSTEPS = Gm::KSTEPS, DB = Gm::DB, TQ = Gm::TQ;
+  constexpr int TILE_BYTES = Gm::TILE_BYTES, LOADS = Gm::LOADS;
   static_assert(LOADS >= 1, "tile too small");
 
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  char* k_lds = smem;                           // [2][KT][ROWB]
-  char* v_lds = smem + 2 * TILE_BYTES;          // [2][KT][ROWB]
+  extern __shared__ __attribute__((aligned(16))) char smem[];   // K[2], V[2], block ids
   int32_t* bt_lds = reinterpret_cast<int32_t*>(smem + 4 * TILE_BYTES);
 
   const int tid = threadIdx.x;
@@ -116,9 +233,9 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(AttnArgs a) {
   const int k1 = min(k0 + a.ps.SEG, kmax);
   if (tok0 >= q || k0 >= k1) return;
 
-  // block ids of the segment into LDS
+  // block ids of the segment into LDS (one-time divisions)
   const int blk_first = k0 / a.B;
-  const int nblk = (k1 - 1) / a.B - blk_first + 1;   // (one-time divisions)
+  const int nblk = (k1 - 1) / a.B - blk_first + 1;
   for (int i = tid; i < nblk && i < kMaxSegBlocks; i += kThreads) {
     int b = a.block_table[(int64_t)r * a.M + blk_first + i];
     bt_lds[i] = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
@@ -146,155 +263,123 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(AttnArgs a) {
     for (int kk = 0; kk < KSTEPS; ++kk)
       qf[kk] = row_ok ? *reinterpret_cast<const u32x4_t*>(qrow + kk * 32) : u32x4_t{0, 0, 0, 0};
   }
+  // lane-constant LDS read offsets within a tile buffer
+  const int l32 = lane & 31, grp = lane >> 5, gam = lane >> 4, li = lane & 15;
+  const lds_cptr lds0 = (lds_cptr)smem;
+  lds_cptr kaddr[KSTEPS];
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk) kaddr[kk] = lds0 + l32 * ROWB + (((2 * kk + grp) ^ swz(l32)) << 4);
+  lds_cptr vaddr[DB];
+  {
+    const int row = 4 * grp + (li >> 2);                 // row m of the 4-row transposed block
+    const int d0_in = 16 * (gam & 1) + 4 * (li & 3);     // d offset within the 32-wide block
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int d0 = db * 32 + d0_in;
+      vaddr[db] = lds0 + row * ROWB + (((d0 >> 3) ^ swz(row)) << 4) + (d0 & 7) * 2;
+    }
+  }
   __syncthreads();  // bt_lds ready
 
+  // global -> register staging, 16-byte chunks; thread's chunk i of a tile is
+  // key row ld_key[i], logical column (pchunk ^ swz(key)), LDS slot ld_lds[i]
   const char* kcache = static_cast<const char*>(a.kcache);
   const char* vcache = static_cast<const char*>(a.vcache);
-  const int64_t slot_stride = (int64_t)a.Hkv * ROWB;
-  const int64_t head_off = (int64_t)g * ROWB;
+  const uint32_t block_bytes = (uint32_t)a.B * a.Hkv * ROWB;
+  const int slot_stride = a.Hkv * ROWB;
   const int lb = 31 - __builtin_clz(a.B);   // block size is a power of two here
   const int bmask = a.B - 1;
-
-  // This thread's 16-byte chunks of every tile: chunk i is key row
-  // (i * kThreads + tid) / CPR of the tile, physical column pchunk, holding
-  // logical column pchunk ^ (key % CPR) (XOR swizzle against LDS conflicts).
-  int ld_key[LOADS], ld_lds[LOADS], ld_col[LOADS];
+  // Tiles start at multiples of 64 keys.  With B <= 64 (B divides 64) a
+  // thread's rows sit at a fixed offset inside their block and a fixed block
+  // delta from the tile's first block; with B > 64 the whole tile lies in one
+  // block.  So the per-tile address is blk * block_bytes + a per-thread
+  // constant (+ a uniform in-block offset when B > 64).
+  const bool small_b = a.B <= KT;
+  int ld_lds[LOADS], ld_key[LOADS], ld_in[LOADS], ld_dblk[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int id = i * kThreads + tid;
-    ld_key[i] = id / CPR;
+    const int key = id / CPR;
     const int pchunk = id % CPR;
-    ld_lds[i] = ld_key[i] * ROWB + pchunk * 16;
-    ld_col[i] = (pchunk ^ (ld_key[i] % CPR)) * 16;
+    ld_key[i] = key;
+    ld_lds[i] = key * ROWB + pchunk * 16;
+    const int col = g * ROWB + ((pchunk ^ swz(key)) << 4);
+    ld_in[i] = (small_b ? (key & bmask) : key) * slot_stride + col;
+    ld_dblk[i] = small_b ? (key >> lb) : 0;
   }
   u32x4_t kst[LOADS], vst[LOADS];
-#define PA_CK_LOAD(KT0)                                                                   \
+  // full tile: every row of the tile is below k1
+#define PA_CK_LOAD_FULL(KT0)                                                              \
+  {                                                                                       \
+    const int bi0 = ((KT0) >> lb) - blk_first;                                            \
+    const int tile_in = small_b ? 0 : ((KT0) & bmask) * slot_stride;                     \
+    static_for<LOADS>([&](auto I) {                                                       \
+      constexpr int i = I;                                                                \
+      const uint32_t blk = (uint32_t)bt_lds[bi0 + ld_dblk[i]];                            \
+      const uint64_t off = (uint64_t)blk * block_bytes + (uint32_t)(ld_in[i] + tile_in);  \
+      kst[i] = *reinterpret_cast<const u32x4_t*>(kcache + off);                           \
+      vst[i] = *reinterpret_cast<const u32x4_t*>(vcache + off);                           \
+    });                                                                                   \
+  }
+  // last tile of the segment: rows at or past k1 re-read row k1 - 1 (finite data)
+#define PA_CK_LOAD_TAIL(KT0)                                                              \
   static_for<LOADS>([&](auto I) {                                                         \
     constexpr int i = I;                                                                  \
     int kabs = (KT0) + ld_key[i];                                                         \
     kabs = kabs < k1 ? kabs : k1 - 1;                                                     \
-    const int blk = bt_lds[(kabs >> lb) - blk_first];                                     \
-    const int64_t off = (((int64_t)blk << lb) + (kabs & bmask)) * slot_stride + head_off + ld_col[i]; \
+    const uint32_t blk = (uint32_t)bt_lds[(kabs >> lb) - blk_first];                      \
+    const uint64_t off = (uint64_t)blk * block_bytes +                                    \
+        ((kabs & bmask) * slot_stride + g * ROWB + (((ld_lds[i] & (ROWB - 1)) >> 4 ^ swz(ld_key[i])) << 4)); \
     kst[i] = *reinterpret_cast<const u32x4_t*>(kcache + off);                             \
     vst[i] = *reinterpret_cast<const u32x4_t*>(vcache + off);                             \
   });
+#define PA_CK_LOAD(KT0)                                                                   \
+  if ((KT0) + KT <= k1) { PA_CK_LOAD_FULL(KT0) } else { PA_CK_LOAD_TAIL(KT0) }
 #define PA_CK_STORE(BUF)                                                                  \
   static_for<LOADS>([&](auto I) {                                                         \
     constexpr int i = I;                                                                  \
-    *reinterpret_cast<u32x4_t*>(k_lds + (BUF) * TILE_BYTES + ld_lds[i]) = kst[i];         \
-    *reinterpret_cast<u32x4_t*>(v_lds + (BUF) * TILE_BYTES + ld_lds[i]) = vst[i];         \
+    *reinterpret_cast<u32x4_t*>(smem + (BUF) * TILE_BYTES + ld_lds[i]) = kst[i];          \
+    *reinterpret_cast<u32x4_t*>(smem + (2 + (BUF)) * TILE_BYTES + ld_lds[i]) = vst[i];    \
   });
 
-  f32x16_t o[DB];
+  ChunkState<D, G> st;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
-  float m_run = kNegInf;   // in log2 units (score * scale * log2 e)
-  float l_run = 0.f;       // this lane's share of the row sum
+    for (int e = 0; e < 16; ++e) st.o[db][e] = 0.f;
+  st.m_run = kNegInf;   // in log2 units (score * scale * log2 e)
+  st.l_run = 0.f;       // this lane's share of the row sum
   const float sl = a.scale_log2;
-  const int grp = lane >> 5;       // 0/1: which 4-key half of each 8-key group
-  const int gam = lane >> 4;       // 16-lane group for transposed V reads
-  const int li = lane & 15;        // lane within the 16-lane group
 
   const int n_tiles = (k1 - k0 + KT - 1) / KT;
   PA_CK_LOAD(k0)
   PA_CK_STORE(0)
-
-  for (int ti = 0; ti < n_tiles; ++ti) {
-    const int kt = k0 + ti * KT;
-    const int buf = ti & 1;
-    if (ti + 1 < n_tiles) { PA_CK_LOAD(kt + KT) }
-    __syncthreads();
-
-    if (kt <= w_qpos_hi) {  // some row of this wave sees part of the tile
-      const char* kb = k_lds + buf * TILE_BYTES;
-      const char* vb = v_lds + buf * TILE_BYTES;
-      // ---- S^T = K Q^T ---------------------------------------------------
-      f32x16_t s[2];
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s[sub][e] = 0.f;
-        const int key = sub * 32 + (lane & 31);
-#pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) {
-          const int ch = (2 * kk + grp) ^ (key % CPR);
-          const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(kb + key * ROWB + ch * 16);
-          s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kv),
-                                                           __builtin_bit_cast(bf16x8_t, qf[kk]),
-                                                           s[sub], 0, 0, 0);
-        }
-      }
-      // ---- mask, online softmax --------------------------------------------
-      const bool need_mask = (kt + KT - 1 > w_qpos_lo) || (kt + KT > k1);
-      float mx = kNegInf;
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          if (need_mask) {
-            const int key = kt + sub * 32 + 8 * (e >> 2) + 4 * grp + (e & 3);
-            s[sub][e] = (key > qpos || key >= k1) ? kNegInf : s[sub][e];
-          }
-          mx = fmaxf(mx, s[sub][e]);
-        }
-      mx = fmaxf(mx, xor32(mx));
-      const float m_new = fmaxf(m_run, mx * sl);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      m_run = m_new;
-      float psum = 0.f;
-      uint32_t pk[2][8];
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int e = 0; e < 16; e += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][e], sl, -m_use));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][e + 1], sl, -m_use));
-          psum += p0 + p1;
-          pk[sub][e >> 1] = pack_bf16(p0, p1);
-        }
-      l_run = l_run * alpha + psum;
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
-      }
-      // ---- O^T += V^T P^T ----------------------------------------------------
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const u32x4_t pw = {pk[sub][4 * h], pk[sub][4 * h + 1], pk[sub][4 * h + 2], pk[sub][4 * h + 3]};
-          const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
-          const int kbase = sub * 32 + 16 * h + 4 * grp + (li >> 2);  // row m = li / 4
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const int d0 = db * 32 + 16 * (gam & 1) + 4 * (li & 3);   // 4 d values, 8 bytes
-            const int key1 = kbase, key2 = kbase + 8;
-            const int c1 = ((d0 >> 3) ^ (key1 % CPR)), c2 = ((d0 >> 3) ^ (key2 % CPR));
-            const int in_chunk = (d0 & 7) * 2;
-            const lds_s16x4_t* p1 = reinterpret_cast<const lds_s16x4_t*>(
-                (__attribute__((address_space(3))) const char*)(vb + key1 * ROWB + c1 * 16 + in_chunk));
-            const lds_s16x4_t* p2 = reinterpret_cast<const lds_s16x4_t*>(
-                (__attribute__((address_space(3))) const char*)(vb + key2 * ROWB + c2 * 16 + in_chunk));
-            const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_s16x4_t*>(p1));
-            const s16x4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_s16x4_t*>(p2));
-            const s16x8_t vv = __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
-            const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, vv);
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[db], 0, 0, 0);
-          }
-        }
+  for (int ti = 0; ti < n_tiles; ti += 2) {
+    // even tile: buffer 0
+    {
+      const int kt = k0 + ti * KT;
+      if (ti + 1 < n_tiles) { PA_CK_LOAD(kt + KT) }
+      __syncthreads();
+      if (kt <= w_qpos_hi)
+        chunk_tile<D, G, 0>(st, qf, kaddr, vaddr, kt, qpos, k1, w_qpos_lo, sl, lane);
+      if (ti + 1 < n_tiles) { PA_CK_STORE(1) }
     }
-    if (ti + 1 < n_tiles) { PA_CK_STORE(buf ^ 1) }
+    if (ti + 1 < n_tiles) {  // odd tile: buffer 1
+      const int kt = k0 + (ti + 1) * KT;
+      if (ti + 2 < n_tiles) { PA_CK_LOAD(kt + KT) }
+      __syncthreads();
+      if (kt <= w_qpos_hi)
+        chunk_tile<D, G, 1>(st, qf, kaddr, vaddr, kt, qpos, k1, w_qpos_lo, sl, lane);
+      if (ti + 2 < n_tiles) { PA_CK_STORE(0) }
+    }
   }
 #undef PA_CK_LOAD
+#undef PA_CK_LOAD_FULL
+#undef PA_CK_LOAD_TAIL
 #undef PA_CK_STORE
 
   // ---- epilogue ---------------------------------------------------------------
-  const float l_tot = l_run + xor32(l_run);
+  const float l_tot = st.l_run + xor32(st.l_run);
   if (!row_ok) return;
   const int t = t0 + tok0 + tau;
   if (part_base < 0) {
@@ -305,8 +390,8 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(AttnArgs a) {
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
         const int d = db * 32 + 8 * e4 + 4 * grp;
-        const uint2 w = make_uint2(pack_bf16(o[db][4 * e4] * inv, o[db][4 * e4 + 1] * inv),
-                                   pack_bf16(o[db][4 * e4 + 2] * inv, o[db][4 * e4 + 3] * inv));
+        const uint2 w = make_uint2(pack_bf16(st.o[db][4 * e4] * inv, st.o[db][4 * e4 + 1] * inv),
+                                   pack_bf16(st.o[db][4 * e4 + 2] * inv, st.o[db][4 * e4 + 3] * inv));
         *reinterpret_cast<uint2*>(orow + d * 2) = w;
       }
   } else {
@@ -318,11 +403,11 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(AttnArgs a) {
       for (int e4 = 0; e4 < 4; ++e4) {
         const int d = db * 32 + 8 * e4 + 4 * grp;
         *reinterpret_cast<float4*>(op + d) =
-            make_float4(o[db][4 * e4], o[db][4 * e4 + 1], o[db][4 * e4 + 2], o[db][4 * e4 + 3]);
+            make_float4(st.o[db][4 * e4], st.o[db][4 * e4 + 1], st.o[db][4 * e4 + 2], st.o[db][4 * e4 + 3]);
       }
     if (grp == 0) {
       float* mp = a.ml_part + (slot * a.Hq + hq) * 2;
-      mp[0] = m_run;
+      mp[0] = st.m_run;
       mp[1] = l_tot;
     }
   }
