@@ -77,11 +77,25 @@ __device__ __forceinline__ float xor32(float x) {
 }
 
 // LDS swizzle: 16-byte chunk c of key row k is stored at chunk c ^ swz(k).
-// swz takes the key's low three bits to {0,2,4,6,1,3,5,7}: eight consecutive
-// keys read at one chunk (the K operand) hit eight different bank groups, and
-// the four rows of a transposed V read (keys differing in the low two bits,
-// two adjacent chunks each) also cover all bank groups.
-__device__ __forceinline__ int swz(int key) { return ((key & 3) << 1) | ((key >> 2) & 1); }
+// gfx950 serves 256 bytes of LDS per clock (64 banks), i.e. 16 lanes of a
+// 16-byte read or 32 lanes of an 8-byte read at a time.  For 256-byte rows
+// (head_dim 128) swz(k) = (k & 3) << 2 | (k >> 2) & 3 is a bijection on k mod
+// 16, so the 16 consecutive key rows of a K-operand read land in 16 different
+// 16-byte bank groups, and the 4 rows x 4 chunks of a 32-lane transposed V
+// read (rows differing in k & 3) land in 16 different groups too.  For
+// 128-byte rows (head_dim 64) two rows share a bank row and swz(k) = (k >> 1)
+// & 7 separates 16 consecutive rows.
+template <int CPR>
+__device__ __forceinline__ int swz(int key) {
+  if constexpr (CPR == 16) return ((key & 3) << 2) | ((key >> 2) & 3);
+  else return (key >> 1) & 7;
+}
+
+// Lazy rescale threshold (log2 units): the running max used for the
+// exponentials is only raised when a row's tile max exceeds it by more than
+// this, so probabilities stay below 2^8 and are exact in fp32/bf16 range;
+// numerator and denominator share the same max, so the result is unchanged.
+constexpr float kRescaleSlack = 8.f;
 
 template <int D, int G>
 struct ChunkGeo {
@@ -109,7 +123,8 @@ template <int D, int G, int BUF>
 __device__ __forceinline__ void chunk_tile(ChunkState<D, G>& st,
                                            const u32x4_t (&qf)[ChunkGeo<D, G>::KSTEPS],
                                            const lds_cptr (&kaddr)[ChunkGeo<D, G>::KSTEPS],
-                                           const lds_cptr (&vaddr)[ChunkGeo<D, G>::DB], int kt,
+                                           const lds_cptr (&vaddr)[ChunkGeo<D, G>::DB],
+                                           const lds_cptr (&vaddr8)[ChunkGeo<D, G>::DB], int kt,
                                            int qpos, int k1, int w_qpos_lo, float sl, int lane) {
   using Gm = ChunkGeo<D, G>;
   constexpr int ROWB = Gm::ROWB, KSTEPS = Gm::KSTEPS, DB = Gm::DB, TILE_BYTES = Gm::TILE_BYTES;
@@ -148,11 +163,19 @@ __device__ __forceinline__ void chunk_tile(ChunkState<D, G>& st,
   for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
     for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[sub][e], s[sub][e + 1]));
-  mx = fmaxf(mx, xor32(mx));
-  const float m_new = fmaxf(st.m_run, mx * sl);
-  const float m_use = m_new == kNegInf ? 0.f : m_new;
-  const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_use);
-  st.m_run = m_new;
+  mx = fmaxf(mx, xor32(mx)) * sl;
+  if (__builtin_amdgcn_ballot_w64(mx > st.m_run + kRescaleSlack)) {
+    // some row's max grew past the slack: move every row to its true max
+    const float m_new = fmaxf(st.m_run, mx);
+    const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(st.m_run - m_new);
+    st.m_run = m_new;
+    st.l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) st.o[db][e] *= alpha;
+  }
+  const float m_use = st.m_run == kNegInf ? 0.f : st.m_run;
   uint32_t pk[2][8];
   float psum = 0.f;
 #pragma unroll
@@ -166,13 +189,7 @@ __device__ __forceinline__ void chunk_tile(ChunkState<D, G>& st,
       psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[sub][e >> 1]),
                                              __builtin_bit_cast(bf16x2_t, 0x3F803F80u), psum, false);
     }
-  st.l_run = st.l_run * alpha + psum;
-  if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) st.o[db][e] *= alpha;
-  }
+  st.l_run += psum;
   // ---- O^T += V^T P^T ---------------------------------------------------------
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub)
@@ -186,7 +203,7 @@ __device__ __forceinline__ void chunk_tile(ChunkState<D, G>& st,
         const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_s16x4_t*)(vaddr[db] + (2 + BUF) * TILE_BYTES + rowoff));
         const s16x4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_t*)(vaddr[db] + (2 + BUF) * TILE_BYTES + rowoff + 8 * ROWB));
+            (lds_s16x4_t*)(vaddr8[db] + (2 + BUF) * TILE_BYTES + rowoff));
         const s16x8_t vv = __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
         st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv), pf,
                                                            st.o[db], 0, 0, 0);
@@ -268,15 +285,18 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(AttnArgs a) {
   const lds_cptr lds0 = (lds_cptr)smem;
   lds_cptr kaddr[KSTEPS];
 #pragma unroll
-  for (int kk = 0; kk < KSTEPS; ++kk) kaddr[kk] = lds0 + l32 * ROWB + (((2 * kk + grp) ^ swz(l32)) << 4);
-  lds_cptr vaddr[DB];
+  for (int kk = 0; kk < KSTEPS; ++kk) kaddr[kk] = lds0 + l32 * ROWB + (((2 * kk + grp) ^ swz<CPR>(l32)) << 4);
+  // rows r and r + 8 of a transposed read have different swizzles, so the
+  // second read of each pair has its own lane address
+  lds_cptr vaddr[DB], vaddr8[DB];
   {
     const int row = 4 * grp + (li >> 2);                 // row m of the 4-row transposed block
     const int d0_in = 16 * (gam & 1) + 4 * (li & 3);     // d offset within the 32-wide block
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int d0 = db * 32 + d0_in;
-      vaddr[db] = lds0 + row * ROWB + (((d0 >> 3) ^ swz(row)) << 4) + (d0 & 7) * 2;
+      vaddr[db] = lds0 + row * ROWB + (((d0 >> 3) ^ swz<CPR>(row)) << 4) + (d0 & 7) * 2;
+      vaddr8[db] = lds0 + (row + 8) * ROWB + (((d0 >> 3) ^ swz<CPR>(row + 8)) << 4) + (d0 & 7) * 2;
     }
   }
   __syncthreads();  // bt_lds ready
@@ -303,7 +323,7 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(AttnArgs a) {
     const int pchunk = id % CPR;
     ld_key[i] = key;
     ld_lds[i] = key * ROWB + pchunk * 16;
-    const int col = g * ROWB + ((pchunk ^ swz(key)) << 4);
+    const int col = g * ROWB + ((pchunk ^ swz<CPR>(key)) << 4);
     ld_in[i] = (small_b ? (key & bmask) : key) * slot_stride + col;
     ld_dblk[i] = small_b ? (key >> lb) : 0;
   }
@@ -329,7 +349,7 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(AttnArgs a) {
     kabs = kabs < k1 ? kabs : k1 - 1;                                                     \
     const uint32_t blk = (uint32_t)bt_lds[(kabs >> lb) - blk_first];                      \
     const uint64_t off = (uint64_t)blk * block_bytes +                                    \
-        ((kabs & bmask) * slot_stride + g * ROWB + (((ld_lds[i] & (ROWB - 1)) >> 4 ^ swz(ld_key[i])) << 4)); \
+        ((kabs & bmask) * slot_stride + g * ROWB + ((((ld_lds[i] & (ROWB - 1)) >> 4) ^ swz<CPR>(ld_key[i])) << 4)); \
     kst[i] = *reinterpret_cast<const u32x4_t*>(kcache + off);                             \
     vst[i] = *reinterpret_cast<const u32x4_t*>(vcache + off);                             \
   });
@@ -361,7 +381,7 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(AttnArgs a) {
       if (ti + 1 < n_tiles) { PA_CK_LOAD(kt + KT) }
       __syncthreads();
       if (kt <= w_qpos_hi)
-        chunk_tile<D, G, 0>(st, qf, kaddr, vaddr, kt, qpos, k1, w_qpos_lo, sl, lane);
+        chunk_tile<D, G, 0>(st, qf, kaddr, vaddr, vaddr8, kt, qpos, k1, w_qpos_lo, sl, lane);
       if (ti + 1 < n_tiles) { PA_CK_STORE(1) }
     }
     if (ti + 1 < n_tiles) {  // odd tile: buffer 1
@@ -369,7 +389,7 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(AttnArgs a) {
       if (ti + 2 < n_tiles) { PA_CK_LOAD(kt + KT) }
       __syncthreads();
       if (kt <= w_qpos_hi)
-        chunk_tile<D, G, 1>(st, qf, kaddr, vaddr, kt, qpos, k1, w_qpos_lo, sl, lane);
+        chunk_tile<D, G, 1>(st, qf, kaddr, vaddr, vaddr8, kt, qpos, k1, w_qpos_lo, sl, lane);
       if (ti + 2 < n_tiles) { PA_CK_STORE(0) }
     }
   }
