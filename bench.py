@@ -71,11 +71,13 @@ def copy_calibration():
 
 
 def cpu_baseline(spec, d, budget_s):
-    """Time the fp64 oracle on a bounded sample of the same step: the decode
-    requests in flattened order until the time budget is spent.  The oracle
-    gets the generator's pre-write pool blocks and the step's query / new K/V
-    rows (copied from the device generator before any step ran) and does its
-    own slot mapping, write, gather and attention."""
+    """Time the fp64 oracle on a bounded sample of the same step: every decode
+    request in flattened order (until the time budget is spent), then the
+    step's prefill chunks (all their rows).  The oracle gets the generator's
+    pre-write pool blocks and the step's query / new K/V rows (copied from the
+    device generator before any step ran) and does its own slot mapping,
+    write, gather and attention.  `value` is the decode part in GB/s (the
+    metric's unit); the chunk part is reported in GFLOP/s."""
     import numpy as np
     import torch
     import oracle
@@ -86,41 +88,56 @@ def cpu_baseline(spec, d, budget_s):
         return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
 
     qsl = spec.query_start_loc
-    dec = [r for r in range(spec.R) if spec.query_lens[r] == 1]
-    spent = 0.0
-    bytes_done = 0
-    n = 0
-    for r in dec:
-        if spent >= budget_s:
-            break
+
+    def run_request(r):
+        q = int(spec.query_lens[r])
         L = int(spec.seq_lens[r])
+        c = L - q
         nblk = -(-L // spec.B)
         ids = torch.from_numpy(spec.block_table[r, :nblk].astype(np.int64)).to(d["key_cache"].device)
         kp = host(d["key_cache"].index_select(0, ids))
         vp = host(d["value_cache"].index_select(0, ids))
         t = int(qsl[r])
-        qrow = host(d["query"][t:t + 1])
-        knew = host(d["key"][t:t + 1])
-        vnew = host(d["value"][t:t + 1])
+        qrows = host(d["query"][t:t + q])
+        knew = host(d["key"][t:t + q])
+        vnew = host(d["value"][t:t + q])
         mini = np.arange(nblk, dtype=np.int32)[None]
         t0 = time.perf_counter()
-        sm = oracle.slot_mapping(mini, [1], [L - 1], spec.B)
+        sm = oracle.slot_mapping(mini, [q], [c], spec.B)
         oracle.write_kv(kp, vp, knew, vnew, sm, spec.B)
         K = oracle.gather_kv(kp, mini[0], L, spec.B)
         V = oracle.gather_kv(vp, mini[0], L, spec.B)
-        oracle.attention_rows(qrow, K, V, [L - 1], spec.scale, spec.dtype)
-        spent += time.perf_counter() - t0
-        bytes_done += L * spec.Hkv * spec.D * 2 * spec.esize + 2 * spec.Hq * spec.D * spec.esize \
-            + 4 * nblk + 12
+        oracle.attention_rows(qrows, K, V, c + np.arange(q), spec.scale, spec.dtype)
+        return time.perf_counter() - t0
+
+    dec = [r for r in range(spec.R) if spec.query_lens[r] == 1]
+    chunks = [r for r in range(spec.R) if spec.query_lens[r] > 1]
+    dec_s = 0.0
+    dec_bytes = 0
+    n = 0
+    for r in dec:
+        if dec_s >= budget_s:
+            break
+        dec_s += run_request(r)
+        L = int(spec.seq_lens[r])
+        dec_bytes += L * spec.Hkv * spec.D * 2 * spec.esize + 2 * spec.Hq * spec.D * spec.esize \
+            + 4 * (-(-L // spec.B)) + 12
         n += 1
+    ck_s = 0.0
+    ck_flops = 0
+    for r in chunks:
+        ck_s += run_request(r)
+        q, c = int(spec.query_lens[r]), int(spec.num_computed[r])
+        ck_flops += 4 * spec.D * spec.Hq * (q * c + q * (q + 1) // 2)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {
-        "value": round(bytes_done / spent / 1e9, 4) if spent > 0 else None,
+        "value": round(dec_bytes / dec_s / 1e9, 4) if dec_s > 0 else None,
         "unit": "GB/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{n} of {len(dec)} decode requests of the same step (fp64 numpy oracle: "
-                  f"slot mapping, write, gather, attention), {spent:.1f} s of oracle time",
+        "sample": f"{n} of {len(dec)} decode requests ({dec_s:.1f} s) and all {len(chunks)} prefill chunks "
+                  f"({ck_s:.1f} s) of the same step; fp64 numpy oracle: slot mapping, write, gather, attention",
+        "chunk_gflops": round(ck_flops / ck_s / 1e9, 3) if ck_s > 0 else None,
         "host_cpus": len(os.sched_getaffinity(0)),
     }
 
