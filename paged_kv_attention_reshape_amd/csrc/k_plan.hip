@@ -129,6 +129,7 @@ plan_kernel(const int32_t* __restrict__ qsl, const int32_t* __restrict__ seq_len
   __shared__ int32_t scan[4][kPlanThreads];   // inclusive scans of the 4 counts
   __shared__ int32_t s_q[kPlanThreads], s_L[kPlanThreads], s_t0[kPlanThreads];
   __shared__ int32_t carry[4];
+  __shared__ int32_t wsum[4][kPlanThreads / 64];
   const int tid = threadIdx.x;
   if (tid < 4) carry[tid] = 0;
   __syncthreads();
@@ -147,20 +148,32 @@ plan_kernel(const int32_t* __restrict__ qsl, const int32_t* __restrict__ seq_len
     s_L[tid] = L;
     s_t0[tid] = t0;
     const ReqCounts n = request_counts(q, L, ps);
-    scan[0][tid] = n.rw;
-    scan[1][tid] = n.ck;
-    scan[2][tid] = n.mg;
-    scan[3][tid] = n.ck_parts;
-    __syncthreads();
-    for (int off = 1; off < kPlanThreads; off <<= 1) {
-      int32_t v[4];
+    // block-wide inclusive scan of the 4 counts: wave scans with shuffles,
+    // then the 16 wave totals
+    int32_t v[4] = {n.rw, n.ck, n.mg, n.ck_parts};
+    const int lane = tid & 63, wave = tid >> 6;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) v[k] = tid >= off ? scan[k][tid - off] : 0;
-      __syncthreads();
+    for (int k = 0; k < 4; ++k) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) scan[k][tid] += v[k];
-      __syncthreads();
+      for (int o = 1; o < 64; o <<= 1) {
+        const int32_t y = __shfl_up(v[k], o, 64);
+        if (lane >= o) v[k] += y;
+      }
+      if (lane == 63) wsum[k][wave] = v[k];
     }
+    __syncthreads();
+    if (tid < 4) {
+      int32_t acc = 0;
+      for (int w = 0; w < kPlanThreads / 64; ++w) {
+        const int32_t t = wsum[tid][w];
+        wsum[tid][w] = acc;
+        acc += t;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) scan[k][tid] = v[k] + wsum[k][wave];
+    __syncthreads();
     auto view = [&](int rl) {
       ReqView v;
       v.r = base + rl;

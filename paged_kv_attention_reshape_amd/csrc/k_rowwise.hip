@@ -26,6 +26,8 @@
 //     v_dot2_f32_bf16 accumulates two tokens per instruction into fp32;
 //   * the next sub-tile's K and V are loaded before the current one is used.
 // fp32 caches use the same structure with plain FMAs.
+#include <stdlib.h>
+
 #include "pa_internal.h"
 
 namespace pa {
@@ -74,12 +76,16 @@ struct Geo {
   static_assert(NL >= 1 && RPL >= 2 && RPL % 2 == 0, "unsupported geometry");
 };
 
-template <bool BF16, int D, int G>
+// QLDS: keep the G query rows in LDS (read with broadcast ds_read_b128 in the
+// q.k loop) instead of registers: G * D / 4 fewer VGPRs per lane, which buys
+// occupancy (more waves, more loads in flight) for the large GQA groups.
+template <bool BF16, int D, int G, bool QLDS>
 __global__ void __launch_bounds__(64) rowwise_kernel(AttnArgs a) {
   using Gm = Geo<BF16, D, G>;
   constexpr int ROWB = Gm::ROWB, LPR = Gm::LPR, NL = Gm::NL, EPC = Gm::EPC;
   constexpr int LPRV = Gm::LPRV, RPI = Gm::RPI, RPL = Gm::RPL, HPL = Gm::HPL;
 
+  __shared__ __attribute__((aligned(16))) char q_lds[QLDS ? G * ROWB : 16];
   __shared__ float p_lds[16 * G];   // bf16: 8 token pairs x G dwords; fp32: 16 x G
   __shared__ float a_lds[G];        // per-head rescale factor of this sub-tile
   __shared__ float m_lds[G];
@@ -100,10 +106,16 @@ __global__ void __launch_bounds__(64) rowwise_kernel(AttnArgs a) {
   const int rsub = lane / LPRV;      // first V row of this lane (p.v layout)
   const int cv = lane % LPRV;        // 16-byte chunk of the V row
 
-  // query rows of the G heads, in the q.k lane layout
-  uint4 qv[G][NL];
-  {
-    const char* qb = static_cast<const char*>(a.query) + ((int64_t)t * a.Hq + g * G) * ROWB;
+  // query rows of the G heads, in the q.k lane layout (16-byte chunk
+  // i * LPR + c of each row); with QLDS the G rows are staged contiguously in
+  // LDS, which is the same byte order
+  const char* qb = static_cast<const char*>(a.query) + ((int64_t)t * a.Hq + g * G) * ROWB;
+  uint4 qv[QLDS ? 1 : G][QLDS ? 1 : NL];
+  if constexpr (QLDS) {
+    for (int o = lane * 16; o < G * ROWB; o += 64 * 16)
+      *reinterpret_cast<uint4*>(q_lds + o) = *reinterpret_cast<const uint4*>(qb + o);
+    __syncthreads();
+  } else {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -160,15 +172,21 @@ __global__ void __launch_bounds__(64) rowwise_kernel(AttnArgs a) {
     for (int h = 0; h < G; ++h) {
       float acc = 0.f;
 #pragma unroll
-      for (int i = 0; i < NL; ++i)
+      for (int i = 0; i < NL; ++i) {
+        uint4 qq;
+        if constexpr (QLDS)
+          qq = *reinterpret_cast<const uint4*>(q_lds + h * ROWB + (i * LPR + c) * 16);
+        else
+          qq = qv[h][i];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           if constexpr (BF16) {
-            acc = dot2(comp(kc[i], w), comp(qv[h][i], w), acc);
+            acc = dot2(comp(kc[i], w), comp(qq, w), acc);
           } else {
-            acc = __builtin_fmaf(__uint_as_float(comp(kc[i], w)), __uint_as_float(comp(qv[h][i], w)), acc);
+            acc = __builtin_fmaf(__uint_as_float(comp(kc[i], w)), __uint_as_float(comp(qq, w)), acc);
           }
         }
+      }
       acc += dpp<kQuadXor1>(acc);
       acc += dpp<kQuadXor2>(acc);
       s[h] = acc;
@@ -406,8 +424,31 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnArgs a) {
     default: return hipErrorInvalidValue;                             \
   }
 
+#define PA_DISPATCH_GDQ(FN, BF, DD, Q)                                \
+  switch (a.Hq / a.Hkv) {                                             \
+    case 1: kern = (const void*)FN<BF, DD, 1, Q>; break;              \
+    case 2: kern = (const void*)FN<BF, DD, 2, Q>; break;              \
+    case 4: kern = (const void*)FN<BF, DD, 4, Q>; break;              \
+    case 8: kern = (const void*)FN<BF, DD, 8, Q>; break;              \
+    default: return hipErrorInvalidValue;                             \
+  }
+
+#define PA_SELECT_Q(FN, Q)                                            \
+  if (a.bf16) {                                                       \
+    if (a.D == 64) { PA_DISPATCH_GDQ(FN, true, 64, Q) }               \
+    else if (a.D == 128) { PA_DISPATCH_GDQ(FN, true, 128, Q) }        \
+    else return hipErrorInvalidValue;                                 \
+  } else {                                                            \
+    if (a.D == 64) { PA_DISPATCH_GDQ(FN, false, 64, Q) }              \
+    else if (a.D == 128) { PA_DISPATCH_GDQ(FN, false, 128, Q) }       \
+    else return hipErrorInvalidValue;                                 \
+  }
+
 #define PA_SELECT(FN)                                                 \
   const void* kern = nullptr;                                         \
+  PA_SELECT_INTO(FN)
+
+#define PA_SELECT_INTO(FN)                                            \
   if (a.bf16) {                                                       \
     if (a.D == 64) { PA_DISPATCH_GD(FN, true, 64) }                   \
     else if (a.D == 128) { PA_DISPATCH_GD(FN, true, 128) }            \
@@ -420,9 +461,22 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnArgs a) {
 
 }  // namespace
 
+// Query rows go to LDS when that lowers the register footprint enough to
+// matter (large GQA groups); PA_DECODE_QLDS=0/1 overrides for measurement.
+static bool use_qlds(const AttnArgs& a) {
+  const char* e = getenv("PA_DECODE_QLDS");
+  if (e != nullptr && *e) return atoi(e) != 0;
+  return (a.Hq / a.Hkv) >= 8;
+}
+
 hipError_t launch_rowwise(const AttnArgs& a, hipStream_t s) {
   if (a.ps.n_rw == 0) return hipSuccess;
-  PA_SELECT(rowwise_kernel)
+  const void* kern = nullptr;
+  if (use_qlds(a)) {
+    PA_SELECT_Q(rowwise_kernel, true)
+  } else {
+    PA_SELECT_Q(rowwise_kernel, false)
+  }
   AttnArgs args = a;
   void* params[] = {&args};
   return hipLaunchKernel(kern, dim3(a.ps.n_rw, a.Hkv), dim3(64), params, 0, s);

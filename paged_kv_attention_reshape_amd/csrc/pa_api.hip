@@ -62,8 +62,8 @@ pa_status check_geometry(int32_t Hq, int32_t Hkv, int32_t D, int32_t B, int32_t 
 int64_t gcd64(int64_t a, int64_t b) { return b == 0 ? a : gcd64(b, a % b); }
 
 // Row-wise partition length: a power-of-two multiple of lcm(64, B), at most
-// 64 blocks (one block id per lane of the wavefront), chosen so that the
-// grid holds roughly 16 wavefronts per compute unit.
+// 64 blocks (one block id per lane of the wavefront) and 1024 keys, chosen so
+// that the grid holds roughly 32 wavefronts per compute unit.
 int32_t choose_split(int64_t rowwise_keys, int32_t Hkv, int32_t B) {
   const int64_t unit = 64 / gcd64(64, B) * B;
   const int64_t cap = std::max<int64_t>(unit, (int64_t)64 * B);
@@ -72,7 +72,7 @@ int32_t choose_split(int64_t rowwise_keys, int32_t Hkv, int32_t B) {
     int64_t s = (forced + unit - 1) / unit * unit;
     return (int32_t)std::min(s, cap / unit * unit);
   }
-  const int64_t target_waves = 256 * 16;
+  const int64_t target_waves = 256 * 32;
   const int64_t want = rowwise_keys * Hkv / target_waves;
   int64_t s = unit;
   while (s < want && s * 2 <= cap && s * 2 <= 1024) s *= 2;
@@ -80,9 +80,9 @@ int32_t choose_split(int64_t rowwise_keys, int32_t Hkv, int32_t B) {
 }
 
 // Key-segment length of the chunk kernel: a multiple of 64 keys between 512
-// and the kernel's limit, sized so the chunk work spreads over about eight
+// and the kernel's limit, sized so the chunk work spreads over about two
 // workgroups per compute unit (long histories are cut into segments that the
-// merge pass recombines).
+// merge pass recombines; longer segments mean fewer partials to merge).
 int32_t choose_segment(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R, int32_t M,
                        int32_t B, int32_t Hkv, const pa::PlanShape& ps) {
   const int64_t limit = pa::chunk_max_segment(B) / 64 * 64;
@@ -100,7 +100,7 @@ int32_t choose_segment(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t 
       tiles += (kmax + 63) / 64;
     }
   }
-  const int64_t target_items = 256 * 8;
+  const int64_t target_items = 256 * 2;
   const int64_t per_item = std::max<int64_t>(1, tiles * Hkv / target_items);
   int64_t seg = 512;
   while (seg < per_item * 64 && seg * 2 <= limit) seg *= 2;
