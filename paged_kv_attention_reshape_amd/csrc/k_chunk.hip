@@ -119,15 +119,15 @@ struct ChunkState {
 // One 64-key tile of the online-softmax loop on LDS buffer BUF.
 typedef const __attribute__((address_space(3))) char* lds_cptr;
 
-template <int D, int G, int BUF>
-__device__ __forceinline__ void chunk_tile(ChunkState<D, G>& st,
+template <int D, int G>
+__device__ __forceinline__ void chunk_tile(ChunkState<D, G>& st, lds_cptr kbuf, lds_cptr vbuf,
                                            const u32x4_t (&qf)[ChunkGeo<D, G>::KSTEPS],
-                                           const lds_cptr (&kaddr)[ChunkGeo<D, G>::KSTEPS],
-                                           const lds_cptr (&vaddr)[ChunkGeo<D, G>::DB],
-                                           const lds_cptr (&vaddr8)[ChunkGeo<D, G>::DB], int kt,
+                                           const int (&koff)[ChunkGeo<D, G>::KSTEPS],
+                                           const int (&voff)[ChunkGeo<D, G>::DB],
+                                           const int (&voff8)[ChunkGeo<D, G>::DB], int kt,
                                            int qpos, int k1, int w_qpos_lo, float sl, int lane) {
   using Gm = ChunkGeo<D, G>;
-  constexpr int ROWB = Gm::ROWB, KSTEPS = Gm::KSTEPS, DB = Gm::DB, TILE_BYTES = Gm::TILE_BYTES;
+  constexpr int ROWB = Gm::ROWB, KSTEPS = Gm::KSTEPS, DB = Gm::DB;
   const int grp = lane >> 5;
   // ---- S^T = K Q^T ---------------------------------------------------------
   f32x16_t s[2];
@@ -141,7 +141,7 @@ __device__ __forceinline__ void chunk_tile(ChunkState<D, G>& st,
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const u32x4_t kv = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
-          kaddr[kk] + BUF * TILE_BYTES + sub * 32 * ROWB);
+          kbuf + koff[kk] + sub * 32 * ROWB);
       s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kv),
                                                        __builtin_bit_cast(bf16x8_t, qf[kk]),
                                                        s[sub], 0, 0, 0);
@@ -201,9 +201,9 @@ __device__ __forceinline__ void chunk_tile(ChunkState<D, G>& st,
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_t*)(vaddr[db] + (2 + BUF) * TILE_BYTES + rowoff));
+            (lds_s16x4_t*)(vbuf + voff[db] + rowoff));
         const s16x4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_t*)(vaddr8[db] + (2 + BUF) * TILE_BYTES + rowoff));
+            (lds_s16x4_t*)(vbuf + voff8[db] + rowoff));
         const s16x8_t vv = __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
         st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv), pf,
                                                            st.o[db], 0, 0, 0);
@@ -218,8 +218,13 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(AttnArgs a) {
   constexpr int TILE_BYTES = Gm::TILE_BYTES, LOADS = Gm::LOADS;
   static_assert(LOADS >= 1, "tile too small");
 
-  extern __shared__ __attribute__((aligned(16))) char smem[];   // K[2], V[2], block ids
-  int32_t* bt_lds = reinterpret_cast<int32_t*>(smem + 4 * TILE_BYTES);
+  // double-buffered K and V tiles (four distinct LDS objects, so reads of one
+  // buffer need not wait for the DMA into the other) and the segment's block ids
+  __shared__ __attribute__((aligned(1024))) char k_lds0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char k_lds1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v_lds0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v_lds1[TILE_BYTES];
+  __shared__ int32_t bt_lds[kMaxSegBlocks];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -282,27 +287,31 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(AttnArgs a) {
   }
   // lane-constant LDS read offsets within a tile buffer
   const int l32 = lane & 31, grp = lane >> 5, gam = lane >> 4, li = lane & 15;
-  const lds_cptr lds0 = (lds_cptr)smem;
-  lds_cptr kaddr[KSTEPS];
+  int koff[KSTEPS];
 #pragma unroll
-  for (int kk = 0; kk < KSTEPS; ++kk) kaddr[kk] = lds0 + l32 * ROWB + (((2 * kk + grp) ^ swz<CPR>(l32)) << 4);
+  for (int kk = 0; kk < KSTEPS; ++kk) koff[kk] = l32 * ROWB + (((2 * kk + grp) ^ swz<CPR>(l32)) << 4);
   // rows r and r + 8 of a transposed read have different swizzles, so the
-  // second read of each pair has its own lane address
-  lds_cptr vaddr[DB], vaddr8[DB];
+  // second read of each pair has its own lane offset
+  int voff[DB], voff8[DB];
   {
     const int row = 4 * grp + (li >> 2);                 // row m of the 4-row transposed block
     const int d0_in = 16 * (gam & 1) + 4 * (li & 3);     // d offset within the 32-wide block
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int d0 = db * 32 + d0_in;
-      vaddr[db] = lds0 + row * ROWB + (((d0 >> 3) ^ swz<CPR>(row)) << 4) + (d0 & 7) * 2;
-      vaddr8[db] = lds0 + (row + 8) * ROWB + (((d0 >> 3) ^ swz<CPR>(row + 8)) << 4) + (d0 & 7) * 2;
+      voff[db] = row * ROWB + (((d0 >> 3) ^ swz<CPR>(row)) << 4) + (d0 & 7) * 2;
+      voff8[db] = (row + 8) * ROWB + (((d0 >> 3) ^ swz<CPR>(row + 8)) << 4) + (d0 & 7) * 2;
     }
   }
   __syncthreads();  // bt_lds ready
 
-  // global -> register staging, 16-byte chunks; thread's chunk i of a tile is
-  // key row ld_key[i], logical column (pchunk ^ swz(key)), LDS slot ld_lds[i]
+  // Tile loads are direct global -> LDS DMA (global_load_lds_dwordx4): lane l
+  // of a wave instruction writes 16 bytes at LDS base + 16 l, so each
+  // instruction fills RPK = 1024 / ROWB consecutive key rows; lane l takes
+  // row l / CPR, physical chunk l % CPR, and fetches logical chunk
+  // (l % CPR) ^ swz(row) of that row from the cache, which realises the
+  // swizzled layout.  Wave w issues instructions w * LOADS .. w * LOADS + LOADS-1.
+  constexpr int RPK = 1024 / ROWB;
   const char* kcache = static_cast<const char*>(a.kcache);
   const char* vcache = static_cast<const char*>(a.vcache);
   const uint32_t block_bytes = (uint32_t)a.B * a.Hkv * ROWB;
@@ -310,57 +319,52 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(AttnArgs a) {
   const int lb = 31 - __builtin_clz(a.B);   // block size is a power of two here
   const int bmask = a.B - 1;
   // Tiles start at multiples of 64 keys.  With B <= 64 (B divides 64) a
-  // thread's rows sit at a fixed offset inside their block and a fixed block
+  // lane's rows sit at a fixed offset inside their block and a fixed block
   // delta from the tile's first block; with B > 64 the whole tile lies in one
-  // block.  So the per-tile address is blk * block_bytes + a per-thread
-  // constant (+ a uniform in-block offset when B > 64).
+  // block.
   const bool small_b = a.B <= KT;
-  int ld_lds[LOADS], ld_key[LOADS], ld_in[LOADS], ld_dblk[LOADS];
+  int ld_row[LOADS], ld_in[LOADS], ld_dblk[LOADS], ld_col[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
-    const int id = i * kThreads + tid;
-    const int key = id / CPR;
-    const int pchunk = id % CPR;
-    ld_key[i] = key;
-    ld_lds[i] = key * ROWB + pchunk * 16;
-    const int col = g * ROWB + ((pchunk ^ swz<CPR>(key)) << 4);
-    ld_in[i] = (small_b ? (key & bmask) : key) * slot_stride + col;
-    ld_dblk[i] = small_b ? (key >> lb) : 0;
+    const int row = (wave * LOADS + i) * RPK + lane / CPR;
+    ld_row[i] = row;
+    ld_col[i] = g * ROWB + (((lane % CPR) ^ swz<CPR>(row)) << 4);
+    ld_in[i] = (small_b ? (row & bmask) : row) * slot_stride + ld_col[i];
+    ld_dblk[i] = small_b ? (row >> lb) : 0;
   }
-  u32x4_t kst[LOADS], vst[LOADS];
-  // full tile: every row of the tile is below k1
-#define PA_CK_LOAD_FULL(KT0)                                                              \
+  typedef __attribute__((address_space(3))) void* lds_vptr;
+  // All block ids are read from LDS before the first DMA of a tile is issued:
+  // the compiler cannot tell an LDS read from the DMA's LDS writes apart and
+  // would otherwise wait for the earlier DMAs of the same tile to land.
+#define PA_CK_DMA(KT0, KB, VB)                                                            \
   {                                                                                       \
-    const int bi0 = ((KT0) >> lb) - blk_first;                                            \
-    const int tile_in = small_b ? 0 : ((KT0) & bmask) * slot_stride;                     \
+    uint32_t blk[LOADS];                                                                  \
+    int inb[LOADS];                                                                       \
+    if ((KT0) + KT <= k1) {                                                               \
+      const int bi0 = ((KT0) >> lb) - blk_first;                                          \
+      const int tile_in = small_b ? 0 : ((KT0) & bmask) * slot_stride;                   \
+      static_for<LOADS>([&](auto I) {                                                     \
+        constexpr int i = I;                                                              \
+        blk[i] = (uint32_t)bt_lds[bi0 + ld_dblk[i]];                                      \
+        inb[i] = ld_in[i] + tile_in;                                                      \
+      });                                                                                 \
+    } else {                                                                              \
+      static_for<LOADS>([&](auto I) {                                                     \
+        constexpr int i = I;                                                              \
+        int kabs = (KT0) + ld_row[i];                                                     \
+        kabs = kabs < k1 ? kabs : k1 - 1; /* rows past the segment re-read a valid row */ \
+        blk[i] = (uint32_t)bt_lds[(kabs >> lb) - blk_first];                              \
+        inb[i] = (kabs & bmask) * slot_stride + ld_col[i];                                \
+      });                                                                                 \
+    }                                                                                     \
+    __builtin_amdgcn_sched_barrier(0);                                                    \
     static_for<LOADS>([&](auto I) {                                                       \
       constexpr int i = I;                                                                \
-      const uint32_t blk = (uint32_t)bt_lds[bi0 + ld_dblk[i]];                            \
-      const uint64_t off = (uint64_t)blk * block_bytes + (uint32_t)(ld_in[i] + tile_in);  \
-      kst[i] = *reinterpret_cast<const u32x4_t*>(kcache + off);                           \
-      vst[i] = *reinterpret_cast<const u32x4_t*>(vcache + off);                           \
+      const uint64_t off = (uint64_t)blk[i] * block_bytes + (uint32_t)inb[i];             \
+      __builtin_amdgcn_global_load_lds(kcache + off, (lds_vptr)((KB) + (wave * LOADS + i) * 1024), 16, 0, 0); \
+      __builtin_amdgcn_global_load_lds(vcache + off, (lds_vptr)((VB) + (wave * LOADS + i) * 1024), 16, 0, 0); \
     });                                                                                   \
   }
-  // last tile of the segment: rows at or past k1 re-read row k1 - 1 (finite data)
-#define PA_CK_LOAD_TAIL(KT0)                                                              \
-  static_for<LOADS>([&](auto I) {                                                         \
-    constexpr int i = I;                                                                  \
-    int kabs = (KT0) + ld_key[i];                                                         \
-    kabs = kabs < k1 ? kabs : k1 - 1;                                                     \
-    const uint32_t blk = (uint32_t)bt_lds[(kabs >> lb) - blk_first];                      \
-    const uint64_t off = (uint64_t)blk * block_bytes +                                    \
-        ((kabs & bmask) * slot_stride + g * ROWB + ((((ld_lds[i] & (ROWB - 1)) >> 4) ^ swz<CPR>(ld_key[i])) << 4)); \
-    kst[i] = *reinterpret_cast<const u32x4_t*>(kcache + off);                             \
-    vst[i] = *reinterpret_cast<const u32x4_t*>(vcache + off);                             \
-  });
-#define PA_CK_LOAD(KT0)                                                                   \
-  if ((KT0) + KT <= k1) { PA_CK_LOAD_FULL(KT0) } else { PA_CK_LOAD_TAIL(KT0) }
-#define PA_CK_STORE(BUF)                                                                  \
-  static_for<LOADS>([&](auto I) {                                                         \
-    constexpr int i = I;                                                                  \
-    *reinterpret_cast<u32x4_t*>(smem + (BUF) * TILE_BYTES + ld_lds[i]) = kst[i];          \
-    *reinterpret_cast<u32x4_t*>(smem + (2 + (BUF)) * TILE_BYTES + ld_lds[i]) = vst[i];    \
-  });
 
   ChunkState<D, G> st;
 #pragma unroll
@@ -372,31 +376,32 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(AttnArgs a) {
   const float sl = a.scale_log2;
 
   const int n_tiles = (k1 - k0 + KT - 1) / KT;
-  PA_CK_LOAD(k0)
-  PA_CK_STORE(0)
+  const lds_cptr kb0 = (lds_cptr)k_lds0, kb1 = (lds_cptr)k_lds1;
+  const lds_cptr vb0 = (lds_cptr)v_lds0, vb1 = (lds_cptr)v_lds1;
+  // vmcnt(0), expcnt/lgkmcnt unconstrained: this wave's DMA into LDS is done
+  constexpr int kWaitDma = 0x0F70;
+  PA_CK_DMA(k0, k_lds0, v_lds0)
   for (int ti = 0; ti < n_tiles; ti += 2) {
-    // even tile: buffer 0
+    // even tile: buffer 0.  Wait for its DMA, then a barrier makes every
+    // wave's part visible and guarantees buffer 1 is no longer being read.
     {
       const int kt = k0 + ti * KT;
-      if (ti + 1 < n_tiles) { PA_CK_LOAD(kt + KT) }
+      __builtin_amdgcn_s_waitcnt(kWaitDma);
       __syncthreads();
+      if (ti + 1 < n_tiles) { PA_CK_DMA(kt + KT, k_lds1, v_lds1) }
       if (kt <= w_qpos_hi)
-        chunk_tile<D, G, 0>(st, qf, kaddr, vaddr, vaddr8, kt, qpos, k1, w_qpos_lo, sl, lane);
-      if (ti + 1 < n_tiles) { PA_CK_STORE(1) }
+        chunk_tile<D, G>(st, kb0, vb0, qf, koff, voff, voff8, kt, qpos, k1, w_qpos_lo, sl, lane);
     }
     if (ti + 1 < n_tiles) {  // odd tile: buffer 1
       const int kt = k0 + (ti + 1) * KT;
-      if (ti + 2 < n_tiles) { PA_CK_LOAD(kt + KT) }
+      __builtin_amdgcn_s_waitcnt(kWaitDma);
       __syncthreads();
+      if (ti + 2 < n_tiles) { PA_CK_DMA(kt + KT, k_lds0, v_lds0) }
       if (kt <= w_qpos_hi)
-        chunk_tile<D, G, 1>(st, qf, kaddr, vaddr, vaddr8, kt, qpos, k1, w_qpos_lo, sl, lane);
-      if (ti + 2 < n_tiles) { PA_CK_STORE(0) }
+        chunk_tile<D, G>(st, kb1, vb1, qf, koff, voff, voff8, kt, qpos, k1, w_qpos_lo, sl, lane);
     }
   }
-#undef PA_CK_LOAD
-#undef PA_CK_LOAD_FULL
-#undef PA_CK_LOAD_TAIL
-#undef PA_CK_STORE
+#undef PA_CK_DMA
 
   // ---- epilogue ---------------------------------------------------------------
   const float l_tot = st.l_run + xor32(st.l_run);
@@ -433,10 +438,7 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(AttnArgs a) {
   }
 }
 
-template <int D>
-size_t chunk_smem() {
-  return 4 * (size_t)KT * D * 2 + kMaxSegBlocks * sizeof(int32_t);
-}
+
 
 }  // namespace
 
@@ -451,38 +453,17 @@ hipError_t launch_chunk(const AttnArgs& a, hipStream_t s) {
   if (a.ps.n_ck == 0) return hipSuccess;
   const int G = a.Hq / a.Hkv;
   const void* kern = nullptr;
-  size_t smem = 0;
 #define PA_CK(DD, GG) \
-  if (a.D == DD && G == GG) { kern = (const void*)chunk_kernel<DD, GG>; smem = chunk_smem<DD>(); }
+  if (a.D == DD && G == GG) { kern = (const void*)chunk_kernel<DD, GG>; }
   PA_CK(64, 1) PA_CK(64, 2) PA_CK(64, 4) PA_CK(64, 8)
   PA_CK(128, 1) PA_CK(128, 2) PA_CK(128, 4) PA_CK(128, 8)
 #undef PA_CK
   if (kern == nullptr) return hipErrorInvalidValue;
-  static bool attr_done[2] = {false, false};
-  if (smem > 64 * 1024) {
-    const int idx = a.D == 128 ? 1 : 0;
-    if (!attr_done[idx]) {
-      // every <D, G> instance of this D shares the size
-      const void* all[4] = {nullptr, nullptr, nullptr, nullptr};
-      if (a.D == 128) {
-        all[0] = (const void*)chunk_kernel<128, 1>; all[1] = (const void*)chunk_kernel<128, 2>;
-        all[2] = (const void*)chunk_kernel<128, 4>; all[3] = (const void*)chunk_kernel<128, 8>;
-      } else {
-        all[0] = (const void*)chunk_kernel<64, 1>; all[1] = (const void*)chunk_kernel<64, 2>;
-        all[2] = (const void*)chunk_kernel<64, 4>; all[3] = (const void*)chunk_kernel<64, 8>;
-      }
-      for (const void* k : all) {
-        hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        if (e != hipSuccess) return e;
-      }
-      attr_done[idx] = true;
-    }
-  }
   AttnArgs args = a;
   void* params[] = {&args};
   const int64_t units = (int64_t)a.ps.n_ck * a.Hkv;
   const int64_t per_xcd = (units + kXcds - 1) / kXcds;
-  return hipLaunchKernel(kern, dim3((unsigned)(per_xcd * kXcds)), dim3(kThreads), params, smem, s);
+  return hipLaunchKernel(kern, dim3((unsigned)(per_xcd * kXcds)), dim3(kThreads), params, 0, s);
 }
 
 }  // namespace pa
