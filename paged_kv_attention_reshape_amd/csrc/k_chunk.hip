@@ -147,6 +147,14 @@ __device__ __forceinline__ void chunk_tile(ChunkState<D, G>& st, lds_cptr kbuf, 
                                                        s[sub], 0, 0, 0);
     }
   }
+  // keep two k-steps of K reads in flight ahead of the MFMAs
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS - 2; ++kk) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   // ---- mask (diagonal / segment-end tiles only) and online softmax ----------
   if (kt + KT - 1 > w_qpos_lo || kt + KT > k1) {
     const int lim = min(qpos + 1, k1) - kt;   // keys < lim (relative) are visible
@@ -240,8 +248,8 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(AttnArgs a) {
   const int g = u / a.ps.n_ck;
   const int4 it = a.items_ck[u - g * a.ps.n_ck];
   const int r = it.x;
-  if (r < 0 || r >= a.R) return;
   const int qt = it.y, seg = it.z, part_base = it.w;
+  if (r < 0 || r >= a.R || qt < 0 || seg < 0) return;
 
   int q = a.qsl[r + 1] - a.qsl[r];
   int L = a.seq_lens[r];
@@ -310,60 +318,57 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(AttnArgs a) {
   // instruction fills RPK = 1024 / ROWB consecutive key rows; lane l takes
   // row l / CPR, physical chunk l % CPR, and fetches logical chunk
   // (l % CPR) ^ swz(row) of that row from the cache, which realises the
-  // swizzled layout.  Wave w issues instructions w * LOADS .. w * LOADS + LOADS-1.
+  // swizzled layout.  Wave w loads the tile's rows 16 w .. 16 w + 15.  The
+  // block size is a multiple of 16 and tiles start at multiples of 64 keys,
+  // so those 16 rows lie in one cache block: the block's address is
+  // wave-uniform (scalar registers) and each lane adds a fixed 32-bit offset.
   constexpr int RPK = 1024 / ROWB;
+  static_assert(LOADS * RPK == 16, "a wave loads 16 rows per tile");
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const char* kcache = static_cast<const char*>(a.kcache);
   const char* vcache = static_cast<const char*>(a.vcache);
   const uint32_t block_bytes = (uint32_t)a.B * a.Hkv * ROWB;
   const int slot_stride = a.Hkv * ROWB;
   const int lb = 31 - __builtin_clz(a.B);   // block size is a power of two here
   const int bmask = a.B - 1;
-  // Tiles start at multiples of 64 keys.  With B <= 64 (B divides 64) a
-  // lane's rows sit at a fixed offset inside their block and a fixed block
-  // delta from the tile's first block; with B > 64 the whole tile lies in one
-  // block.
-  const bool small_b = a.B <= KT;
-  int ld_row[LOADS], ld_in[LOADS], ld_dblk[LOADS], ld_col[LOADS];
+  int ld_rl[LOADS], ld_off[LOADS];          // row within the wave's 16, lane offset
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
-    const int row = (wave * LOADS + i) * RPK + lane / CPR;
-    ld_row[i] = row;
-    ld_col[i] = g * ROWB + (((lane % CPR) ^ swz<CPR>(row)) << 4);
-    ld_in[i] = (small_b ? (row & bmask) : row) * slot_stride + ld_col[i];
-    ld_dblk[i] = small_b ? (row >> lb) : 0;
+    const int rl = i * RPK + lane / CPR;
+    ld_rl[i] = rl;
+    ld_off[i] = rl * slot_stride + g * ROWB + (((lane % CPR) ^ swz<CPR>(wave * 16 + rl)) << 4);
   }
   typedef __attribute__((address_space(3))) void* lds_vptr;
-  // All block ids are read from LDS before the first DMA of a tile is issued:
-  // the compiler cannot tell an LDS read from the DMA's LDS writes apart and
-  // would otherwise wait for the earlier DMAs of the same tile to land.
-#define PA_CK_DMA(KT0, KB, VB)                                                            \
-  {                                                                                       \
-    uint32_t blk[LOADS];                                                                  \
-    int inb[LOADS];                                                                       \
-    if ((KT0) + KT <= k1) {                                                               \
-      const int bi0 = ((KT0) >> lb) - blk_first;                                          \
-      const int tile_in = small_b ? 0 : ((KT0) & bmask) * slot_stride;                   \
-      static_for<LOADS>([&](auto I) {                                                     \
-        constexpr int i = I;                                                              \
-        blk[i] = (uint32_t)bt_lds[bi0 + ld_dblk[i]];                                      \
-        inb[i] = ld_in[i] + tile_in;                                                      \
-      });                                                                                 \
-    } else {                                                                              \
-      static_for<LOADS>([&](auto I) {                                                     \
-        constexpr int i = I;                                                              \
-        int kabs = (KT0) + ld_row[i];                                                     \
-        kabs = kabs < k1 ? kabs : k1 - 1; /* rows past the segment re-read a valid row */ \
-        blk[i] = (uint32_t)bt_lds[(kabs >> lb) - blk_first];                              \
-        inb[i] = (kabs & bmask) * slot_stride + ld_col[i];                                \
-      });                                                                                 \
-    }                                                                                     \
-    __builtin_amdgcn_sched_barrier(0);                                                    \
-    static_for<LOADS>([&](auto I) {                                                       \
-      constexpr int i = I;                                                                \
-      const uint64_t off = (uint64_t)blk[i] * block_bytes + (uint32_t)inb[i];             \
-      __builtin_amdgcn_global_load_lds(kcache + off, (lds_vptr)((KB) + (wave * LOADS + i) * 1024), 16, 0, 0); \
-      __builtin_amdgcn_global_load_lds(vcache + off, (lds_vptr)((VB) + (wave * LOADS + i) * 1024), 16, 0, 0); \
-    });                                                                                   \
+  // The block id is read from LDS before the DMAs are issued: the compiler
+  // cannot tell that read from the DMA's LDS writes apart and would otherwise
+  // wait for the earlier DMAs to land.  In the segment's last tile a wave
+  // whose rows pass the segment end starts at the last valid 16-row group and
+  // clamps its rows to the last valid key (masked rows then hold finite
+  // values).
+#define PA_CK_DMA(KT0, KB, VB)                                                                  \
+  {                                                                                             \
+    const int wr0 = (KT0) + wave_u * 16;                                                        \
+    const bool wfull = wr0 + 16 <= k1;                                                          \
+    const int wrow = wfull ? wr0 : min(wr0, (k1 - 1) & ~15);                                    \
+    const uint32_t blk = (uint32_t)__builtin_amdgcn_readfirstlane(bt_lds[(wrow >> lb) - blk_first]); \
+    const uint64_t sb = (uint64_t)blk * block_bytes + (uint32_t)((wrow & bmask) * slot_stride); \
+    int off[LOADS];                                                                             \
+    static_for<LOADS>([&](auto I) {                                                             \
+      constexpr int i = I;                                                                      \
+      off[i] = ld_off[i];                                                                       \
+      if (!wfull) {                                                                             \
+        const int over = wrow + ld_rl[i] - (k1 - 1);                                            \
+        off[i] -= (over > 0 ? over : 0) * slot_stride;                                          \
+      }                                                                                         \
+    });                                                                                         \
+    __builtin_amdgcn_sched_barrier(0);                                                          \
+    static_for<LOADS>([&](auto I) {                                                             \
+      constexpr int i = I;                                                                      \
+      __builtin_amdgcn_global_load_lds(kcache + sb + (uint32_t)off[i],                         \
+                                       (lds_vptr)((KB) + (wave_u * LOADS + i) * 1024), 16, 0, 0); \
+      __builtin_amdgcn_global_load_lds(vcache + sb + (uint32_t)off[i],                         \
+                                       (lds_vptr)((VB) + (wave_u * LOADS + i) * 1024), 16, 0, 0); \
+    });                                                                                         \
   }
 
   ChunkState<D, G> st;

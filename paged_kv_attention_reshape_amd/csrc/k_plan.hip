@@ -7,7 +7,10 @@
 // counts into offsets.  Phase 2: the threads emit the records in parallel,
 // record index idx going to the request whose scanned range contains idx
 // (binary search in LDS), so a request with many records does not serialise
-// the kernel.  Every write is bounded by the capacities the host computed and
+// the kernel.  Phase 3 orders the chunk items by decreasing size of their
+// (request, key segment) group (a counting sort in LDS): workgroups are
+// dispatched in item order, and longest-first list scheduling keeps the
+// last, partly filled round of workgroups short.  Every write is bounded by the capacities the host computed and
 // unused trailing records get sentinels: device metadata that disagrees with
 // the host mirrors gives wrong numbers, never an out-of-bounds access.
 #include "pa_internal.h"
@@ -69,10 +72,11 @@ __device__ void emit_merge_rowwise(const ReqView& v, int32_t j, int32_t k_first,
 }
 
 // j-th chunk item of a chunk request whose partial slots start at pbase.
-// Items are ordered segment-major, (seg, qt): the q-tiles that read the same
-// key segment are consecutive, so the XCD-aware launch keeps them on one L2.
-// A q-tile's segment count grows with qt, so the q-tiles that have segment s
-// form a suffix of the tile range.
+// Items are ordered segment-major, (seg, qt descending): the q-tiles that
+// read the same key segment are consecutive, so the XCD-aware launch keeps
+// them on one L2, and within a segment the longer (later) q-tiles come
+// first.  A q-tile's segment count grows with qt, so the q-tiles that have
+// segment s form a suffix of the tile range.
 __device__ void emit_chunk(const ReqView& v, int32_t j, int32_t k, int32_t pbase,
                            const PlanShape& ps, int4* items_ck) {
   const int32_t nqt = cdiv(v.q, ps.TQ);
@@ -83,7 +87,7 @@ __device__ void emit_chunk(const ReqView& v, int32_t j, int32_t k, int32_t pbase
       if (cdiv(v.c + min32((qt + 1) * ps.TQ, v.q), ps.SEG) > sg) { first_qt = qt; break; }
     const int32_t count = nqt - first_qt;
     if (j < count) {
-      const int32_t qt = first_qt + j;
+      const int32_t qt = nqt - 1 - j;
       const int32_t nseg = cdiv(v.c + min32((qt + 1) * ps.TQ, v.q), ps.SEG);
       int32_t pb = pbase;  // partial slots of earlier split tiles
       for (int32_t t = 0; t < qt; ++t) {
@@ -123,9 +127,50 @@ __device__ void emit_merge_chunk(const ReqView& v, int32_t j, int32_t m, int32_t
   }
 }
 
+// Sort key of a chunk item: the 64-key tiles of its key segment for the
+// request's last q-tile (0 for a sentinel).  All q-tiles of one (request,
+// segment) share the key, so they stay together (they read the same keys
+// and values, which the XCD's L2 then serves); the item's own size is at
+// most 512 keys smaller.
+__device__ int32_t chunk_item_tiles(const int4 it, const int32_t* qsl, const int32_t* seq_lens,
+                                    const PlanShape& ps) {
+  const int32_t r = it.x;
+  if (r < 0 || r >= ps.R) return 0;
+  int32_t q = qsl[r + 1] - qsl[r];
+  int32_t L = seq_lens[r];
+  sanitize(q, L, ps.M, ps.B);
+  const int32_t k0 = it.z * ps.SEG;
+  const int32_t k1 = min32(k0 + ps.SEG, L);
+  return k1 > k0 ? cdiv(k1 - k0, 64) : 0;
+}
+
+// block-wide exclusive scan of one value per thread (1024 threads)
+__device__ int32_t block_exclusive_scan(int32_t x, int32_t* wsum16) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int32_t v = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t y = __shfl_up(v, o, 64);
+    if (lane >= o) v += y;
+  }
+  if (lane == 63) wsum16[wave] = v;
+  __syncthreads();
+  if (tid == 0) {
+    int32_t acc = 0;
+    for (int w = 0; w < kPlanThreads / 64; ++w) {
+      const int32_t t = wsum16[w];
+      wsum16[w] = acc;
+      acc += t;
+    }
+  }
+  __syncthreads();
+  return v - x + wsum16[wave];
+}
+
 __global__ void __launch_bounds__(kPlanThreads)
 plan_kernel(const int32_t* __restrict__ qsl, const int32_t* __restrict__ seq_lens, PlanShape ps,
-            int4* __restrict__ items_rw, int4* __restrict__ items_ck, int4* __restrict__ merge) {
+            int4* __restrict__ items_rw, int4* __restrict__ items_ck, int4* __restrict__ ck_stage,
+            int4* __restrict__ merge) {
   __shared__ int32_t scan[4][kPlanThreads];   // inclusive scans of the 4 counts
   __shared__ int32_t s_q[kPlanThreads], s_L[kPlanThreads], s_t0[kPlanThreads];
   __shared__ int32_t carry[4];
@@ -193,7 +238,7 @@ plan_kernel(const int32_t* __restrict__ qsl, const int32_t* __restrict__ seq_len
     for (int32_t idx = tid; idx < scan[1][n_here - 1]; idx += kPlanThreads) {
       const int rl = upper_bound(scan[1], n_here, idx);
       const int32_t pbase = ps.n_rw + carry[3] + excl(3, rl);
-      emit_chunk(view(rl), idx - excl(1, rl), carry[1] + idx, pbase, ps, items_ck);
+      emit_chunk(view(rl), idx - excl(1, rl), carry[1] + idx, pbase, ps, ck_stage);
     }
     // merge records
     for (int32_t idx = tid; idx < scan[2][n_here - 1]; idx += kPlanThreads) {
@@ -215,15 +260,40 @@ plan_kernel(const int32_t* __restrict__ qsl, const int32_t* __restrict__ seq_len
   // metadata disagrees with the host mirrors)
   for (int32_t i = carry[0] + tid; i < ps.n_rw; i += kPlanThreads) items_rw[i] = make_int4(-1, 0, 0, 0);
   for (int32_t i = carry[1] + tid; i < ps.n_ck; i += kPlanThreads) items_ck[i] = make_int4(-1, 0, 0, 0);
+
+  // phase 3: chunk items, longest first (bucket b holds items of 1023 - b
+  // tiles; larger items share bucket 0).  The staged items were written by
+  // this workgroup: the barrier makes them visible to all its threads.
+  const int32_t n_items = min32(carry[1], ps.n_ck);
+  if (n_items > 0) {
+    int32_t* hist = scan[0];
+    hist[tid] = 0;
+    __syncthreads();
+    for (int32_t i = tid; i < n_items; i += kPlanThreads) {
+      const int32_t t = chunk_item_tiles(ck_stage[i], qsl, seq_lens, ps);
+      atomicAdd(&hist[kPlanThreads - 1 - min32(t, kPlanThreads - 1)], 1);
+    }
+    __syncthreads();
+    const int32_t start = block_exclusive_scan(hist[tid], wsum[0]);
+    __syncthreads();
+    hist[tid] = start;
+    __syncthreads();
+    for (int32_t i = tid; i < n_items; i += kPlanThreads) {
+      const int4 it = ck_stage[i];
+      const int32_t t = chunk_item_tiles(it, qsl, seq_lens, ps);
+      const int32_t pos = atomicAdd(&hist[kPlanThreads - 1 - min32(t, kPlanThreads - 1)], 1);
+      if (pos < n_items) items_ck[pos] = it;
+    }
+  }
   for (int32_t i = carry[2] + tid; i < ps.n_mg; i += kPlanThreads) merge[i] = make_int4(-1, 0, 0, 0);
 }
 
 }  // namespace
 
 hipError_t launch_plan(const int32_t* qsl, const int32_t* seq_lens, const PlanShape& ps,
-                       int4* items_rw, int4* items_ck, int4* merge, hipStream_t s) {
+                       int4* items_rw, int4* items_ck, int4* ck_stage, int4* merge, hipStream_t s) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, qsl, seq_lens, ps, items_rw,
-                     items_ck, merge);
+                     items_ck, ck_stage, merge);
   return hipGetLastError();
 }
 

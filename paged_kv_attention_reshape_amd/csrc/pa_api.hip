@@ -361,7 +361,8 @@ pa_status pa_attention(void* out, const void* query, const void* key_cache,
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
   prof_mark(0, s);
-  hipError_t e = pa::launch_plan(query_start_loc, seq_lens, ps, a.items_rw, a.items_ck, a.merge, s);
+  hipError_t e = pa::launch_plan(query_start_loc, seq_lens, ps, a.items_rw, a.items_ck,
+                                  reinterpret_cast<int4*>(ws + wl.off_cks), a.merge, s);
   if (e != hipSuccess) return hip_fail(e, "plan launch");
   prof_mark(1, s);
   e = pa::launch_rowwise(a, s);

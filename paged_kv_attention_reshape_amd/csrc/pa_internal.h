@@ -113,7 +113,7 @@ __host__ __device__ inline ReqCounts request_counts(int32_t q, int32_t L, const 
 }
 
 struct WorkspaceLayout {
-  size_t off_rw, off_ck, off_mg, off_ml, off_o, total;
+  size_t off_rw, off_ck, off_cks, off_mg, off_ml, off_o, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -123,6 +123,7 @@ inline WorkspaceLayout workspace_layout(const PlanShape& ps, int32_t Hq, int32_t
   size_t o = 0;
   w.off_rw = o; o = align256(o + sizeof(int4) * (size_t)ps.n_rw);
   w.off_ck = o; o = align256(o + sizeof(int4) * (size_t)ps.n_ck);
+  w.off_cks = o; o = align256(o + sizeof(int4) * (size_t)ps.n_ck);   // chunk items before sorting
   w.off_mg = o; o = align256(o + sizeof(int4) * (size_t)ps.n_mg);
   const size_t parts = (size_t)ps.n_rw + (size_t)ps.n_ck_parts;
   w.off_ml = o; o = align256(o + sizeof(float) * 2 * parts * Hq);
@@ -143,7 +144,7 @@ hipError_t launch_slot_mapping(int64_t* slots, const int32_t* block_table, int32
                                int64_t T, int32_t num_blocks, int32_t B, hipStream_t s);
 
 hipError_t launch_plan(const int32_t* qsl, const int32_t* seq_lens, const PlanShape& ps,
-                       int4* items_rw, int4* items_ck, int4* merge, hipStream_t s);
+                       int4* items_rw, int4* items_ck, int4* ck_stage, int4* merge, hipStream_t s);
 
 struct AttnArgs {
   void* out;
