@@ -7,10 +7,12 @@
 // counts into offsets.  Phase 2: the threads emit the records in parallel,
 // record index idx going to the request whose scanned range contains idx
 // (binary search in LDS), so a request with many records does not serialise
-// the kernel.  Phase 3 orders the chunk items by decreasing size of their
-// (request, key segment) group (a counting sort in LDS): workgroups are
-// dispatched in item order, and longest-first list scheduling keeps the
-// last, partly filled round of workgroups short.  Every write is bounded by the capacities the host computed and
+// the kernel.  Phase 3 puts the items in launch order, longest first (a
+// counting sort in LDS): workgroups are dispatched in item order, and
+// longest-first list scheduling keeps the last, partly filled round of
+// workgroups short.  Row-wise items are sorted by their key count and keep
+// their plan-order index as partial slot (rw_slot); chunk items are sorted by
+// the size of their (request, key segment) group and carry their slots.  Every write is bounded by the capacities the host computed and
 // unused trailing records get sentinels: device metadata that disagrees with
 // the host mirrors gives wrong numbers, never an out-of-bounds access.
 #include "pa_internal.h"
@@ -167,10 +169,38 @@ __device__ int32_t block_exclusive_scan(int32_t x, int32_t* wsum16) {
   return v - x + wsum16[wave];
 }
 
+// Stable-enough counting sort of n staged records into out, by bucket
+// key(rec) in [0, kPlanThreads) ascending; slot_out (optional) receives each
+// record's staged index.  Within a bucket the order follows the atomics of
+// the LDS histogram (each wave's records stay in lane order).  Uses hist as
+// scratch; every thread of the block must call it.
+template <typename KeyFn>
+__device__ void bucket_sort(const int4* stage, int32_t n, KeyFn key, int4* out, int32_t* slot_out,
+                            int32_t* hist, int32_t* wsum16) {
+  const int tid = threadIdx.x;
+  hist[tid] = 0;
+  __syncthreads();
+  for (int32_t i = tid; i < n; i += kPlanThreads) atomicAdd(&hist[key(stage[i])], 1);
+  __syncthreads();
+  const int32_t start = block_exclusive_scan(hist[tid], wsum16);
+  __syncthreads();
+  hist[tid] = start;
+  __syncthreads();
+  for (int32_t i = tid; i < n; i += kPlanThreads) {
+    const int4 rec = stage[i];
+    const int32_t pos = atomicAdd(&hist[key(rec)], 1);
+    if (pos < n) {
+      out[pos] = rec;
+      if (slot_out != nullptr) slot_out[pos] = i;
+    }
+  }
+  __syncthreads();
+}
+
 __global__ void __launch_bounds__(kPlanThreads)
 plan_kernel(const int32_t* __restrict__ qsl, const int32_t* __restrict__ seq_lens, PlanShape ps,
-            int4* __restrict__ items_rw, int4* __restrict__ items_ck, int4* __restrict__ ck_stage,
-            int4* __restrict__ merge) {
+            int4* __restrict__ items_rw, int4* __restrict__ rw_stage, int32_t* __restrict__ rw_slot,
+            int4* __restrict__ items_ck, int4* __restrict__ ck_stage, int4* __restrict__ merge) {
   __shared__ int32_t scan[4][kPlanThreads];   // inclusive scans of the 4 counts
   __shared__ int32_t s_q[kPlanThreads], s_L[kPlanThreads], s_t0[kPlanThreads];
   __shared__ int32_t carry[4];
@@ -232,7 +262,7 @@ plan_kernel(const int32_t* __restrict__ qsl, const int32_t* __restrict__ seq_len
     // row-wise items
     for (int32_t idx = tid; idx < scan[0][n_here - 1]; idx += kPlanThreads) {
       const int rl = upper_bound(scan[0], n_here, idx);
-      emit_rowwise(view(rl), idx - excl(0, rl), carry[0] + idx, ps, items_rw);
+      emit_rowwise(view(rl), idx - excl(0, rl), carry[0] + idx, ps, rw_stage);
     }
     // chunk items
     for (int32_t idx = tid; idx < scan[1][n_here - 1]; idx += kPlanThreads) {
@@ -261,39 +291,34 @@ plan_kernel(const int32_t* __restrict__ qsl, const int32_t* __restrict__ seq_len
   for (int32_t i = carry[0] + tid; i < ps.n_rw; i += kPlanThreads) items_rw[i] = make_int4(-1, 0, 0, 0);
   for (int32_t i = carry[1] + tid; i < ps.n_ck; i += kPlanThreads) items_ck[i] = make_int4(-1, 0, 0, 0);
 
-  // phase 3: chunk items, longest first (bucket b holds items of 1023 - b
-  // tiles; larger items share bucket 0).  The staged items were written by
-  // this workgroup: the barrier makes them visible to all its threads.
-  const int32_t n_items = min32(carry[1], ps.n_ck);
-  if (n_items > 0) {
-    int32_t* hist = scan[0];
-    hist[tid] = 0;
-    __syncthreads();
-    for (int32_t i = tid; i < n_items; i += kPlanThreads) {
-      const int32_t t = chunk_item_tiles(ck_stage[i], qsl, seq_lens, ps);
-      atomicAdd(&hist[kPlanThreads - 1 - min32(t, kPlanThreads - 1)], 1);
-    }
-    __syncthreads();
-    const int32_t start = block_exclusive_scan(hist[tid], wsum[0]);
-    __syncthreads();
-    hist[tid] = start;
-    __syncthreads();
-    for (int32_t i = tid; i < n_items; i += kPlanThreads) {
-      const int4 it = ck_stage[i];
-      const int32_t t = chunk_item_tiles(it, qsl, seq_lens, ps);
-      const int32_t pos = atomicAdd(&hist[kPlanThreads - 1 - min32(t, kPlanThreads - 1)], 1);
-      if (pos < n_items) items_ck[pos] = it;
-    }
+  // phase 3: launch order, longest first.  The staged records were written
+  // by this workgroup: the barrier makes them visible to all its threads.
+  __syncthreads();
+  const int32_t n_rw_items = min32(carry[0], ps.n_rw);
+  if (n_rw_items > 0) {
+    auto rw_key = [&](const int4 it) {
+      const int32_t keys = (it.w & 0x7FFFFFFF) - it.z;
+      return kPlanThreads - 1 - min32(keys < 0 ? 0 : keys, kPlanThreads - 1);
+    };
+    bucket_sort(rw_stage, n_rw_items, rw_key, items_rw, rw_slot, scan[0], wsum[0]);
   }
-  for (int32_t i = carry[2] + tid; i < ps.n_mg; i += kPlanThreads) merge[i] = make_int4(-1, 0, 0, 0);
+  const int32_t n_ck_items = min32(carry[1], ps.n_ck);
+  if (n_ck_items > 0) {
+    auto ck_key = [&](const int4 it) {
+      const int32_t t = chunk_item_tiles(it, qsl, seq_lens, ps);
+      return kPlanThreads - 1 - min32(t, kPlanThreads - 1);
+    };
+    bucket_sort(ck_stage, n_ck_items, ck_key, items_ck, nullptr, scan[0], wsum[0]);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_plan(const int32_t* qsl, const int32_t* seq_lens, const PlanShape& ps,
-                       int4* items_rw, int4* items_ck, int4* ck_stage, int4* merge, hipStream_t s) {
+                       int4* items_rw, int4* rw_stage, int32_t* rw_slot, int4* items_ck,
+                       int4* ck_stage, int4* merge, hipStream_t s) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, qsl, seq_lens, ps, items_rw,
-                     items_ck, ck_stage, merge);
+                     rw_stage, rw_slot, items_ck, ck_stage, merge);
   return hipGetLastError();
 }
 

@@ -100,6 +100,7 @@ __global__ void __launch_bounds__(64) rowwise_kernel(AttnArgs a) {
   const int kb = it.z;
   const int ke = it.w & 0x7FFFFFFF;
   const bool direct = (it.w & kDirect) != 0;
+  const int slot = direct ? 0 : a.rw_slot[blockIdx.x];   // partial slot (plan order)
 
   const int j = lane >> 2;           // token of the sub-tile (q.k layout)
   const int c = lane & 3;            // quarter of the head dimension
@@ -322,7 +323,7 @@ __global__ void __launch_bounds__(64) rowwise_kernel(AttnArgs a) {
         }
       }
     } else {
-      float* op = a.o_part + ((int64_t)blockIdx.x * a.Hq + hq0) * D + cv * EPC;
+      float* op = a.o_part + ((int64_t)slot * a.Hq + hq0) * D + cv * EPC;
 #pragma unroll
       for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -331,7 +332,7 @@ __global__ void __launch_bounds__(64) rowwise_kernel(AttnArgs a) {
     }
   }
   if (!direct && lane < G) {
-    float* mp = a.ml_part + ((int64_t)blockIdx.x * a.Hq + g * G + lane) * 2;
+    float* mp = a.ml_part + ((int64_t)slot * a.Hq + g * G + lane) * 2;
     mp[0] = m_lds[lane];
     mp[1] = l_lds[lane];
   }

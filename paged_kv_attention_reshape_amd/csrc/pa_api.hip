@@ -354,6 +354,7 @@ pa_status pa_attention(void* out, const void* query, const void* key_cache,
   a.bf16 = bf16;
   a.ps = ps;
   a.items_rw = reinterpret_cast<int4*>(ws + wl.off_rw);
+  a.rw_slot = reinterpret_cast<const int32_t*>(ws + wl.off_rwslot);
   a.items_ck = reinterpret_cast<int4*>(ws + wl.off_ck);
   a.merge = reinterpret_cast<int4*>(ws + wl.off_mg);
   a.ml_part = reinterpret_cast<float*>(ws + wl.off_ml);
@@ -361,7 +362,9 @@ pa_status pa_attention(void* out, const void* query, const void* key_cache,
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
   prof_mark(0, s);
-  hipError_t e = pa::launch_plan(query_start_loc, seq_lens, ps, a.items_rw, a.items_ck,
+  hipError_t e = pa::launch_plan(query_start_loc, seq_lens, ps, a.items_rw,
+                                  reinterpret_cast<int4*>(ws + wl.off_rws),
+                                  reinterpret_cast<int32_t*>(ws + wl.off_rwslot), a.items_ck,
                                   reinterpret_cast<int4*>(ws + wl.off_cks), a.merge, s);
   if (e != hipSuccess) return hip_fail(e, "plan launch");
   prof_mark(1, s);

@@ -29,7 +29,9 @@ namespace pa {
 // ---------------------------------------------------------------------------
 
 // Records (int4):
-//   row-wise item  {r, t, kb, ke | kDirect}   t = flattened query row
+//   row-wise item  {r, t, kb, ke | kDirect}   t = flattened query row; the
+//                  items are launched longest first and rw_slot[i] is the
+//                  partial slot of launched item i (its index in plan order)
 //   chunk item     {r, qt, seg, part_base}    part_base < 0: single segment
 //   merge record   {t_first, first_part, n_parts, (n_tok << 8) | stride}:
 //                  tokens t_first + tau (tau < n_tok); token tau's partials
@@ -113,7 +115,7 @@ __host__ __device__ inline ReqCounts request_counts(int32_t q, int32_t L, const 
 }
 
 struct WorkspaceLayout {
-  size_t off_rw, off_ck, off_cks, off_mg, off_ml, off_o, total;
+  size_t off_rw, off_rws, off_rwslot, off_ck, off_cks, off_mg, off_ml, off_o, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -122,6 +124,8 @@ inline WorkspaceLayout workspace_layout(const PlanShape& ps, int32_t Hq, int32_t
   WorkspaceLayout w;
   size_t o = 0;
   w.off_rw = o; o = align256(o + sizeof(int4) * (size_t)ps.n_rw);
+  w.off_rws = o; o = align256(o + sizeof(int4) * (size_t)ps.n_rw);      // items in plan order
+  w.off_rwslot = o; o = align256(o + sizeof(int32_t) * (size_t)ps.n_rw);
   w.off_ck = o; o = align256(o + sizeof(int4) * (size_t)ps.n_ck);
   w.off_cks = o; o = align256(o + sizeof(int4) * (size_t)ps.n_ck);   // chunk items before sorting
   w.off_mg = o; o = align256(o + sizeof(int4) * (size_t)ps.n_mg);
@@ -144,7 +148,8 @@ hipError_t launch_slot_mapping(int64_t* slots, const int32_t* block_table, int32
                                int64_t T, int32_t num_blocks, int32_t B, hipStream_t s);
 
 hipError_t launch_plan(const int32_t* qsl, const int32_t* seq_lens, const PlanShape& ps,
-                       int4* items_rw, int4* items_ck, int4* ck_stage, int4* merge, hipStream_t s);
+                       int4* items_rw, int4* rw_stage, int32_t* rw_slot, int4* items_ck,
+                       int4* ck_stage, int4* merge, hipStream_t s);
 
 struct AttnArgs {
   void* out;
@@ -160,6 +165,7 @@ struct AttnArgs {
   bool bf16;
   PlanShape ps;
   int4* items_rw;
+  const int32_t* rw_slot;
   int4* items_ck;
   int4* merge;
   float* ml_part;     // [parts, Hq, 2] (running max in log2 units, sum)
