@@ -25,9 +25,9 @@
 //                 read straight from the row-major [key][d] LDS tile with
 //                 ds_read_b64_tr_b16 transposed loads.  O^T stays one query
 //                 row per lane, so the online-softmax rescale is lane-local.
-// K/V tiles of 64 keys are gathered through the block table (16-byte chunks,
-// rows XOR-swizzled in LDS against bank conflicts) into a double buffer while
-// the previous tile is on the matrix cores.
+// K/V tiles of 64 keys are gathered through the block table by global->LDS
+// DMA (16-byte chunks, rows XOR-swizzled in LDS against bank conflicts) into a
+// double buffer while the previous tile is on the matrix cores.
 #include "pa_internal.h"
 
 namespace pa {
@@ -41,7 +41,8 @@ typedef short s16x8_t __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
-constexpr int kThreads = 256;  // 4 waves
+constexpr int kThreads = kChunkRows * 2;  // one wave per 32 rows
+constexpr int kWaves = kThreads / 64;
 constexpr int KT = 64;         // keys per tile
 constexpr int kMaxSegBlocks = 512;
 constexpr int kXcds = 8;       // accelerator complex dies of an MI355X
@@ -103,7 +104,7 @@ struct ChunkGeo {
   static constexpr int CPR = ROWB / 16;     // 16-byte chunks per row
   static constexpr int KSTEPS = D / 16;     // MFMA k-steps for q.k
   static constexpr int DB = D / 32;         // 32-wide d blocks of O
-  static constexpr int TQ = 128 / G;
+  static constexpr int TQ = kChunkRows / G;
   static constexpr int TILE_BYTES = KT * ROWB;
   static constexpr int LOADS = KT * CPR / kThreads;  // 16-byte chunks per thread per tile
 };
@@ -116,21 +117,18 @@ struct ChunkState {
   float l_run;
 };
 
-// One 64-key tile of the online-softmax loop on LDS buffer BUF.
 typedef const __attribute__((address_space(3))) char* lds_cptr;
 
+
+// S^T = K Q^T for one 64-key tile: two 32-key halves, KSTEPS k-steps each.
+// The K fragments are read from the swizzled LDS tile two k-steps ahead of
+// the MFMAs that use them.
 template <int D, int G>
-__device__ __forceinline__ void chunk_tile(ChunkState<D, G>& st, lds_cptr kbuf, lds_cptr vbuf,
-                                           const u32x4_t (&qf)[ChunkGeo<D, G>::KSTEPS],
-                                           const int (&koff)[ChunkGeo<D, G>::KSTEPS],
-                                           const int (&voff)[ChunkGeo<D, G>::DB],
-                                           const int (&voff8)[ChunkGeo<D, G>::DB], int kt,
-                                           int qpos, int k1, int w_qpos_lo, float sl, int lane) {
+__device__ __forceinline__ void chunk_qk(f32x16_t (&s)[2], lds_cptr kbuf,
+                                         const u32x4_t (&qf)[ChunkGeo<D, G>::KSTEPS],
+                                         const int (&koff)[ChunkGeo<D, G>::KSTEPS]) {
   using Gm = ChunkGeo<D, G>;
-  constexpr int ROWB = Gm::ROWB, KSTEPS = Gm::KSTEPS, DB = Gm::DB;
-  const int grp = lane >> 5;
-  // ---- S^T = K Q^T ---------------------------------------------------------
-  f32x16_t s[2];
+  constexpr int ROWB = Gm::ROWB, KSTEPS = Gm::KSTEPS;
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
@@ -147,7 +145,6 @@ __device__ __forceinline__ void chunk_tile(ChunkState<D, G>& st, lds_cptr kbuf, 
                                                        s[sub], 0, 0, 0);
     }
   }
-  // keep two k-steps of K reads in flight ahead of the MFMAs
   __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
   for (int kk = 0; kk < KSTEPS - 2; ++kk) {
@@ -155,7 +152,17 @@ __device__ __forceinline__ void chunk_tile(ChunkState<D, G>& st, lds_cptr kbuf, 
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
   }
   __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-  // ---- mask (diagonal / segment-end tiles only) and online softmax ----------
+}
+
+// Mask (diagonal / segment-end tiles only), lazy online-softmax update and
+// the tile's probabilities as bf16 pairs in the MFMA operand order.
+template <int D, int G>
+__device__ __forceinline__ void chunk_softmax(ChunkState<D, G>& st, f32x16_t (&s)[2],
+                                              uint32_t (&pk)[2][8], int kt, int qpos, int k1,
+                                              int w_qpos_lo, float sl, int lane) {
+  using Gm = ChunkGeo<D, G>;
+  constexpr int DB = Gm::DB;
+  const int grp = lane >> 5;
   if (kt + KT - 1 > w_qpos_lo || kt + KT > k1) {
     const int lim = min(qpos + 1, k1) - kt;   // keys < lim (relative) are visible
 #pragma unroll
@@ -184,7 +191,6 @@ __device__ __forceinline__ void chunk_tile(ChunkState<D, G>& st, lds_cptr kbuf, 
       for (int e = 0; e < 16; ++e) st.o[db][e] *= alpha;
   }
   const float m_use = st.m_run == kNegInf ? 0.f : st.m_run;
-  uint32_t pk[2][8];
   float psum = 0.f;
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub)
@@ -198,7 +204,16 @@ __device__ __forceinline__ void chunk_tile(ChunkState<D, G>& st, lds_cptr kbuf, 
                                              __builtin_bit_cast(bf16x2_t, 0x3F803F80u), psum, false);
     }
   st.l_run += psum;
-  // ---- O^T += V^T P^T ---------------------------------------------------------
+}
+
+// O^T += V^T P^T for one tile: V^T fragments by transposed LDS reads.
+template <int D, int G>
+__device__ __forceinline__ void chunk_pv(ChunkState<D, G>& st, lds_cptr vbuf,
+                                         const uint32_t (&pk)[2][8],
+                                         const int (&voff)[ChunkGeo<D, G>::DB],
+                                         const int (&voff8)[ChunkGeo<D, G>::DB]) {
+  using Gm = ChunkGeo<D, G>;
+  constexpr int ROWB = Gm::ROWB, DB = Gm::DB;
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
@@ -219,8 +234,23 @@ __device__ __forceinline__ void chunk_tile(ChunkState<D, G>& st, lds_cptr kbuf, 
     }
 }
 
+// One whole 64-key tile in order: q.k, softmax, p.v.
 template <int D, int G>
-__global__ void __launch_bounds__(kThreads, 2) chunk_kernel(AttnArgs a) {
+__device__ __forceinline__ void chunk_tile(ChunkState<D, G>& st, lds_cptr kbuf, lds_cptr vbuf,
+                                           const u32x4_t (&qf)[ChunkGeo<D, G>::KSTEPS],
+                                           const int (&koff)[ChunkGeo<D, G>::KSTEPS],
+                                           const int (&voff)[ChunkGeo<D, G>::DB],
+                                           const int (&voff8)[ChunkGeo<D, G>::DB], int kt,
+                                           int qpos, int k1, int w_qpos_lo, float sl, int lane) {
+  f32x16_t s[2];
+  uint32_t pk[2][8];
+  chunk_qk<D, G>(s, kbuf, qf, koff);
+  chunk_softmax<D, G>(st, s, pk, kt, qpos, k1, w_qpos_lo, sl, lane);
+  chunk_pv<D, G>(st, vbuf, pk, voff, voff8);
+}
+
+template <int D, int G>
+__global__ void __launch_bounds__(kThreads, 512 / kThreads) chunk_kernel(AttnArgs a) {
   using Gm = ChunkGeo<D, G>;
   constexpr int ROWB = Gm::ROWB, CPR = Gm::CPR, KSTEPS = Gm::KSTEPS, DB = Gm::DB, TQ = Gm::TQ;
   constexpr int TILE_BYTES = Gm::TILE_BYTES, LOADS = Gm::LOADS;
@@ -318,12 +348,14 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(AttnArgs a) {
   // instruction fills RPK = 1024 / ROWB consecutive key rows; lane l takes
   // row l / CPR, physical chunk l % CPR, and fetches logical chunk
   // (l % CPR) ^ swz(row) of that row from the cache, which realises the
-  // swizzled layout.  Wave w loads the tile's rows 16 w .. 16 w + 15.  The
-  // block size is a multiple of 16 and tiles start at multiples of 64 keys,
-  // so those 16 rows lie in one cache block: the block's address is
-  // wave-uniform (scalar registers) and each lane adds a fixed 32-bit offset.
+  // swizzled layout.  Wave w loads the tile's rows WROWS w .. WROWS w + WROWS-1
+  // (WROWS = 64 / waves, 8 or 16).  The block size is a multiple of 16 and
+  // tiles start at multiples of 64 keys, so those rows lie in one cache block:
+  // the block's address is wave-uniform (scalar registers) and each lane adds
+  // a fixed 32-bit offset.
   constexpr int RPK = 1024 / ROWB;
-  static_assert(LOADS * RPK == 16, "a wave loads 16 rows per tile");
+  constexpr int WROWS = KT / kWaves;       // rows of a tile one wave loads
+  static_assert(LOADS * RPK == WROWS && WROWS % 8 == 0, "a wave loads WROWS rows per tile");
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const char* kcache = static_cast<const char*>(a.kcache);
   const char* vcache = static_cast<const char*>(a.vcache);
@@ -336,7 +368,7 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(AttnArgs a) {
   for (int i = 0; i < LOADS; ++i) {
     const int rl = i * RPK + lane / CPR;
     ld_rl[i] = rl;
-    ld_off[i] = rl * slot_stride + g * ROWB + (((lane % CPR) ^ swz<CPR>(wave * 16 + rl)) << 4);
+    ld_off[i] = rl * slot_stride + g * ROWB + (((lane % CPR) ^ swz<CPR>(wave * WROWS + rl)) << 4);
   }
   typedef __attribute__((address_space(3))) void* lds_vptr;
   // The block id is read from LDS before the DMAs are issued: the compiler
@@ -347,9 +379,9 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(AttnArgs a) {
   // values).
 #define PA_CK_DMA(KT0, KB, VB)                                                                  \
   {                                                                                             \
-    const int wr0 = (KT0) + wave_u * 16;                                                        \
-    const bool wfull = wr0 + 16 <= k1;                                                          \
-    const int wrow = wfull ? wr0 : min(wr0, (k1 - 1) & ~15);                                    \
+    const int wr0 = (KT0) + wave_u * WROWS;                                                     \
+    const bool wfull = wr0 + WROWS <= k1;                                                       \
+    const int wrow = wfull ? wr0 : min(wr0, (k1 - 1) & ~(WROWS - 1));                           \
     const uint32_t blk = (uint32_t)__builtin_amdgcn_readfirstlane(bt_lds[(wrow >> lb) - blk_first]); \
     const uint64_t sb = (uint64_t)blk * block_bytes + (uint32_t)((wrow & bmask) * slot_stride); \
     int off[LOADS];                                                                             \

@@ -63,7 +63,7 @@ __device__ void emit_merge_rowwise(const ReqView& v, int32_t j, int32_t k_first,
     if (parts > 1) {
       if (j == 0) {
         if (m < ps.n_mg)
-          merge[m] = item + parts <= ps.n_rw ? make_int4(v.t0 + i, item, parts, (1 << 8) | 1)
+          merge[m] = item + parts <= ps.n_rw ? make_int4(v.t0 + i, item, parts, (1 << 16) | 1)
                                              : make_int4(-1, 0, 0, 0);
         return;
       }
@@ -119,7 +119,7 @@ __device__ void emit_merge_chunk(const ReqView& v, int32_t j, int32_t m, int32_t
         const int32_t n = min32(ps.MT, ntok - tau0);
         const bool split = pbase + nseg * ps.TQ <= ps.n_rw + ps.n_ck_parts;
         if (m < ps.n_mg)
-          merge[m] = split ? make_int4(v.t0 + qt * ps.TQ + tau0, pbase + tau0, nseg, (n << 8) | ps.TQ)
+          merge[m] = split ? make_int4(v.t0 + qt * ps.TQ + tau0, pbase + tau0, nseg, (n << 16) | ps.TQ)
                            : make_int4(-1, 0, 0, 0);
         return;
       }

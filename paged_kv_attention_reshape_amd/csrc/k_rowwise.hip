@@ -362,7 +362,7 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnArgs a) {
   const int4 mr = a.merge[blockIdx.x];
   const int t_first = mr.x;
   if (t_first < 0) return;
-  const int first = mr.y, n = mr.z, n_tok = mr.w >> 8, stride = mr.w & 0xFF;
+  const int first = mr.y, n = mr.z, n_tok = mr.w >> 16, stride = mr.w & 0xFFFF;
   const int g = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;

@@ -33,7 +33,7 @@ namespace pa {
 //                  items are launched longest first and rw_slot[i] is the
 //                  partial slot of launched item i (its index in plan order)
 //   chunk item     {r, qt, seg, part_base}    part_base < 0: single segment
-//   merge record   {t_first, first_part, n_parts, (n_tok << 8) | stride}:
+//   merge record   {t_first, first_part, n_parts, (n_tok << 16) | stride}:
 //                  tokens t_first + tau (tau < n_tok); token tau's partials
 //                  are first_part + tau + p * stride, p < n_parts.  One record
 //                  per split decode row (n_tok 1, stride 1) or per group of at
@@ -44,7 +44,8 @@ constexpr int32_t kDirect = (int32_t)0x80000000;
 
 // Number of query tokens per chunk-kernel tile as a function of the GQA group:
 // a tile is always 128 (token, head) rows of one kv head.
-__host__ __device__ inline int32_t chunk_tile_tokens(int32_t G) { return 128 / G; }
+constexpr int32_t kChunkRows = 128;
+__host__ __device__ inline int32_t chunk_tile_tokens(int32_t G) { return kChunkRows / G; }
 __host__ __device__ inline int32_t chunk_merge_tokens(int32_t G) { return G >= 16 ? 1 : 16 / G; }
 
 struct PlanShape {
