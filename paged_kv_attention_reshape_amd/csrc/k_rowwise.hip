@@ -371,9 +371,12 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnArgs a) {
     const int tau = pair / G;
     const int hq = g * G + pair % G;
     const int64_t p0 = first + tau;
-    // max over partitions
-    float M = kNegInf;
-    for (int pb = 0; pb < n; pb += 64) {
+    // (m, l) of up to 64 partitions per pass: lane p holds partition p's pair;
+    // with at most 64 partitions (the usual case) one load serves both passes
+    float2 ml0 = make_float2(kNegInf, 0.f);
+    if (lane < n) ml0 = *reinterpret_cast<const float2*>(a.ml_part + ((p0 + (int64_t)lane * stride) * a.Hq + hq) * 2);
+    float M = ml0.x;
+    for (int pb = 64; pb < n; pb += 64) {
       const int p = pb + lane;
       const float m = p < n ? a.ml_part[((p0 + (int64_t)p * stride) * a.Hq + hq) * 2] : kNegInf;
       M = fmaxf(M, m);
@@ -387,16 +390,33 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnArgs a) {
       const int p = pb + lane;
       float w = 0.f;
       if (p < n) {
-        const float* ml = a.ml_part + ((p0 + (int64_t)p * stride) * a.Hq + hq) * 2;
-        w = __builtin_amdgcn_exp2f(ml[0] - M);
-        den += w * ml[1];
+        const float2 ml = pb == 0 ? ml0
+            : *reinterpret_cast<const float2*>(a.ml_part + ((p0 + (int64_t)p * stride) * a.Hq + hq) * 2);
+        w = __builtin_amdgcn_exp2f(ml.x - M);
+        den += w * ml.y;
       }
       const int cnt = min(64, n - pb);
-      for (int j = 0; j < cnt; ++j) {
-        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));
-        const float* op = a.o_part + ((p0 + (int64_t)(pb + j) * stride) * a.Hq + hq) * D + lane * PER;
+      const float* obase = a.o_part + ((p0 + (int64_t)pb * stride) * a.Hq + hq) * D + lane * PER;
+      const int64_t pstep = (int64_t)stride * a.Hq * D;   // floats between partitions
+      // eight partitions' slices in flight at a time
+      int j = 0;
+      for (; j + 8 <= cnt; j += 8) {
+        float v[8][PER];
 #pragma unroll
-        for (int e = 0; e < PER; ++e) num[e] += wj * op[e];
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int e = 0; e < PER; ++e) v[u][e] = obase[(j + u) * pstep + e];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j + u));
+#pragma unroll
+          for (int e = 0; e < PER; ++e) num[e] += wj * v[u][e];
+        }
+      }
+      for (; j < cnt; ++j) {
+        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));
+#pragma unroll
+        for (int e = 0; e < PER; ++e) num[e] += wj * obase[j * pstep + e];
       }
     }
     den = wave_sum(den);

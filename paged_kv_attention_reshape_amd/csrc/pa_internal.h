@@ -38,7 +38,8 @@ namespace pa {
 //                  are first_part + tau + p * stride, p < n_parts.  One record
 //                  per split decode row (n_tok 1, stride 1) or per group of at
 //                  most MT = chunk_merge_tokens(G) tokens of a split chunk tile
-//                  (stride TQ), so a record is at most 16 (token, head) pairs.
+//                  (stride TQ), so a record is at most max(4, G) (token, head)
+//                  pairs: one per wave of the merge workgroup.
 // Unused trailing records hold r = -1 / t = -1.
 constexpr int32_t kDirect = (int32_t)0x80000000;
 
@@ -46,7 +47,7 @@ constexpr int32_t kDirect = (int32_t)0x80000000;
 // a tile is always 128 (token, head) rows of one kv head.
 constexpr int32_t kChunkRows = 128;
 __host__ __device__ inline int32_t chunk_tile_tokens(int32_t G) { return kChunkRows / G; }
-__host__ __device__ inline int32_t chunk_merge_tokens(int32_t G) { return G >= 16 ? 1 : 16 / G; }
+__host__ __device__ inline int32_t chunk_merge_tokens(int32_t G) { return G >= 4 ? 1 : 4 / G; }
 
 struct PlanShape {
   int32_t R;
