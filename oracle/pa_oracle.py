@@ -45,6 +45,15 @@ What it computes, and where the pages define it
                        "可运行等价性与成本核算": blocks released, tokens recomputed
                        and the swap round-trip bound 2 * payload / bandwidth.
 * kv_bytes_per_token -- "显存与调度", equation kappa = 2 L n_kv d_head b_kv.
+* rope              -- "AI Infra入门干货总结…", section "Attention Module
+                       (以标准GQA + RoPE为例)": Q and K of a token are multiplied
+                       by a block-diagonal rotation matrix whose angles come
+                       from the row of a precomputed cos_sin_cache
+                       [max_position, rotary_dim] selected by the token's
+                       position; the kernel realises it elementwise with
+                       sin/cos, the oracle builds the matrix and multiplies.
+* rope_write_kv     -- same section, step order: rotate Q and K, then scatter
+                       the rotated K (and V) into the paged cache by slot.
 
 Every function here is pinned by tests against values and properties the pages
 and the mathematics fix (worked examples, closed forms, brute force,
@@ -70,6 +79,9 @@ __all__ = [
     "block_accounting",
     "preemption_accounting",
     "kv_bytes_per_token",
+    "rope_matrix",
+    "rope",
+    "rope_write_kv",
 ]
 
 
@@ -331,6 +343,71 @@ def merge_partials(m: np.ndarray, l: np.ndarray, o: np.ndarray) -> np.ndarray:
 
 
 __all__.append("merge_partials")
+
+
+# ----------------------------------------------------------------------------
+# rotary position embedding ("Attention Module (以标准GQA + RoPE为例)")
+# ----------------------------------------------------------------------------
+def _rope_pairs(rotary_dim: int, neox: bool) -> List[Tuple[int, int]]:
+    """Coordinate pairs the 2x2 rotation blocks act on; pair i uses angle
+    column i of the cache.  Adjacent pairs (2i, 2i+1) when neox is False;
+    split halves (i, i + rotary_dim/2) when neox is True."""
+    half = rotary_dim // 2
+    if neox:
+        return [(i, i + half) for i in range(half)]
+    return [(2 * i, 2 * i + 1) for i in range(half)]
+
+
+def rope_matrix(cos_sin_row: np.ndarray, head_dim: int, rotary_dim: int,
+                neox: bool) -> np.ndarray:
+    """[head_dim, head_dim] rotation for one position, fp64.
+
+    cos_sin_row holds rotary_dim values: cos of the rotary_dim/2 angles, then
+    their sin.  Pair (a, b) with angle column i gets the block
+    [[cos_i, -sin_i], [sin_i, cos_i]]; dimensions at or past rotary_dim keep
+    the identity.  A pure rotation: the matrix is orthogonal (pinned)."""
+    row = np.asarray(cos_sin_row, dtype=np.float64)
+    half = rotary_dim // 2
+    R = np.eye(head_dim, dtype=np.float64)
+    for i, (a, b) in enumerate(_rope_pairs(rotary_dim, neox)):
+        c, s = row[i], row[half + i]
+        R[a, a] = c
+        R[a, b] = -s
+        R[b, a] = s
+        R[b, b] = c
+    return R
+
+
+def rope(x: np.ndarray, positions: np.ndarray, cos_sin_cache: np.ndarray,
+         rotary_dim: int, neox: bool) -> np.ndarray:
+    """Rotate x [T, H, head_dim] (fp64 values) token by token: row t of every
+    head is multiplied by rope_matrix(cos_sin_cache[positions[t]])."""
+    x = np.asarray(x, dtype=np.float64)
+    T, H, D = x.shape
+    out = np.empty_like(x)
+    cache = np.asarray(cos_sin_cache, dtype=np.float64)
+    for t in range(T):
+        R = rope_matrix(cache[int(positions[t])], D, rotary_dim, neox)
+        out[t] = x[t] @ R.T
+    return out
+
+
+def rope_write_kv(query: np.ndarray, key: np.ndarray, value: np.ndarray,
+                  key_cache: np.ndarray, value_cache: np.ndarray, slots: np.ndarray,
+                  positions: np.ndarray, cos_sin_cache: np.ndarray, rotary_dim: int,
+                  neox: bool, block_size: int) -> np.ndarray:
+    """The fused step in the pages' order: rotate Q and K, then write the
+    rotated K and the unchanged V to the paged cache by slot.
+
+    query / key / value are fp64 values; the caches must be float64 arrays
+    (the rotated values are not representable in the storage dtype, so the
+    comparison with a device cache is done to a tolerance).  Returns the
+    rotated query."""
+    q_rot = rope(query, positions, cos_sin_cache, rotary_dim, neox)
+    k_rot = rope(key, positions, cos_sin_cache, rotary_dim, neox)
+    write_kv(key_cache, value_cache, k_rot, np.asarray(value, dtype=np.float64), slots,
+             block_size)
+    return q_rot
 
 
 def _self_check() -> None:  # pragma: no cover - manual sanity hook

@@ -463,3 +463,119 @@ def test_bf16_widening_exact():
     bits = (vals.view(np.uint32) >> 16).astype(np.uint16)
     assert np.array_equal(oracle.bf16_bits_to_f64(bits), vals.astype(np.float64))
     assert np.isnan(oracle.bf16_bits_to_f64(np.array([0x7FC0], np.uint16)))[0]
+
+
+# ----------------------------------------------------------------------------
+# rotary position embedding
+# ----------------------------------------------------------------------------
+def _angle_cache(max_pos, rotary_dim, base=10000.0):
+    """cos/sin rows built from angles p * base^(-2i/rotary_dim) (the usual
+    frequency ladder); cos in the first half of a row, sin in the second."""
+    inv = base ** (-np.arange(0, rotary_dim, 2, dtype=np.float64) / rotary_dim)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * inv[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1)
+
+
+def _rope_complex(x, pos, cache, rotary_dim, neox):
+    """Independent formulation: each rotated pair (a, b) is the complex number
+    x_a + i x_b multiplied by e^{i theta} = cos + i sin, with Python complex
+    arithmetic on scalars."""
+    D = len(x)
+    half = rotary_dim // 2
+    out = [float(v) for v in x]
+    for i in range(half):
+        a, b = (i, i + half) if neox else (2 * i, 2 * i + 1)
+        z = complex(float(x[a]), float(x[b])) * complex(float(cache[pos][i]), float(cache[pos][half + i]))
+        out[a], out[b] = z.real, z.imag
+    assert len(out) == D
+    return out
+
+
+def test_rope_quarter_turn_by_hand():
+    # cos 0 / sin 1 on the first angle: the pair's first axis turns into the
+    # second (counter-clockwise, the standard rotation sign)
+    row = np.array([0.0, 1.0, 1.0, 0.0])            # rotary_dim 4: cos(th0, th1), sin(th0, th1)
+    x = np.zeros((1, 1, 4))
+    x[0, 0, 0] = 1.0
+    got_gptj = oracle.rope(x, [0], row[None, :], 4, neox=False)[0, 0]
+    got_neox = oracle.rope(x, [0], row[None, :], 4, neox=True)[0, 0]
+    assert np.allclose(got_gptj, [0, 1, 0, 0])      # pair (0, 1)
+    assert np.allclose(got_neox, [0, 0, 1, 0])      # pair (0, 2)
+    # second angle is 0: its pair is untouched
+    x2 = np.array([[[0.0, 3.0, 0.0, 5.0]]])
+    assert np.allclose(oracle.rope(x2, [0], row[None, :], 4, neox=True)[0, 0], [0, 3, 0, 5])
+
+
+@pytest.mark.parametrize("neox", [False, True])
+@pytest.mark.parametrize("D,rd", [(8, 8), (16, 8), (64, 64), (128, 128)])
+def test_rope_brute_force_complex(neox, D, rd):
+    rng = np.random.default_rng(D + rd + neox)
+    cache = _angle_cache(50, rd)
+    x = rng.standard_normal((5, 2, D))
+    pos = rng.integers(0, 50, 5)
+    got = oracle.rope(x, pos, cache, rd, neox)
+    for t in range(5):
+        for h in range(2):
+            want = _rope_complex(x[t, h], int(pos[t]), cache, rd, neox)
+            assert np.max(np.abs(got[t, h] - np.array(want))) < 1e-12
+    # dimensions at or past rotary_dim pass through unchanged
+    assert np.array_equal(got[:, :, rd:], x[:, :, rd:])
+
+
+@pytest.mark.parametrize("neox", [False, True])
+def test_rope_rotation_invariants(neox):
+    rng = np.random.default_rng(7)
+    D = 64
+    cache = _angle_cache(4096, D, base=500000.0)
+    q = rng.standard_normal((1, 1, D))
+    k = rng.standard_normal((1, 1, D))
+    # position 0 is the identity
+    assert np.allclose(oracle.rope(q, [0], cache, D, neox), q, atol=0, rtol=0)
+    # orthogonal: norms are kept
+    for p in (1, 17, 4095):
+        R = oracle.rope_matrix(cache[p], D, D, neox)
+        assert np.allclose(R @ R.T, np.eye(D), atol=1e-13)
+        assert abs(np.linalg.norm(oracle.rope(q, [p], cache, D, neox)) - np.linalg.norm(q)) < 1e-12
+    # the score of rotated q (pos m) and k (pos n) depends only on m - n
+    def score(m, n):
+        return float(np.sum(oracle.rope(q, [m], cache, D, neox) * oracle.rope(k, [n], cache, D, neox)))
+    for m, n, s in ((100, 40, 7), (5, 5, 300), (900, 12, 1000)):
+        assert abs(score(m, n) - score(m + s, n + s)) < 1e-9
+    # rotations compose: R(m) R(n) = R(m + n) for a cache built from angles
+    Rm, Rn, Rmn = (oracle.rope_matrix(cache[p], D, D, neox) for p in (123, 456, 579))
+    assert np.allclose(Rm @ Rn, Rmn, atol=1e-12)
+
+
+def test_rope_styles_related_by_permutation():
+    # the split-halves layout is the adjacent-pairs layout on permuted coordinates
+    rng = np.random.default_rng(3)
+    D = rd = 16
+    cache = _angle_cache(10, rd)
+    x = rng.standard_normal((3, 1, D))
+    perm = np.empty(D, dtype=int)             # adjacent slot 2i <- i, 2i+1 <- i + rd/2
+    perm[0::2] = np.arange(rd // 2)
+    perm[1::2] = np.arange(rd // 2) + rd // 2
+    pos = [0, 3, 9]
+    neox = oracle.rope(x, pos, cache, rd, neox=True)
+    gptj = oracle.rope(x[:, :, perm], pos, cache, rd, neox=False)
+    assert np.allclose(neox[:, :, perm], gptj, atol=1e-14)
+
+
+def test_rope_write_kv_order_and_skip():
+    # rotated K lands at its slot, V unrotated, negative slots write nothing,
+    # untouched slots keep their poison
+    rng = np.random.default_rng(11)
+    B, nb, H, D = 4, 3, 2, 8
+    cache = _angle_cache(20, D)
+    q = rng.standard_normal((3, 4, D))
+    k = rng.standard_normal((3, H, D))
+    v = rng.standard_normal((3, H, D))
+    kc = np.full((nb, B, H, D), np.nan)
+    vc = np.full((nb, B, H, D), np.nan)
+    slots = np.array([5, -1, 8])
+    pos = np.array([2, 3, 19])
+    q_rot = oracle.rope_write_kv(q, k, v, kc, vc, slots, pos, cache, D, True, B)
+    assert np.allclose(q_rot, oracle.rope(q, pos, cache, D, True))
+    assert np.allclose(kc[1, 1], oracle.rope(k[0:1], pos[0:1], cache, D, True)[0])
+    assert np.array_equal(vc[2, 0], v[2])
+    assert np.isnan(kc[0]).all() and np.isnan(kc[1, [0, 2, 3]]).all() and np.isnan(vc[2, 1:]).all()
