@@ -12,7 +12,9 @@ block 16, bf16), i.e. the configuration that exercises every part of the step.
 Prints ONE JSON line.  `value` is the decode KV-read bandwidth (algorithmic
 bytes of the decode rows / time of the split-K and merge kernels in the timed
 steps); chunk TFLOP/s, per-kernel times, the roofline of the dominant kernel
-and a CPU-oracle baseline ride along.
+and a CPU-oracle baseline ride along.  The fused rotary-embedding + cache-write
+kernel (the step that precedes the write when Q/K still need their position
+rotation) is timed on its own on the same tokens and reported beside it.
 """
 from __future__ import annotations
 
@@ -49,6 +51,8 @@ def parse():
     p.add_argument("--workload", default="c3", choices=["c2", "c3", "c4"])
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="budget of oracle work for the CPU baseline (0 disables it)")
+    p.add_argument("--no-rope", dest="rope", action="store_false",
+                   help="skip the separate timing of the fused rotary + cache-write kernel")
     p.add_argument("--copy-calibration", action="store_true",
                    help="instead of the step, run a plain 1 GiB device copy a few times "
                         "(reference for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -259,6 +263,45 @@ def main():
             acc[k] += e[a].elapsed_time(e[b])
     us = {k: 1e3 * v / args.steps for k, v in acc.items()}
 
+    # fused rotary embedding + cache write on the same step's tokens (timed on
+    # its own: Q rotated in place on a copy, K/V into the first pool copy)
+    rope = None
+    if args.rope:
+        rd = spec.D
+        cos_sin = torch.from_numpy(configs.rope_cache(int(spec.seq_lens.max()), rd)).to(dev)
+        positions = torch.from_numpy(spec.positions()).to(dev)
+        kc, vc = pools[0]
+        # the step's Q/K/V (about 25 MB) would stay in the 256 MB last-level
+        # cache across back-to-back calls: rotate over copies so consecutive
+        # calls read >= 256 MB apart
+        per_set = 3 * d["query"].numel() * d["query"].element_size()
+        n_sets = max(2, min(64, -(-(256 << 20) // per_set) + 1))
+        sets = [(d["query"].clone(), d["key"].clone(), d["value"].clone()) for _ in range(n_sets)]
+        call_no = [0]
+
+        def rope_call():
+            q_i, k_i, v_i = sets[call_no[0] % n_sets]
+            call_no[0] += 1
+            pa.rope_write_kv(q_i, k_i, v_i, kc, vc, slot_mapping, positions, cos_sin, rd, True)
+
+        for _ in range(args.warmup):
+            rope_call()
+        r0 = torch.cuda.Event(enable_timing=True)
+        r1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        r0.record(stream)
+        for _ in range(max(args.steps, 2 * n_sets)):
+            rope_call()
+        r1.record(stream)
+        torch.cuda.synchronize()
+        rope_us = 1e3 * r0.elapsed_time(r1) / max(args.steps, 2 * n_sets)
+        rope_bytes = spec.rope_write_bytes(rd)
+        rope_gbs = rope_bytes / (rope_us * 1e-6) / 1e9
+        rope = {"kernel": "fused rotary embedding + cache write", "bound": "hbm",
+                "tokens": spec.T, "rotary_dim": rd, "input_copies": n_sets, "us": round(rope_us, 2),
+                "bytes_per_launch": rope_bytes, "achieved": round(rope_gbs, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(rope_gbs / HBM_PEAK_GBS, 4)}
+
     dec_bytes = spec.decode_bytes()
     chunk_fl = spec.chunk_flops()
     dec_s = (us["rowwise"] + us["merge"]) * 1e-6
@@ -314,6 +357,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(chunk_tf / MFMA_BF16_PEAK_TFLOPS, 4),
         },
+        "rope_write_kv": rope,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -153,6 +153,46 @@ pa_status pa_write_kv(const void* key, const void* value, void* key_cache, void*
                       pa_dtype dtype, void* stream);
 
 /*
+ * pa_rope_write_kv -- rotary position embedding of Q and K fused with the
+ * cache write.
+ *
+ * [P1] "Attention Module (以标准GQA + RoPE为例)": Q and K of a token are
+ * multiplied by a block-diagonal rotation whose angles depend on the token's
+ * position; the rotation is applied elementwise from a table cos_sin_cache
+ * [max_position_embeddings, rotary_dim] prepared once, whose row p holds the
+ * cos of the rotary_dim / 2 angles of position p followed by their sin; then
+ * K and V are scattered into the paged cache by slot_mapping.  For angle
+ * column i and coordinate pair (a, b): x_a' = x_a cos_i - x_b sin_i,
+ * x_b' = x_b cos_i + x_a sin_i.  neox_style = 1 pairs (i, i + rotary_dim/2),
+ * neox_style = 0 pairs (2i, 2i + 1); coordinates at or past rotary_dim are
+ * not rotated.
+ *
+ *   query               device [T, num_heads, head_dim], rotated in place
+ *   key, value          device [T, num_kv_heads, head_dim] (read only; the
+ *                       rotated K is written to the cache, not back to key)
+ *   key_cache,
+ *   value_cache         device [num_blocks, block_size, num_kv_heads, head_dim];
+ *                       slot s gets the rotated K row and the V row of its
+ *                       token, exactly as pa_write_kv would write them
+ *   slot_mapping        device int64 [T]; a negative slot writes nothing to
+ *                       the caches (its query row is still rotated)
+ *   positions           device int64 [T] absolute position of each token
+ *                       (num_computed_tokens + i); values outside
+ *                       [0, max_position) are clamped into it
+ *   cos_sin_cache       device float32 [max_position, rotary_dim]
+ *   rotary_dim          positive multiple of 16, at most head_dim
+ * Arithmetic is fp32, rounded once to dtype.  Slots must be distinct and
+ * below num_blocks * block_size (past the pool: skipped).  T == 0 is a no-op.
+ * pa_attention of the layer must be enqueued after this call.
+ */
+pa_status pa_rope_write_kv(void* query, const void* key, const void* value, void* key_cache,
+                           void* value_cache, const int64_t* slot_mapping, const int64_t* positions,
+                           const float* cos_sin_cache, int32_t max_position, int32_t rotary_dim,
+                           int32_t neox_style, int64_t T, int32_t num_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                           pa_dtype dtype, void* stream);
+
+/*
  * pa_attention_workspace_size -- bytes of device workspace pa_attention needs
  * for this step (plan tables plus split-K partial results).  Takes the same
  * host mirrors pa_attention plans from; returns 0 and sets pa_last_error() if

@@ -28,7 +28,7 @@ STATUS = {
 EXPORTS = [
     "pa_abi_version", "pa_status_str", "pa_last_error", "pa_build_step_metadata",
     "pa_compute_slot_mapping", "pa_write_kv", "pa_attention_workspace_size", "pa_attention",
-    "pa_set_profiling_events", "pa_validate_metadata",
+    "pa_set_profiling_events", "pa_validate_metadata", "pa_rope_write_kv",
 ]
 
 
@@ -71,6 +71,11 @@ def lib():
     L.pa_write_kv.restype = ctypes.c_int
     L.pa_write_kv.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int64, ctypes.c_int32,
                               ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int, _vp]
+    L.pa_rope_write_kv.restype = ctypes.c_int
+    L.pa_rope_write_kv.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32,
+                                   ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                   ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_int, _vp]
     L.pa_attention_workspace_size.restype = ctypes.c_size_t
     L.pa_attention_workspace_size.argtypes = [_i32p, _i32p, ctypes.c_int32, ctypes.c_int32,
                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -205,6 +210,20 @@ def write_kv(key, value, key_cache, value_cache, slot_mapping, stream=None) -> N
     _check(lib().pa_write_kv(_ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
                              _ptr(slot_mapping), T, N, B, Hkv, D, _dtype_code(key),
                              ctypes.c_void_p(_stream(stream))), "pa_write_kv")
+
+
+def rope_write_kv(query, key, value, key_cache, value_cache, slot_mapping, positions,
+                  cos_sin_cache, rotary_dim: int, neox: bool = True, stream=None) -> None:
+    """query [T, Hq, D] (rotated in place); key/value [T, Hkv, D]; caches
+    [N, B, Hkv, D]; slot_mapping and positions int64 [T]; cos_sin_cache
+    float32 [max_position, rotary_dim] (device tensors)."""
+    T, Hq, _ = query.shape
+    N, B, Hkv, D = key_cache.shape
+    _check(lib().pa_rope_write_kv(_ptr(query), _ptr(key), _ptr(value), _ptr(key_cache),
+                                  _ptr(value_cache), _ptr(slot_mapping), _ptr(positions),
+                                  _ptr(cos_sin_cache), cos_sin_cache.shape[0], rotary_dim,
+                                  1 if neox else 0, T, Hq, Hkv, D, N, B, _dtype_code(query),
+                                  ctypes.c_void_p(_stream(stream))), "pa_rope_write_kv")
 
 
 def attention_workspace_size(h_query_start_loc, h_seq_lens, num_heads: int, num_kv_heads: int,

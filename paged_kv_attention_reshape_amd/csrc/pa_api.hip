@@ -3,6 +3,7 @@
 // Host side only: argument checks, the step-metadata builder, the launch
 // plan sizing and the kernel launch sequence
 //   pa_write_kv:  write_kv
+//   pa_rope_write_kv: rope_write_kv (rotary embedding of Q and K fused with the write)
 //   pa_attention: plan -> row-wise split-K -> chunk (matrix cores) -> merge
 // all on the caller's stream.
 #include <stdarg.h>
@@ -280,6 +281,51 @@ pa_status pa_write_kv(const void* key, const void* value, void* key_cache, void*
                                      (int64_t)num_blocks * block_size, row_bytes,
                                      reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "write_kv launch");
+  return PA_OK;
+}
+
+pa_status pa_rope_write_kv(void* query, const void* key, const void* value, void* key_cache,
+                           void* value_cache, const int64_t* slot_mapping, const int64_t* positions,
+                           const float* cos_sin_cache, int32_t max_position, int32_t rotary_dim,
+                           int32_t neox_style, int64_t T, int32_t num_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                           pa_dtype dtype, void* stream) {
+  g_err.clear();
+  pa_status st = check_geometry(num_heads, num_kv_heads, head_dim, block_size, num_blocks, dtype);
+  if (st != PA_OK) return st;
+  if (T < 0) return fail(PA_ERR_BAD_SHAPE, "T=%lld < 0", (long long)T);
+  if (T > INT32_MAX) return fail(PA_ERR_BAD_SHAPE, "T=%lld too large for one call", (long long)T);
+  if (rotary_dim <= 0 || rotary_dim > head_dim || rotary_dim % 16 != 0)
+    return fail(PA_ERR_UNSUPPORTED, "rotary_dim %d must be a positive multiple of 16 and <= head_dim %d",
+                rotary_dim, head_dim);
+  if (max_position <= 0) return fail(PA_ERR_BAD_SHAPE, "max_position=%d <= 0", max_position);
+  if (neox_style != 0 && neox_style != 1) return fail(PA_ERR_BAD_SHAPE, "neox_style must be 0 or 1");
+  if (T == 0) return PA_OK;
+  if (!query || !key || !value || !key_cache || !value_cache || !slot_mapping || !positions ||
+      !cos_sin_cache)
+    return fail(PA_ERR_NULL_PTR, "NULL pointer argument");
+  const uintptr_t mis = (uintptr_t)query | (uintptr_t)key | (uintptr_t)value |
+                        (uintptr_t)key_cache | (uintptr_t)value_cache;
+  if (mis & 15) return fail(PA_ERR_BAD_SHAPE, "tensors must be 16-byte aligned");
+  if ((uintptr_t)cos_sin_cache & 3) return fail(PA_ERR_BAD_SHAPE, "cos_sin_cache must be 4-byte aligned");
+  pa::RopeArgs a{};
+  a.query = query;
+  a.key = key;
+  a.value = value;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.slots = slot_mapping;
+  a.positions = positions;
+  a.cos_sin = cos_sin_cache;
+  a.T = T;
+  a.num_slots = (int64_t)num_blocks * block_size;
+  a.max_position = max_position;
+  a.rotary_dim = rotary_dim;
+  a.Hq = num_heads;
+  a.Hkv = num_kv_heads;
+  hipError_t e = pa::launch_rope_write_kv(a, dtype == PA_BF16, head_dim, neox_style != 0,
+                                          reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "rope_write_kv launch");
   return PA_OK;
 }
 

@@ -174,6 +174,24 @@ struct AttnArgs {
   float* o_part;      // [parts, Hq, D] unnormalised
 };
 
+// Fused rotary embedding + cache write (one workgroup per token).
+struct RopeArgs {
+  void* query;                 // [T, Hq, D], rotated in place
+  const void* key;             // [T, Hkv, D]
+  const void* value;           // [T, Hkv, D]
+  void* key_cache;             // [num_slots, Hkv, D]
+  void* value_cache;
+  const int64_t* slots;        // [T]
+  const int64_t* positions;    // [T]
+  const float* cos_sin;        // [max_position, rotary_dim]
+  int64_t T;
+  int64_t num_slots;
+  int64_t max_position;
+  int32_t rotary_dim;
+  int32_t Hq, Hkv;
+};
+hipError_t launch_rope_write_kv(const RopeArgs& a, bool bf16, int32_t D, bool neox, hipStream_t s);
+
 hipError_t launch_rowwise(const AttnArgs& a, hipStream_t s);
 hipError_t launch_chunk(const AttnArgs& a, hipStream_t s);
 hipError_t launch_merge(const AttnArgs& a, hipStream_t s);

@@ -202,6 +202,32 @@ def test_write_kv_host_checks():
     assert rc(T=0, k=0) == "PA_OK"
 
 
+def test_rope_write_kv_host_checks():
+    L = pa.lib()
+    def rc(**over):
+        a = dict(q=4096, k=4096, v=4096, kc=4096, vc=4096, sm=4096, pos=4096, cs=4096, mp=100,
+                 rd=64, nx=1, T=3, Hq=8, Hkv=2, D=64, N=4, B=16, dt=1)
+        a.update(over)
+        return pa.status_str(L.pa_rope_write_kv(a["q"], a["k"], a["v"], a["kc"], a["vc"], a["sm"],
+                                                a["pos"], a["cs"], a["mp"], a["rd"], a["nx"], a["T"],
+                                                a["Hq"], a["Hkv"], a["D"], a["N"], a["B"], a["dt"],
+                                                None))
+    assert rc(D=32) == "PA_ERR_UNSUPPORTED"
+    assert rc(rd=0) == "PA_ERR_UNSUPPORTED"
+    assert rc(rd=24) == "PA_ERR_UNSUPPORTED"          # not a multiple of 16
+    assert rc(rd=128) == "PA_ERR_UNSUPPORTED"         # past head_dim
+    assert rc(mp=0) == "PA_ERR_BAD_SHAPE"
+    assert rc(nx=2) == "PA_ERR_BAD_SHAPE"
+    assert rc(Hq=6) == "PA_ERR_UNSUPPORTED"           # GQA group 3
+    assert rc(dt=3) == "PA_ERR_BAD_DTYPE"
+    assert rc(pos=0) == "PA_ERR_NULL_PTR"
+    assert rc(cs=0) == "PA_ERR_NULL_PTR"
+    assert rc(q=4100) == "PA_ERR_BAD_SHAPE"
+    assert rc(cs=4098) == "PA_ERR_BAD_SHAPE"
+    assert rc(T=-1) == "PA_ERR_BAD_SHAPE"
+    assert rc(T=0, q=0, pos=0) == "PA_OK"
+
+
 def test_generator_host_mirror_properties():
     # deterministic, distinct streams, ~N(0,1), bf16 rounding to nearest even
     a = rng.row_values(rng.base_row_keys(rng.key(1, 2), np.arange(64)), 256, "f32")

@@ -172,8 +172,38 @@ class StepSpec:
                 tot += 4 * self.D * self.Hq * pairs
         return tot
 
+    def positions(self) -> np.ndarray:
+        """Absolute position of every scheduled token, flattened order
+        (num_computed[r] + i): the rows the rotary table is indexed by."""
+        return np.concatenate([np.arange(c, c + q, dtype=np.int64)
+                               for q, c in zip(self.query_lens, self.num_computed)]
+                              + [np.zeros(0, np.int64)])
+
+    def rope_write_bytes(self, rotary_dim: int) -> int:
+        """Bytes the fused rotary + cache write must move: Q read and written
+        back, K and V read and written to the cache, one cos/sin row (fp32)
+        and a slot and a position per token."""
+        e = self.esize
+        return (2 * self.T * self.D * e * (self.Hq + 2 * self.Hkv)
+                + self.T * rotary_dim * 4 + 16 * self.T)
+
     def write_bytes(self) -> int:
         return 4 * self.T * self.Hkv * self.D * self.esize + 8 * self.T
+
+
+# ----------------------------------------------------------------------------
+# rotary table (model configuration, prepared once like the weights)
+# ----------------------------------------------------------------------------
+LLAMA3_ROPE_BASE = 500000.0
+
+
+def rope_cache(max_position: int, rotary_dim: int, base: float = LLAMA3_ROPE_BASE) -> np.ndarray:
+    """float32 [max_position, rotary_dim]: row p holds cos(p * f_i) for the
+    rotary_dim/2 frequencies f_i = base^(-2i/rotary_dim), then sin(p * f_i).
+    Computed in float64 and rounded once to float32."""
+    inv = base ** (-np.arange(0, rotary_dim, 2, dtype=np.float64) / rotary_dim)
+    ang = np.arange(max_position, dtype=np.float64)[:, None] * inv[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
 
 
 # ----------------------------------------------------------------------------
