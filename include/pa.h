@@ -63,7 +63,8 @@ typedef enum pa_status {
   PA_ERR_DUPLICATE_SLOT = 6,
   PA_ERR_INCONSISTENT_METADATA = 7,
   PA_ERR_WORKSPACE_TOO_SMALL = 8,
-  PA_ERR_HIP = 9
+  PA_ERR_HIP = 9,
+  PA_ERR_BAD_STATE = 10   /* a stateful object (scheduler) called out of order */
 } pa_status;
 
 typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;

@@ -1,7 +1,8 @@
 """Paged-KV attention step for AMD Instinct MI355X (gfx950).
 
-The work happens in libpa.so (HIP kernels behind the C ABI of include/pa.h);
-this package only marshals arguments.  Importing it does not load the
+The work happens in libpa.so (HIP kernels behind the C ABI of include/pa.h)
+and libpa_sched.so (the host scheduler and block allocator of
+include/pa_sched.h); this package only marshals arguments.  Importing it does not load the
 library; the first call does, and raises if it has not been built.
 """
 from ._lib import (  # noqa: F401
@@ -9,3 +10,4 @@ from ._lib import (  # noqa: F401
     attention_workspace_size, build_step_metadata, compute_slot_mapping, set_profiling_events, last_error, lib, status_str,
     validate_metadata, write_kv, rope_write_kv,
 )
+from ._sched import SCHED_EXPORTS, SCHED_LIB_PATH, Scheduler, sched_lib  # noqa: F401,E402

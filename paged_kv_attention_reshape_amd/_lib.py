@@ -23,6 +23,7 @@ STATUS = {
     0: "PA_OK", 1: "PA_ERR_NULL_PTR", 2: "PA_ERR_BAD_SHAPE", 3: "PA_ERR_BAD_DTYPE",
     4: "PA_ERR_UNSUPPORTED", 5: "PA_ERR_OUT_OF_RANGE", 6: "PA_ERR_DUPLICATE_SLOT",
     7: "PA_ERR_INCONSISTENT_METADATA", 8: "PA_ERR_WORKSPACE_TOO_SMALL", 9: "PA_ERR_HIP",
+    10: "PA_ERR_BAD_STATE",
 }
 
 EXPORTS = [

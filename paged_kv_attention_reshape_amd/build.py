@@ -1,6 +1,8 @@
 """Build the HIP libraries in-tree for gfx950.
 
   libpa.so            paged_kv_attention_reshape_amd/  (the attention library)
+  libpa_sched.so      paged_kv_attention_reshape_amd/  (host scheduler / block
+                                                        allocator, plain C++)
   libpa_workloads.so  workloads/                        (device input generator,
                                                         test/benchmark only)
 
@@ -70,13 +72,31 @@ def _build_lib(name: str, srcs, includes, out: str, verbose: bool) -> str:
     return out
 
 
+CXX = os.environ.get("CXX", "g++")
+
+
+def _build_host_lib(srcs, includes, out: str, verbose: bool) -> str:
+    tmp = out + ".tmp"
+    cmd = [CXX, "-O2", "-std=c++17", "-fPIC", "-shared", "-Wall", *[f"-I{i}" for i in includes],
+           *srcs, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"host build failed for {out}:\n{r.stdout}{r.stderr}")
+    os.replace(tmp, out)
+    return out
+
+
 def build(verbose: bool = False):
     inc = [os.path.join(ROOT, "include"), os.path.join(PKG, "csrc")]
+    sched = _build_host_lib([os.path.join(PKG, "csrc", "sched.cpp")], [os.path.join(ROOT, "include")],
+                            os.path.join(PKG, "libpa_sched.so"), verbose)
     srcs = sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
     lib = _build_lib("pa", srcs, inc, os.path.join(PKG, "libpa.so"), verbose)
     wsrcs = sorted(glob.glob(os.path.join(ROOT, "workloads", "csrc", "*.hip")))
     wlib = _build_lib("workloads", wsrcs, [], os.path.join(ROOT, "workloads", "libpa_workloads.so"), verbose)
-    return lib, wlib
+    return lib, wlib, sched
 
 
 if __name__ == "__main__":

@@ -184,6 +184,7 @@ const char* pa_status_str(int status) {
     case PA_ERR_INCONSISTENT_METADATA: return "PA_ERR_INCONSISTENT_METADATA";
     case PA_ERR_WORKSPACE_TOO_SMALL: return "PA_ERR_WORKSPACE_TOO_SMALL";
     case PA_ERR_HIP: return "PA_ERR_HIP";
+    case PA_ERR_BAD_STATE: return "PA_ERR_BAD_STATE";
     default: return "PA_UNKNOWN";
   }
 }

@@ -1,6 +1,7 @@
 """Serving-trace parity: 200 consecutive steps of write_kv + attention over a
-32-layer cache, with the shapes a continuous-batching scheduler with recompute
-preemption produces (workloads.serving_trace), checked three ways:
+32-layer cache, with the steps the product scheduler / block allocator
+(libpa_sched.so, recompute preemption) plans for the seeded request trace of
+workloads.serving_trace, checked four ways:
 
 * sampled (step, layer, request) triples against the fp64 oracle, which
   regenerates the request's whole history from the counter-based generator
@@ -8,8 +9,8 @@ preemption produces (workloads.serving_trace), checked three ways:
 * outputs of a preempted request after its re-prefill against the outputs the
   same (layer, position) had before the preemption (both GPU; the K/V are
   identical by construction, so only rounding may differ);
-* scheduler invariants (conservation, budgets) are asserted by the
-  simulator itself and covered on the CPU by test_sched_sim.py.
+* every plan equals the reference scheduler's plan (also covered on the CPU by
+  test_sched_parity.py, with the pool and scheduling invariants).
 """
 import numpy as np
 import pytest
@@ -17,7 +18,9 @@ import pytest
 import oracle
 from helpers import assert_close, bits, say, storage_np
 from workloads import rng
-from workloads.serving_trace import TraceConfig, simulate, step_arrays, token_row_keys
+from oracle.sched_oracle import Scheduler as RefScheduler
+from workloads import serving_trace as st
+from workloads.serving_trace import TraceConfig, step_arrays, token_row_keys
 
 pytestmark = pytest.mark.gpu
 
@@ -39,20 +42,23 @@ def _fill_rows(t, keys):
 
 def test_serving_trace_200_steps_32_layers():
     cfg = TraceConfig()
-    plans, reqs = simulate(cfg)
+    plans = st.drive(pa.Scheduler(**st.scheduler_args(cfg)), cfg)
+    ref = st.drive(RefScheduler(**st.scheduler_args(cfg)), cfg)
+    assert [(p['sched'], p['blocks'], p['preempted']) for p in plans] == \
+        [(p['sched'], p['blocks'], p['preempted']) for p in ref]
     B = cfg.block_size
     scale = 1.0 / np.sqrt(D)
-    n_pre = sum(len(p.preempted) for p in plans)
+    n_pre = sum(len(p['preempted']) for p in plans)
     say(f"trace: {len(plans)} steps, {n_pre} recompute preemptions, "
-        f"{sum(sum(n for _, _, n in p.sched) for p in plans)} scheduled tokens")
+        f"{sum(sum(n for _, _, n in p['sched']) for p in plans)} scheduled tokens")
     assert n_pre >= 1
 
     # which (rid, pos) to remember for the re-prefill comparison: positions a
     # request computed before its first preemption (every 37th + the last)
     first_pre = {}
     for p in plans:
-        for rid, held, _ in p.preempted:
-            first_pre.setdefault(rid, (p.index, held))
+        for rid, held, _ in p['preempted']:
+            first_pre.setdefault(rid, (p['index'], held))
     watch = {}
     for rid, (k, held) in first_pre.items():
         if held > 0:
@@ -73,7 +79,7 @@ def test_serving_trace_200_steps_32_layers():
     worst = 0.0
     n_checked = 0
     for p in plans:
-        if not p.sched:
+        if not p['sched']:
             continue
         ql, cp, bt, rids, pos = step_arrays(p, B)
         T = int(ql.sum())
@@ -96,7 +102,7 @@ def test_serving_trace_200_steps_32_layers():
                          workspace=ws)
             if layer in KEEP_LAYERS:
                 idx, keys = [], []
-                for i, (rid, c, n) in enumerate(p.sched):
+                for i, (rid, c, n) in enumerate(p['sched']):
                     if rid not in watch:
                         continue
                     for j in range(n):
@@ -115,12 +121,12 @@ def test_serving_trace_200_steps_32_layers():
                             compared += 1
                         else:
                             before[key] = row.copy()
-            if p.index in sample_steps and layer in KEEP_LAYERS:
+            if p['index'] in sample_steps and layer in KEEP_LAYERS:
                 torch.cuda.synchronize()
-                cand = [i for i, (_, _, n) in enumerate(p.sched) if n == 1][:2] + \
-                       [i for i, (_, _, n) in enumerate(p.sched) if n > 1][:1]
+                cand = [i for i, (_, _, n) in enumerate(p['sched']) if n == 1][:2] + \
+                       [i for i, (_, _, n) in enumerate(p['sched']) if n > 1][:1]
                 for i in cand:
-                    rid, c, n = p.sched[i]
+                    rid, c, n = p['sched'][i]
                     L = c + n
                     allpos = np.arange(L)
                     kh = rng.row_values(token_row_keys(cfg.seed, rng.TAG_K, layer, np.full(L, rid), allpos),
@@ -132,19 +138,19 @@ def test_serving_trace_200_steps_32_layers():
                                                        c + rows), HQ * D, "bf16").reshape(len(rows), HQ, D)
                     want, _ = oracle.attention_rows(qh, kh, vh, c + rows, scale, "bf16")
                     got = oracle.as_f64(storage_np(out[int(qsl[i]) + torch.from_numpy(rows).cuda()]), "bf16")
-                    worst = max(worst, assert_close(got, want, "bf16", f"step {p.index} layer {layer} req {rid}"))
+                    worst = max(worst, assert_close(got, want, "bf16", f"step {p['index']} layer {layer} req {rid}"))
                     # the request's cache rows 0..L-1, gathered through its blocks, bit-exact
-                    blk = torch.from_numpy(np.asarray(p.blocks[rid], np.int64)).cuda()
+                    blk = torch.from_numpy(np.asarray(p['blocks'][rid], np.int64)).cuda()
                     gk = oracle.gather_kv(storage_np(kc[layer].index_select(0, blk)),
-                                          np.arange(len(p.blocks[rid])), L, B)
+                                          np.arange(len(p['blocks'][rid])), L, B)
                     gv = oracle.gather_kv(storage_np(vc[layer].index_select(0, blk)),
-                                          np.arange(len(p.blocks[rid])), L, B)
+                                          np.arange(len(p['blocks'][rid])), L, B)
                     assert np.array_equal(bits(gk), bits(kh)), f"key cache of request {rid} differs"
                     assert np.array_equal(bits(gv), bits(vh)), f"value cache of request {rid} differs"
                     n_checked += 1
-        if p.index % 40 == 0:
+        if p['index'] % 40 == 0:
             torch.cuda.synchronize()
-            say(f"step {p.index}: R={len(p.sched)} T={T} preempted={len(p.preempted)}")
+            say(f"step {p['index']}: R={len(p['sched'])} T={T} preempted={len(p['preempted'])}")
     torch.cuda.synchronize()
     say(f"oracle-checked {n_checked} (step, layer, request) samples, max err {worst:.2e}; "
         f"{compared} re-prefilled rows matched their pre-preemption outputs")
