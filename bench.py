@@ -143,8 +143,67 @@ def cpu_baseline(spec, d, budget_s):
         "sample": f"{n} of {len(dec)} decode requests ({dec_s:.1f} s) and all {len(chunks)} prefill chunks "
                   f"({ck_s:.1f} s) of the same step; fp64 numpy oracle: slot mapping, write, gather, attention",
         "chunk_gflops": round(ck_flops / ck_s / 1e9, 3) if ck_s > 0 else None,
+        "scheduler_us_per_step": scheduler_timing(product=False)["us_per_step"],
         "host_cpus": len(os.sched_getaffinity(0)),
     }
+
+
+def scheduler_timing(product: bool, steps: int = 200):
+    """Host time per planned step of the serving trace (2048 requests, 16384
+    blocks of 16, budget 8192, chunk 512): schedule + copy of the step's
+    arrays + commit.  product=False times the reference scheduler (only the
+    CPU-baseline leg does that)."""
+    from workloads import serving_trace as st
+    cfg = st.TraceConfig(steps=steps)
+    toks = 0
+    if product:
+        # the C ABI directly, with preallocated output arrays (what a serving
+        # loop would do): plan, copy the step's metadata, commit
+        import ctypes
+        import numpy as np
+        import paged_kv_attention_reshape_amd as pa
+        from paged_kv_attention_reshape_amd import _sched
+        s = pa.Scheduler(**st.scheduler_args(cfg))
+        for rid, p, o in st.requests(cfg):
+            s.add_request(rid, p, o)
+        L = pa.sched_lib()
+        cap, M = cfg.max_num_seqs, -(-(cfg.prompt_max + 4096) // cfg.block_size)
+        ids = np.zeros(cap, np.int64)
+        comp = np.zeros(cap, np.int32)
+        ql = np.zeros(cap, np.int32)
+        bt = np.zeros((cap, M), np.int32)
+        pre = np.zeros((cap, 3), np.int64)
+        fin = np.zeros(cap, np.int64)
+        info = _sched._PlanInfo()
+        nfin = ctypes.c_int32()
+        P = ctypes.POINTER
+        a_ids, a_comp, a_ql = (x.ctypes.data_as(P(t)) for x, t in
+                               ((ids, ctypes.c_int64), (comp, ctypes.c_int32), (ql, ctypes.c_int32)))
+        a_bt = bt.ctypes.data_as(P(ctypes.c_int32))
+        a_pre = pre.ctypes.data_as(P(ctypes.c_int64))
+        a_fin = fin.ctypes.data_as(P(ctypes.c_int64))
+        t0 = time.perf_counter()
+        for _ in range(cfg.steps):
+            assert L.pa_sched_schedule(s._h, ctypes.byref(info)) == 0
+            assert L.pa_sched_plan_copy(s._h, a_ids, a_comp, a_ql, cap, a_bt, info.max_blocks,
+                                        a_pre, cap) == 0
+            toks += info.num_tokens
+            assert L.pa_sched_commit(s._h, a_fin, cap, ctypes.byref(nfin)) == 0
+        dt = time.perf_counter() - t0
+    else:
+        from oracle.sched_oracle import Scheduler as RefScheduler
+        s = RefScheduler(**st.scheduler_args(cfg))
+        for rid, p, o in st.requests(cfg):
+            s.add_request(rid, p, o)
+        t0 = time.perf_counter()
+        for _ in range(cfg.steps):
+            plan = s.schedule()
+            toks += sum(n for _, _, n in plan["sched"])
+            s.commit()
+        dt = time.perf_counter() - t0
+    m = s.metrics()
+    return {"us_per_step": round(dt / cfg.steps * 1e6, 1), "steps": cfg.steps,
+            "scheduled_tokens": toks, "preemptions": m["preemptions"]}
 
 
 def load_traffic(kernel: str):
@@ -302,6 +361,11 @@ def main():
                 "bytes_per_launch": rope_bytes, "achieved": round(rope_gbs, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(rope_gbs / HBM_PEAK_GBS, 4)}
 
+    # host scheduler / block allocator (C++) on the serving trace
+    sched_t = scheduler_timing(product=True)
+    sched_t["trace"] = "2048 requests at step 0, 200 steps, 16384 blocks of 16, budget 8192, chunk 512"
+    sched_t["includes"] = "pa_sched_schedule + pa_sched_plan_copy (block table rows at the step's own width) + pa_sched_commit, through ctypes"
+
     dec_bytes = spec.decode_bytes()
     chunk_fl = spec.chunk_flops()
     dec_s = (us["rowwise"] + us["merge"]) * 1e-6
@@ -358,6 +422,7 @@ def main():
             "frac": round(chunk_tf / MFMA_BF16_PEAK_TFLOPS, 4),
         },
         "rope_write_kv": rope,
+        "scheduler": sched_t,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
