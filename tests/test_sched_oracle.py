@@ -66,7 +66,7 @@ def test_cancel_between_reserve_and_commit_returns_every_block():
     s.schedule(); s.commit()             # 40-token chunks: every request grows next step
     committed1 = len(s.reqs[1].blocks)
     p = s.schedule()                     # reserves the blocks of the next chunks
-    reserved1 = s.reqs[1].reserved
+    reserved1 = s.reqs[1].pend_new
     assert reserved1 > 0 and any(rid == 1 for rid, _, _ in p["sched"])
     free_mid = s.metrics()["q_free"]
     s.cancel(1)                          # cancelled between reserve and commit
@@ -172,3 +172,114 @@ def test_random_trace_invariants(B):
     m = plans[-1]["metrics"]
     assert m["rollbacks"] == len(fail)
     assert m["preemptions"] > 0 and m["allocation_failures"] >= m["preemptions"]
+
+
+# ----------------------------------------------------------------------------
+# shared blocks: prefix index, reference counts, eviction, copy-on-write
+# ----------------------------------------------------------------------------
+def _keys(ns, n):
+    """Keys of n full prompt blocks of a prompt in namespace ns."""
+    return [hash((ns, j)) & 0x7FFFFFFFFFFF for j in range(n)]
+
+
+def test_shared_prefix_reclaimed_only_after_the_last_reference():
+    # "同时验证分配器与调度器": requests sharing a prefix finish in different
+    # orders; shared blocks come back only when the last reference goes
+    B = 4
+    s = _sched(40, B, seqs=8, budget=64, chunk=64)
+    pre = _keys("sys", 3)                          # 3 full blocks = 12 shared tokens
+    s.add_request(0, 14, 1, keys=pre)              # A computes the prefix first
+    s.schedule(); s.commit()
+    assert s.metrics()["cached_blocks"] == 3 and s.reqs[0].status == "FINISHED"
+    shared = [s.index[k] for k in pre]
+    assert all(b in s.evictable for b in shared)   # cached, unreferenced, still committed
+    m = s.metrics()
+    assert m["q_live"] == m["q_committed"] - 3 == 0
+    s.add_request(1, 13, 3, keys=pre)              # B: 12 cached + 1 own token
+    s.add_request(2, 18, 1, keys=pre + _keys("x", 1))   # C: 12 cached + 6 own tokens
+    p = s.schedule()
+    assert p["sched"] == [(1, 12, 1), (2, 12, 6)]
+    assert p["blocks"][1][:3] == shared == p["blocks"][2][:3]
+    assert all(s.ref[b] == 2 for b in shared)
+    m = s.metrics()
+    assert m["prefix_hit_tokens"] == 24 and m["q_live"] == 3 + 1 + 2
+    s.commit()                                      # C finishes first
+    assert all(s.ref[b] == 1 for b in shared) and all(b not in s.evictable for b in shared)
+    s.schedule(); s.commit()                        # B decodes once more
+    s.schedule(); s.commit()                        # B finishes
+    assert s.reqs[1].status == "FINISHED"
+    assert all(s.ref[b] == 0 and b in s.evictable for b in shared)
+    m = s.metrics()
+    assert m["q_free"] + m["q_reserved"] + m["q_committed"] == 40 and m["q_live"] == 0
+
+
+def test_prefix_match_leaves_one_token_and_namespaces_do_not_mix():
+    B = 4
+    s = _sched(40, B, budget=64, chunk=64)
+    s.add_request(0, 8, 1, keys=_keys("m1", 2))
+    s.schedule(); s.commit()
+    s.add_request(1, 8, 1, keys=_keys("m1", 2))    # whole prompt cached: recompute the last token
+    s.add_request(2, 8, 1, keys=_keys("m2", 2))    # another model version: no hit
+    p = s.schedule()
+    assert p["sched"] == [(1, 4, 4), (2, 0, 8)]
+    assert s.metrics()["prefix_hit_tokens"] == 4
+    s.commit()
+
+
+def test_eviction_before_preemption_in_lru_order():
+    B = 4
+    s = _sched(6, B, seqs=4, budget=64, chunk=64)
+    s.add_request(0, 8, 1, keys=_keys("a", 2))     # 2 blocks, cached after it finishes
+    s.add_request(1, 4, 1, keys=_keys("b", 1))     # 1 block, cached after it finishes
+    s.schedule(); s.commit()
+    assert s.metrics()["evictable"] == 3 and s.metrics()["q_free"] == 3
+    order = list(s.evictable)
+    s.add_request(2, 20, 1)                        # needs 5 blocks: 3 free + 2 evicted
+    p = s.schedule()
+    assert p["preempted"] == [] and p["sched"] == [(2, 0, 20)]
+    m = s.metrics()
+    assert m["evictions"] == 2 and m["evictable"] == 1
+    assert list(s.evictable) == order[2:]           # the least recently released went first
+    s.commit()
+
+
+def test_fork_copy_on_write_and_rollback():
+    B = 4
+    s = _sched(20, B, seqs=4, budget=64, chunk=64)
+    s.add_request(0, 6, 5)                          # 6 tokens: block 1 half full
+    s.schedule(); s.commit()                        # computes 6, samples the 7th
+    s.fork(0, 1, 5)                                 # child shares both blocks
+    b0, b1 = s.reqs[0].blocks
+    assert s.ref[b0] == 2 and s.ref[b1] == 2
+    p = s.schedule()                                # both write position 6 into the shared block 1
+    # the parent copies first; the child is then the only owner of the old block
+    assert len(p["copies"]) == 1 and p["copies"][0][0] == b1
+    new = p["copies"][0][1]
+    assert p["blocks"][0] == [b0, new] and p["blocks"][1] == [b0, b1]
+    assert s.ref[b1] == 1 and s.ref[new] == 1 and s.ref[b0] == 2
+    m = s.metrics()
+    assert m["cow_copies"] == 1 and m["q_reserved"] == 1
+    s.rollback()                                    # the failed step undoes the copy
+    assert s.reqs[0].blocks == [b0, b1] and s.ref[b1] == 2
+    assert s.metrics()["q_reserved"] == 0 and s.metrics()["q_free"] == 18
+    p = s.schedule(); s.commit()
+    assert len(p["copies"]) == 1
+    m = s.metrics()
+    assert m["q_live"] == 3 and m["q_free"] + m["q_committed"] == 20
+
+
+def test_cancel_with_shared_blocks_drops_only_its_references():
+    B = 4
+    s = _sched(20, B, seqs=4, budget=64, chunk=64)
+    s.add_request(0, 6, 9)
+    s.schedule(); s.commit()
+    s.fork(0, 1, 9)
+    p = s.schedule()                                # parent copies the shared partial block
+    s.cancel(0)                                     # between reserve and commit
+    assert p["copies"] and s.pending[4] == []       # its copy has no reader any more
+    b0 = s.reqs[1].blocks[0]
+    assert s.ref[b0] == 1
+    s.commit()
+    m = s.metrics()
+    assert m["q_free"] + m["q_reserved"] + m["q_committed"] == 20
+    assert m["q_live"] == len(s.reqs[1].blocks) == 2
