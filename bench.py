@@ -173,6 +173,7 @@ def scheduler_timing(product: bool, steps: int = 200):
         ql = np.zeros(cap, np.int32)
         bt = np.zeros((cap, M), np.int32)
         pre = np.zeros((cap, 3), np.int64)
+        cps = np.zeros((cap, 2), np.int32)
         fin = np.zeros(cap, np.int64)
         info = _sched._PlanInfo()
         nfin = ctypes.c_int32()
@@ -181,12 +182,13 @@ def scheduler_timing(product: bool, steps: int = 200):
                                ((ids, ctypes.c_int64), (comp, ctypes.c_int32), (ql, ctypes.c_int32)))
         a_bt = bt.ctypes.data_as(P(ctypes.c_int32))
         a_pre = pre.ctypes.data_as(P(ctypes.c_int64))
+        a_cps = cps.ctypes.data_as(P(ctypes.c_int32))
         a_fin = fin.ctypes.data_as(P(ctypes.c_int64))
         t0 = time.perf_counter()
         for _ in range(cfg.steps):
             assert L.pa_sched_schedule(s._h, ctypes.byref(info)) == 0
             assert L.pa_sched_plan_copy(s._h, a_ids, a_comp, a_ql, cap, a_bt, info.max_blocks,
-                                        a_pre, cap) == 0
+                                        a_pre, cap, a_cps, cap) == 0
             toks += info.num_tokens
             assert L.pa_sched_commit(s._h, a_fin, cap, ctypes.byref(nfin)) == 0
         dt = time.perf_counter() - t0

@@ -39,6 +39,22 @@
  * input: the initial free-list order and the uniform draws the
  * artificial-preemption hook consumes (one per free-block check while armed).
  *
+ * Shared blocks ([P5] "共享前缀会改变块的所有权", figure 32.2): every block has a
+ * reference count; a request that stops using a block (finish, preemption,
+ * cancel, rollback) decrements it and only a block at 0 leaves: to the back
+ * of the free list, or -- if the prefix index holds it -- into the evictable
+ * set (cached state, still committed) in release order.  A request admitted
+ * with nothing computed attaches the longest run of its leading block keys
+ * found in the index (at most floor((tokens - 1) / block_size) blocks, so a
+ * token is always computed and no write lands in a shared full block) and
+ * starts after it; after each committed step a request offers its full
+ * prompt blocks to the index.  When free blocks run short the least recently
+ * released cached blocks are evicted before anything is preempted.  A request
+ * about to write into a partly filled block others also reference takes a
+ * fresh block instead, drops its reference to the old one, and the plan
+ * lists the copy (old -> new) that must run, on every layer's K and V cache,
+ * before the step's cache write (copy-on-write); rollback undoes it.
+ *
  * Conventions: every pointer is host memory; the library copies what it
  * keeps.  A pa_sched object is not thread-safe.  Failing calls return a
  * status and leave the object unchanged; the detail is in
@@ -75,6 +91,7 @@ typedef struct pa_sched_config {
 typedef struct pa_sched_plan_info {
   int32_t num_reqs;        /* requests scheduled in the pending plan */
   int32_t num_preempted;   /* preemptions done while planning it */
+  int32_t num_copies;      /* copy-on-write block copies the step must run first */
   int64_t num_tokens;      /* sum of their query lengths */
   int32_t max_blocks;      /* longest block list among the scheduled requests */
   int32_t q_free, q_reserved, q_committed;   /* pool counters after planning */
@@ -91,6 +108,12 @@ typedef struct pa_sched_metrics {
   int64_t steps, rollbacks, admissions, preemptions, recompute_tokens, finished, cancelled;
   int64_t scheduled_tokens;     /* tokens of committed steps */
   int64_t running, waiting;
+  /* reuse and reclaim */
+  int64_t prefix_hit_tokens;    /* tokens attached from the prefix index */
+  int64_t evictions;            /* cached blocks evicted under pressure */
+  int64_t cow_copies;           /* copy-on-write block copies planned */
+  int64_t cached_blocks;        /* blocks in the prefix index */
+  int64_t evictable;            /* cached blocks no request references */
 } pa_sched_metrics;
 
 /* Create a scheduler.  Checks: positive sizes, block_order a permutation,
@@ -100,9 +123,19 @@ pa_status pa_sched_create(const pa_sched_config* cfg, pa_sched** out);
 void pa_sched_destroy(pa_sched* s);
 
 /* Queue a request at the back of the waiting queue.  request_id must be new;
- * prompt_len >= 1, output_len >= 1. */
+ * prompt_len >= 1, output_len >= 1.  block_keys [n_keys] (may be NULL when
+ * n_keys is 0, n_keys <= prompt_len / block_size): key j identifies the
+ * content of the first (j+1)*block_size prompt tokens, including everything
+ * that makes cached K/V reusable (token ids, model version, adapters, ...);
+ * requests with keys share cached prefix blocks (see "Shared blocks"). */
 pa_status pa_sched_add_request(pa_sched* s, int64_t request_id, int32_t prompt_len,
-                               int32_t output_len);
+                               int32_t output_len, const uint64_t* block_keys, int32_t n_keys);
+
+/* Parallel sampling: child_id (new) shares every block and the token state of
+ * the RUNNING request parent_id and runs after every other running request;
+ * output_len must exceed the tokens already generated.  PA_ERR_BAD_STATE if
+ * a plan is pending or the parent is not running. */
+pa_status pa_sched_fork(pa_sched* s, int64_t parent_id, int64_t child_id, int32_t output_len);
 
 /* Plan one step (see the header comment); the plan stays pending until
  * commit or rollback.  info may be NULL. */
@@ -116,11 +149,13 @@ pa_status pa_sched_schedule(pa_sched* s, pa_sched_plan_info* info);
  *   preempted   [cap_preempted, 3] int64: (request id, tokens it held,
  *               blocks released), in the order they happened; may be NULL
  *               when cap_preempted is 0
+ *   copies      [cap_copies, 2] int32: (source block, destination block) of
+ *               each copy-on-write; may be NULL when cap_copies is 0
  * PA_ERR_BAD_SHAPE if a capacity is too small (nothing is written). */
 pa_status pa_sched_plan_copy(const pa_sched* s, int64_t* request_ids, int32_t* num_computed,
                              int32_t* query_lens, int32_t cap_reqs, int32_t* block_table,
                              int32_t max_blocks_per_req, int64_t* preempted,
-                             int32_t cap_preempted);
+                             int32_t cap_preempted, int32_t* copies, int32_t cap_copies);
 
 /* The step ran.  finished_ids [cap_finished] receives the requests that
  * finished (may be NULL when cap_finished is 0; PA_ERR_BAD_SHAPE and no

@@ -16,7 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 SCHED_LIB_PATH = os.path.join(_HERE, "libpa_sched.so")
 
 SCHED_EXPORTS = [
-    "pa_sched_create", "pa_sched_destroy", "pa_sched_add_request", "pa_sched_schedule",
+    "pa_sched_create", "pa_sched_destroy", "pa_sched_add_request", "pa_sched_fork", "pa_sched_schedule",
     "pa_sched_plan_copy", "pa_sched_commit", "pa_sched_rollback", "pa_sched_cancel",
     "pa_sched_get_metrics", "pa_sched_last_error",
 ]
@@ -32,7 +32,7 @@ class _Config(ctypes.Structure):
 
 class _PlanInfo(ctypes.Structure):
     _fields_ = [("num_reqs", ctypes.c_int32), ("num_preempted", ctypes.c_int32),
-                ("num_tokens", ctypes.c_int64), ("max_blocks", ctypes.c_int32),
+                ("num_copies", ctypes.c_int32), ("num_tokens", ctypes.c_int64), ("max_blocks", ctypes.c_int32),
                 ("q_free", ctypes.c_int32), ("q_reserved", ctypes.c_int32),
                 ("q_committed", ctypes.c_int32)]
 
@@ -40,7 +40,8 @@ class _PlanInfo(ctypes.Structure):
 _METRIC_FIELDS = ["q_free", "q_reserved", "q_committed", "q_capacity", "q_live", "tail_waste",
                   "peak_used", "allocation_failures", "steps", "rollbacks", "admissions",
                   "preemptions", "recompute_tokens", "finished", "cancelled", "scheduled_tokens",
-                  "running", "waiting"]
+                  "running", "waiting", "prefix_hit_tokens", "evictions", "cow_copies",
+                  "cached_blocks", "evictable"]
 
 
 class _Metrics(ctypes.Structure):
@@ -67,12 +68,15 @@ def sched_lib():
     L.pa_sched_destroy.restype = None
     L.pa_sched_destroy.argtypes = [vp]
     L.pa_sched_add_request.restype = ctypes.c_int
-    L.pa_sched_add_request.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
+    L.pa_sched_add_request.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.POINTER(ctypes.c_uint64), ctypes.c_int32]
+    L.pa_sched_fork.restype = ctypes.c_int
+    L.pa_sched_fork.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32]
     L.pa_sched_schedule.restype = ctypes.c_int
     L.pa_sched_schedule.argtypes = [vp, ctypes.POINTER(_PlanInfo)]
     L.pa_sched_plan_copy.restype = ctypes.c_int
     L.pa_sched_plan_copy.argtypes = [vp, i64p, i32p, i32p, ctypes.c_int32, i32p, ctypes.c_int32,
-                                     i64p, ctypes.c_int32]
+                                     i64p, ctypes.c_int32, i32p, ctypes.c_int32]
     L.pa_sched_commit.restype = ctypes.c_int
     L.pa_sched_commit.argtypes = [vp, i64p, ctypes.c_int32, i32p]
     L.pa_sched_rollback.restype = ctypes.c_int
@@ -120,35 +124,43 @@ class Scheduler:
     def __del__(self):
         self.close()
 
-    def add_request(self, rid: int, prompt_len: int, output_len: int) -> None:
-        _check(sched_lib().pa_sched_add_request(self._h, rid, prompt_len, output_len),
+    def add_request(self, rid: int, prompt_len: int, output_len: int, keys: Sequence[int] = ()) -> None:
+        k = np.ascontiguousarray(np.asarray(keys, dtype=np.uint64))
+        _check(sched_lib().pa_sched_add_request(self._h, rid, prompt_len, output_len,
+                                                _ptr(k, ctypes.c_uint64) if len(k) else None, len(k)),
                "pa_sched_add_request")
+
+    def fork(self, parent: int, child: int, output_len: int) -> None:
+        _check(sched_lib().pa_sched_fork(self._h, parent, child, output_len), "pa_sched_fork")
 
     def schedule_arrays(self):
         """Plan a step; return (info, request_ids, num_computed, query_lens,
-        block_table [R, M] -1 padded, preempted [P, 3])."""
+        block_table [R, M] -1 padded, preempted [P, 3], copies [C, 2])."""
         L = sched_lib()
         info = _PlanInfo()
         _check(L.pa_sched_schedule(self._h, ctypes.byref(info)), "pa_sched_schedule")
-        R, P, M = info.num_reqs, info.num_preempted, max(info.max_blocks, 1)
+        R, P, C, M = info.num_reqs, info.num_preempted, info.num_copies, max(info.max_blocks, 1)
         ids = np.zeros(R, np.int64)
         comp = np.zeros(R, np.int32)
         ql = np.zeros(R, np.int32)
         bt = np.full((R, M), -1, np.int32)
         pre = np.zeros((P, 3), np.int64)
+        cp = np.zeros((C, 2), np.int32)
         _check(L.pa_sched_plan_copy(self._h, _ptr(ids, ctypes.c_int64), _ptr(comp, ctypes.c_int32),
                                     _ptr(ql, ctypes.c_int32), R, _ptr(bt, ctypes.c_int32), M,
-                                    _ptr(pre, ctypes.c_int64) if P else None, P),
+                                    _ptr(pre, ctypes.c_int64) if P else None, P,
+                                    _ptr(cp, ctypes.c_int32) if C else None, C),
                "pa_sched_plan_copy")
-        return info, ids, comp, ql, bt, pre
+        return info, ids, comp, ql, bt, pre, cp
 
     def schedule(self) -> dict:
         """The pending plan in the reference scheduler's format."""
-        info, ids, comp, ql, bt, pre = self.schedule_arrays()
+        info, ids, comp, ql, bt, pre, cp = self.schedule_arrays()
         sched = [(int(i), int(c), int(n)) for i, c, n in zip(ids, comp, ql)]
-        blocks = {int(i): [int(b) for b in row if b >= 0] for i, row in zip(ids, bt)}
+        blocks = {int(i): row[row >= 0].tolist() for i, row in zip(ids, bt)}
         return {"sched": sched, "blocks": blocks,
                 "preempted": [(int(a), int(b), int(c)) for a, b, c in pre],
+                "copies": [(int(a), int(b)) for a, b in cp],
                 "q_free": info.q_free, "q_reserved": info.q_reserved,
                 "q_committed": info.q_committed}
 

@@ -165,3 +165,64 @@ def test_c_abi_error_paths():
     s.cancel(7)
     s.cancel(7)                                       # idempotent
     assert s.metrics()["cancelled"] == 1 and s.metrics()["q_free"] == 4
+
+
+def test_shared_prefix_trace_identical():
+    cfg = st.TraceConfig(num_requests=600, steps=150, num_blocks=3000, max_num_seqs=96,
+                         max_num_batched_tokens=4096, chunk=512, shared_prompts=4,
+                         shared_len=700, shared_frac=0.8, seed=13)
+    prod, ref = _both(cfg)
+    pp = st.drive(prod, cfg, fail_steps=(7, 40, 41))
+    pr = st.drive(ref, cfg, fail_steps=(7, 40, 41))
+    _same_plans(pp, pr)
+    m = pp[-1]["metrics"]
+    assert m["prefix_hit_tokens"] > 0 and m["evictions"] > 0 and m["preemptions"] > 0
+    assert m["q_live"] <= m["q_committed"]
+    for p in pp:
+        # shared blocks appear in several requests' tables: ownership is counted once
+        owned = [b for rid, _, _ in p["sched"] for b in p["blocks"][rid]]
+        assert len(set(owned)) <= len(owned)
+
+
+@pytest.mark.parametrize("seed", [4, 5, 6, 7])
+def test_forks_cow_cancels_rollbacks_identical(seed):
+    rng = random.Random(seed)
+    B = rng.choice([2, 4, 16])
+    nb = rng.choice([24, 60, 300])
+    order = list(range(nb)); rng.shuffle(order)
+    args = dict(num_blocks=nb, block_size=B, max_num_seqs=rng.choice([4, 16]),
+                max_num_batched_tokens=rng.choice([32, 256]), chunk=rng.choice([8, 64]),
+                block_order=order)
+    prod, ref = pa.Scheduler(**args), RefScheduler(**args)
+    sysk = [[rng.getrandbits(60) for _ in range(6)] for _ in range(3)]
+    nid = 0
+    for i in range(30):
+        p, o = rng.randint(1, 100), rng.randint(1, 25)
+        keys = sysk[rng.randrange(3)][:min(6, p // B)] if rng.random() < 0.7 else []
+        prod.add_request(nid, p, o, keys); ref.add_request(nid, p, o, keys)
+        nid += 1
+    for k in range(200):
+        if rng.random() < 0.15:                    # parallel sampling of a running request
+            running = [r.rid for r in ref.running]
+            if running:
+                par = rng.choice(running)
+                out = ref.reqs[par].generated + rng.randint(1, 10)
+                prod.fork(par, nid, out); ref.fork(par, nid, out)
+                nid += 1
+        a, b = prod.schedule(), ref.schedule()
+        assert a == b, f"step {k}: plans differ"
+        if rng.random() < 0.1:
+            victim = rng.randrange(nid)
+            prod.cancel(victim); ref.cancel(victim)
+        if rng.random() < 0.12:
+            prod.rollback(); ref.rollback()
+        else:
+            assert prod.commit() == ref.commit()
+        assert prod.metrics() == ref.metrics(), f"step {k}: metrics differ"
+        if rng.random() < 0.05:                    # new arrivals
+            p, o = rng.randint(1, 100), rng.randint(1, 25)
+            keys = sysk[rng.randrange(3)][:min(6, p // B)]
+            prod.add_request(nid, p, o, keys); ref.add_request(nid, p, o, keys)
+            nid += 1
+    m = prod.metrics()
+    assert m["q_free"] + m["q_reserved"] + m["q_committed"] == nb

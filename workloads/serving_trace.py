@@ -44,6 +44,11 @@ class TraceConfig:
     seed: int = 5
     artificial_preempt_prob: float = 0.0   # test hook (0 disables)
     artificial_preempt_max: int = 500
+    # shared system prompts: a request starts with one of `shared_prompts`
+    # prompts of `shared_len` tokens with probability `shared_frac`
+    shared_prompts: int = 0
+    shared_len: int = 0
+    shared_frac: float = 0.0
 
 
 def requests(cfg: TraceConfig) -> List[Tuple[int, int, int]]:
@@ -53,6 +58,38 @@ def requests(cfg: TraceConfig) -> List[Tuple[int, int, int]]:
                                             cfg.num_requests), 1, cfg.prompt_max)).astype(int)
     outputs = gen.geometric(1.0 / cfg.output_mean, cfg.num_requests).astype(int)
     return [(i, int(p), int(o)) for i, (p, o) in enumerate(zip(prompts, outputs))]
+
+
+def _mix(x: np.ndarray) -> np.ndarray:
+    """SplitMix64 finaliser (Steele, Lea, Flood 2014) on uint64 arrays."""
+    x = x.astype(np.uint64)
+    with np.errstate(over="ignore"):
+        x = (x ^ (x >> np.uint64(30))) * np.uint64(0xBF58476D1CE4E5B9)
+        x = (x ^ (x >> np.uint64(27))) * np.uint64(0x94D049BB133111EB)
+    return x ^ (x >> np.uint64(31))
+
+
+def block_keys(cfg: TraceConfig) -> dict:
+    """Prefix keys of each request's full prompt blocks: a block lying wholly
+    inside the request's shared system prompt gets the key of (prompt, block
+    index) -- identical across requests -- any other block a key of (request,
+    block index).  Requests without a shared prompt get no keys."""
+    if cfg.shared_prompts <= 0 or cfg.shared_len <= 0:
+        return {}
+    gen = np.random.default_rng(cfg.seed + 3000)
+    out = {}
+    for rid, p, _ in requests(cfg):
+        if gen.random() >= cfg.shared_frac:
+            continue
+        sp = int(gen.integers(cfg.shared_prompts))
+        nfull = p // cfg.block_size
+        j = np.arange(nfull, dtype=np.uint64)
+        inside = (j + np.uint64(1)) * np.uint64(cfg.block_size) <= np.uint64(cfg.shared_len)
+        with np.errstate(over="ignore"):
+            shared = _mix(np.uint64(sp + 1) * np.uint64(0x9E3779B97F4A7C15) + j)
+            own = _mix(np.uint64(rid + 1) * np.uint64(0xD1B54A32D192ED03) + j + np.uint64(1 << 40))
+        out[rid] = np.where(inside, shared, own).tolist()
+    return out
 
 
 def block_order(cfg: TraceConfig) -> np.ndarray:
@@ -80,8 +117,9 @@ def drive(sched, cfg: TraceConfig, fail_steps: Sequence[int] = ()) -> List[dict]
     committed.  Returns the plans (dicts: sched [(rid, num_computed, n)],
     blocks {rid: [block ids]}, preempted [(rid, held, released)], pool
     counters, index, rolled_back, finished, metrics)."""
+    keys = block_keys(cfg)
     for rid, p, o in requests(cfg):
-        sched.add_request(rid, p, o)
+        sched.add_request(rid, p, o, keys.get(rid, ()))
     fail = set(fail_steps)
     plans = []
     for k in range(cfg.steps):
