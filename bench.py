@@ -51,6 +51,8 @@ def parse():
     p.add_argument("--workload", default="c3", choices=["c2", "c3", "c4"])
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="budget of oracle work for the CPU baseline (0 disables it)")
+    p.add_argument("--no-swap", dest="swap", action="store_false",
+                   help="skip the swap-out / swap-in round-trip measurement")
     p.add_argument("--no-rope", dest="rope", action="store_false",
                    help="skip the separate timing of the fused rotary + cache-write kernel")
     p.add_argument("--copy-calibration", action="store_true",
@@ -208,6 +210,61 @@ def scheduler_timing(product: bool, steps: int = 200):
             "scheduled_tokens": toks, "preemptions": m["preemptions"]}
 
 
+def swap_measurement(dev, reps: int = 10):
+    """Swap-out + swap-in of whole block columns (every layer's K and V
+    block) between the device cache and a pinned host pool with
+    pa_copy_blocks, in the geometry of the pages' worked swap example (512 KiB
+    of K/V per token: 32 layers, 32 kv heads, head_dim 128, bf16; block 16).
+    Returns the measured round trips and the pages' formula
+    2 * payload / bandwidth beside them."""
+    import numpy as np
+    import torch
+    import paged_kv_attention_reshape_amd as pa
+    L, HKV, D, B = 32, 32, 128, 16
+    kappa = 2 * L * HKV * D * 2                  # bytes of K/V per token (all layers)
+    nb, hb = 96, 64
+    pools = torch.zeros((2 * L, nb, B, HKV, D), dtype=torch.bfloat16, device=dev)
+    host = torch.empty((2 * L, hb, B, HKV, D), dtype=torch.bfloat16, pin_memory=True)
+    stream = torch.cuda.current_stream()
+    out = {}
+    for n in (1, 64):
+        g = np.random.default_rng(n)
+        src = g.choice(nb, n, replace=False).astype(np.int32)
+        dst = g.choice(hb, n, replace=False).astype(np.int32)
+        p_out = torch.from_numpy(np.stack([src, dst], 1)).to(dev)
+        p_in = torch.from_numpy(np.stack([dst, src], 1)).to(dev)
+        for _ in range(2):
+            pa.copy_blocks(pools, host, p_out)
+            pa.copy_blocks(host, pools, p_in)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        torch.cuda.synchronize()
+        e[0].record(stream)
+        for _ in range(reps):
+            pa.copy_blocks(pools, host, p_out)
+        e[1].record(stream)
+        for _ in range(reps):
+            pa.copy_blocks(host, pools, p_in)
+        e[2].record(stream)
+        torch.cuda.synchronize()
+        t_out = e[0].elapsed_time(e[1]) / reps
+        t_in = e[1].elapsed_time(e[2]) / reps
+        payload = n * B * kappa
+        out[f"{n}_block"] = {"bytes_each_way": payload, "out_ms": round(t_out, 4), "in_ms": round(t_in, 4),
+                             "roundtrip_ms": round(t_out + t_in, 4),
+                             "out_gbs": round(payload / t_out / 1e6, 1), "in_gbs": round(payload / t_in / 1e6, 1)}
+    beta = 2 * out["64_block"]["bytes_each_way"] / (out["64_block"]["roundtrip_ms"] * 1e6)   # GB/s
+    tokens = 7
+    out["pages_example"] = {
+        "tokens": tokens, "kv_bytes_per_token": kappa,
+        "formula_ms_at_24_gbs": round(2 * tokens * kappa / 24e9 * 1e3, 4),
+        "formula_ms_at_measured_bandwidth": round(2 * tokens * kappa / (beta * 1e9) * 1e3, 4),
+        "measured_bandwidth_gbs": round(beta, 1),
+        "measured_ms_one_block": out["1_block"]["roundtrip_ms"],
+        "note": "the pool moves whole blocks: 7 tokens occupy one 16-token block column (16 * kappa bytes each way)",
+    }
+    return out
+
+
 def load_traffic(kernel: str):
     """HBM traffic per launch measured by rocprofv3 counters (FETCH_SIZE,
     WRITE_SIZE), scaled by the copy-kernel calibration, if a summary exists for
@@ -363,6 +420,8 @@ def main():
                 "bytes_per_launch": rope_bytes, "achieved": round(rope_gbs, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(rope_gbs / HBM_PEAK_GBS, 4)}
 
+    swap = swap_measurement(dev) if args.swap else None
+
     # host scheduler / block allocator (C++) on the serving trace
     sched_t = scheduler_timing(product=True)
     sched_t["trace"] = "2048 requests at step 0, 200 steps, 16384 blocks of 16, budget 8192, chunk 512"
@@ -425,6 +484,7 @@ def main():
         },
         "rope_write_kv": rope,
         "scheduler": sched_t,
+        "swap_roundtrip": swap,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -194,6 +194,38 @@ pa_status pa_rope_write_kv(void* query, const void* key, const void* value, void
                            pa_dtype dtype, void* stream);
 
 /*
+ * pa_copy_blocks -- copy whole cache blocks between pools of one block layout.
+ *
+ * Serves two block movements the pages describe: copy-on-write of a shared,
+ * partly filled block before a request writes into it ([P5] "显存与调度",
+ * "共享前缀会改变块的所有权": a writable shared block needs copy-on-write; the
+ * scheduler of pa_sched.h lists the pairs), and swap-out / swap-in of a
+ * preempted request's blocks between the device cache and a pinned host
+ * pool ([P2] "vLLM 抢占机制源码精读", section "Swap 模式"; [P4] "Chunked Prefill
+ * 与 Preemption": the swap round trip moves the payload out and back).
+ *
+ *   src_pools, dst_pools  num_pools pools each, pool k at base + k * stride
+ *                         bytes (e.g. the 2L per-layer K and V caches of a
+ *                         model); device memory, or pinned host memory from
+ *                         hipHostMalloc (read or written over the host link)
+ *   block_pairs           device int32 [num_pairs, 2]: (source block,
+ *                         destination block); pair i copies block_bytes bytes
+ *                         from source block of every source pool to the
+ *                         destination block of the matching destination pool
+ *   src_num_blocks,
+ *   dst_num_blocks        blocks per pool; pairs outside them are skipped
+ *   block_bytes           bytes of one block (block_size * num_kv_heads *
+ *                         head_dim * element size), a multiple of 16
+ * Destination blocks must be distinct and must not be a source of the same
+ * call (else the result is undefined).  The copy is exact.  Enqueued on
+ * stream; a plan's copies must be enqueued before its cache write.
+ */
+pa_status pa_copy_blocks(const void* src_pools, void* dst_pools, const int32_t* block_pairs,
+                         int32_t num_pairs, int32_t num_pools, int64_t src_pool_stride,
+                         int64_t dst_pool_stride, int32_t src_num_blocks, int32_t dst_num_blocks,
+                         int64_t block_bytes, void* stream);
+
+/*
  * pa_attention_workspace_size -- bytes of device workspace pa_attention needs
  * for this step (plan tables plus split-K partial results).  Takes the same
  * host mirrors pa_attention plans from; returns 0 and sets pa_last_error() if

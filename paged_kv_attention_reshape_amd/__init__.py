@@ -8,6 +8,6 @@ library; the first call does, and raises if it has not been built.
 from ._lib import (  # noqa: F401
     EXPORTS, LIB_PATH, PA_BF16, PA_F32, PAError, Workspace, abi_version, attention,
     attention_workspace_size, build_step_metadata, compute_slot_mapping, set_profiling_events, last_error, lib, status_str,
-    validate_metadata, write_kv, rope_write_kv,
+    validate_metadata, write_kv, rope_write_kv, copy_blocks,
 )
 from ._sched import SCHED_EXPORTS, SCHED_LIB_PATH, Scheduler, sched_lib  # noqa: F401,E402

@@ -29,7 +29,7 @@ STATUS = {
 EXPORTS = [
     "pa_abi_version", "pa_status_str", "pa_last_error", "pa_build_step_metadata",
     "pa_compute_slot_mapping", "pa_write_kv", "pa_attention_workspace_size", "pa_attention",
-    "pa_set_profiling_events", "pa_validate_metadata", "pa_rope_write_kv",
+    "pa_set_profiling_events", "pa_validate_metadata", "pa_rope_write_kv", "pa_copy_blocks",
 ]
 
 
@@ -77,6 +77,9 @@ def lib():
                                    ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                                    ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                    ctypes.c_int, _vp]
+    L.pa_copy_blocks.restype = ctypes.c_int
+    L.pa_copy_blocks.argtypes = [_vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                 ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, _vp]
     L.pa_attention_workspace_size.restype = ctypes.c_size_t
     L.pa_attention_workspace_size.argtypes = [_i32p, _i32p, ctypes.c_int32, ctypes.c_int32,
                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -225,6 +228,23 @@ def rope_write_kv(query, key, value, key_cache, value_cache, slot_mapping, posit
                                   _ptr(cos_sin_cache), cos_sin_cache.shape[0], rotary_dim,
                                   1 if neox else 0, T, Hq, Hkv, D, N, B, _dtype_code(query),
                                   ctypes.c_void_p(_stream(stream))), "pa_rope_write_kv")
+
+
+def copy_blocks(src_pools, dst_pools, block_pairs, stream=None) -> None:
+    """src_pools / dst_pools: tensors [P, N, B, Hkv, D] (or [N, B, Hkv, D]
+    for one pool), device or pinned host; block_pairs: device int32 [n, 2]
+    (source block, destination block).  Copies each pair in every pool."""
+    src = src_pools if src_pools.dim() == 5 else src_pools.unsqueeze(0)
+    dst = dst_pools if dst_pools.dim() == 5 else dst_pools.unsqueeze(0)
+    if src.shape[0] != dst.shape[0] or src.shape[2:] != dst.shape[2:] or src.dtype != dst.dtype:
+        raise ValueError("source and destination pools must have the same count, block layout and dtype")
+    P, Ns = src.shape[0], src.shape[1]
+    Nd = dst.shape[1]
+    block_bytes = src[0, 0].numel() * src.element_size()
+    _check(lib().pa_copy_blocks(_ptr(src), _ptr(dst), _ptr(block_pairs), block_pairs.shape[0], P,
+                                src.stride(0) * src.element_size(), dst.stride(0) * dst.element_size(),
+                                Ns, Nd, block_bytes, ctypes.c_void_p(_stream(stream))),
+           "pa_copy_blocks")
 
 
 def attention_workspace_size(h_query_start_loc, h_seq_lens, num_heads: int, num_kv_heads: int,

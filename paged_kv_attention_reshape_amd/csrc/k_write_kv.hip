@@ -13,6 +13,9 @@
 // K and V of a token are handled by the same workgroup (second half of the
 // block), which keeps the slot value in one cache line for both.  The kernel
 // is bandwidth- and latency-bound and touches each byte exactly once.
+//
+// The same file holds the device slot mapping and the block-copy kernel that
+// executes a plan's copy-on-write copies and swap transfers.
 #include "pa_internal.h"
 
 namespace pa {
@@ -67,6 +70,37 @@ slot_mapping_kernel(int64_t* __restrict__ slots, const int32_t* __restrict__ blo
   }
 }
 
+// Block copies between pools of the same block layout: pair i moves block
+// pairs[i].src of every source pool to block pairs[i].dst of the matching
+// destination pool (pool k at base + k * stride).  One workgroup per (pair,
+// pool); each thread moves 16-byte chunks, eight loads in flight before the
+// stores.  Serves copy-on-write (same pool) and swap between the device
+// cache and a pinned host pool (the kernel reads or writes host memory over
+// the host link directly, one launch for any scattered block list).
+__global__ void __launch_bounds__(kThreads)
+copy_blocks_kernel(const char* src, char* dst,
+                   const int32_t* __restrict__ pairs, int64_t src_stride, int64_t dst_stride,
+                   int32_t src_blocks, int32_t dst_blocks, int64_t chunks) {
+  const int64_t i = blockIdx.x;
+  const int64_t k = blockIdx.y;
+  const int32_t sb = pairs[2 * i];
+  const int32_t db = pairs[2 * i + 1];
+  if (sb < 0 || sb >= src_blocks || db < 0 || db >= dst_blocks) return;
+  // source and destination may be the same pool (distinct blocks)
+  const uint4* sp = reinterpret_cast<const uint4*>(src + k * src_stride) + (int64_t)sb * chunks;
+  uint4* dp = reinterpret_cast<uint4*>(dst + k * dst_stride) + (int64_t)db * chunks;
+  constexpr int U = 8;
+  int64_t c = threadIdx.x;
+  for (; c + (U - 1) * kThreads < chunks; c += U * kThreads) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = sp[c + u * kThreads];
+#pragma unroll
+    for (int u = 0; u < U; ++u) dp[c + u * kThreads] = v[u];
+  }
+  for (; c < chunks; c += kThreads) dp[c] = sp[c];
+}
+
 }  // namespace
 
 hipError_t launch_slot_mapping(int64_t* slots, const int32_t* block_table, int32_t M,
@@ -88,6 +122,17 @@ hipError_t launch_write_kv(const void* key, const void* value, void* key_cache, 
                      static_cast<const uint4*>(key), static_cast<const uint4*>(value),
                      static_cast<uint4*>(key_cache), static_cast<uint4*>(value_cache), slots, T,
                      num_slots, cpr);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(const void* src, void* dst, const int32_t* pairs, int32_t n,
+                              int32_t num_pools, int64_t src_stride, int64_t dst_stride,
+                              int32_t src_blocks, int32_t dst_blocks, int64_t block_bytes,
+                              hipStream_t s) {
+  if (n == 0 || num_pools == 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)n, (unsigned)num_pools), dim3(kThreads), 0, s,
+                     static_cast<const char*>(src), static_cast<char*>(dst), pairs, src_stride,
+                     dst_stride, src_blocks, dst_blocks, block_bytes / 16);
   return hipGetLastError();
 }
 

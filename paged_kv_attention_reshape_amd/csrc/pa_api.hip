@@ -4,6 +4,7 @@
 // plan sizing and the kernel launch sequence
 //   pa_write_kv:  write_kv
 //   pa_rope_write_kv: rope_write_kv (rotary embedding of Q and K fused with the write)
+//   pa_copy_blocks: copy_blocks (copy-on-write copies, swap transfers)
 //   pa_attention: plan -> row-wise split-K -> chunk (matrix cores) -> merge
 // all on the caller's stream.
 #include <stdarg.h>
@@ -327,6 +328,30 @@ pa_status pa_rope_write_kv(void* query, const void* key, const void* value, void
   hipError_t e = pa::launch_rope_write_kv(a, dtype == PA_BF16, head_dim, neox_style != 0,
                                           reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "rope_write_kv launch");
+  return PA_OK;
+}
+
+pa_status pa_copy_blocks(const void* src_pools, void* dst_pools, const int32_t* block_pairs,
+                         int32_t num_pairs, int32_t num_pools, int64_t src_pool_stride,
+                         int64_t dst_pool_stride, int32_t src_num_blocks, int32_t dst_num_blocks,
+                         int64_t block_bytes, void* stream) {
+  g_err.clear();
+  if (num_pairs < 0 || num_pools < 0) return fail(PA_ERR_BAD_SHAPE, "negative count");
+  if (num_pairs == 0 || num_pools == 0) return PA_OK;
+  if (num_pools > 65535) return fail(PA_ERR_BAD_SHAPE, "num_pools %d > 65535", num_pools);
+  if (!src_pools || !dst_pools || !block_pairs) return fail(PA_ERR_NULL_PTR, "NULL pointer argument");
+  if (block_bytes <= 0 || block_bytes % 16 != 0)
+    return fail(PA_ERR_BAD_SHAPE, "block_bytes %lld must be a positive multiple of 16", (long long)block_bytes);
+  if (src_num_blocks <= 0 || dst_num_blocks <= 0) return fail(PA_ERR_BAD_SHAPE, "pool sizes must be positive");
+  if (num_pools > 1 && (src_pool_stride < (int64_t)src_num_blocks * block_bytes ||
+                        dst_pool_stride < (int64_t)dst_num_blocks * block_bytes))
+    return fail(PA_ERR_BAD_SHAPE, "pool strides smaller than a pool");
+  if ((src_pool_stride | dst_pool_stride) % 16 != 0 || (((uintptr_t)src_pools | (uintptr_t)dst_pools) & 15))
+    return fail(PA_ERR_BAD_SHAPE, "pools and strides must be 16-byte aligned");
+  hipError_t e = pa::launch_copy_blocks(src_pools, dst_pools, block_pairs, num_pairs, num_pools,
+                                        src_pool_stride, dst_pool_stride, src_num_blocks,
+                                        dst_num_blocks, block_bytes, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "copy_blocks launch");
   return PA_OK;
 }
 

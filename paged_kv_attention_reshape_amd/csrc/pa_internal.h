@@ -174,6 +174,11 @@ struct AttnArgs {
   float* o_part;      // [parts, Hq, D] unnormalised
 };
 
+hipError_t launch_copy_blocks(const void* src, void* dst, const int32_t* pairs, int32_t n,
+                              int32_t num_pools, int64_t src_stride, int64_t dst_stride,
+                              int32_t src_blocks, int32_t dst_blocks, int64_t block_bytes,
+                              hipStream_t s);
+
 // Fused rotary embedding + cache write (one workgroup per token).
 struct RopeArgs {
   void* query;                 // [T, Hq, D], rotated in place

@@ -228,6 +228,23 @@ def test_rope_write_kv_host_checks():
     assert rc(T=0, q=0, pos=0) == "PA_OK"
 
 
+def test_copy_blocks_host_checks():
+    L = pa.lib()
+    def rc(**over):
+        a = dict(s=4096, d=4096, p=4096, n=3, P=2, ss=1 << 20, ds=1 << 20, ns=16, nd=16, bb=4096)
+        a.update(over)
+        return pa.status_str(L.pa_copy_blocks(a["s"], a["d"], a["p"], a["n"], a["P"], a["ss"], a["ds"],
+                                              a["ns"], a["nd"], a["bb"], None))
+    assert rc(n=-1) == "PA_ERR_BAD_SHAPE"
+    assert rc(p=0) == "PA_ERR_NULL_PTR"
+    assert rc(bb=100) == "PA_ERR_BAD_SHAPE"
+    assert rc(ss=4096) == "PA_ERR_BAD_SHAPE"           # pools would overlap
+    assert rc(s=4100) == "PA_ERR_BAD_SHAPE"
+    assert rc(nd=0) == "PA_ERR_BAD_SHAPE"
+    assert rc(P=70000) == "PA_ERR_BAD_SHAPE"
+    assert rc(n=0, s=0) == "PA_OK"
+
+
 def test_generator_host_mirror_properties():
     # deterministic, distinct streams, ~N(0,1), bf16 rounding to nearest even
     a = rng.row_values(rng.base_row_keys(rng.key(1, 2), np.arange(64)), 256, "f32")
