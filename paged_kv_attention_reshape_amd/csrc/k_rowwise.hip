@@ -372,7 +372,16 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnArgs a) {
     const int hq = g * G + pair % G;
     const int64_t p0 = first + tau;
     // (m, l) of up to 64 partitions per pass: lane p holds partition p's pair;
-    // with at most 64 partitions (the usual case) one load serves both passes
+    // with at most 64 partitions (the usual case) one load serves both passes.
+    // The first eight partitions' output slices do not depend on the max, so
+    // they are loaded together with (m, l).
+    const float* obase0 = a.o_part + (p0 * a.Hq + hq) * D + lane * PER;
+    const int64_t pstep = (int64_t)stride * a.Hq * D;   // floats between partitions
+    float v0[8][PER];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int e = 0; e < PER; ++e) v0[u][e] = u < n ? obase0[u * pstep + e] : 0.f;
     float2 ml0 = make_float2(kNegInf, 0.f);
     if (lane < n) ml0 = *reinterpret_cast<const float2*>(a.ml_part + ((p0 + (int64_t)lane * stride) * a.Hq + hq) * 2);
     float M = ml0.x;
@@ -397,9 +406,17 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnArgs a) {
       }
       const int cnt = min(64, n - pb);
       const float* obase = a.o_part + ((p0 + (int64_t)pb * stride) * a.Hq + hq) * D + lane * PER;
-      const int64_t pstep = (int64_t)stride * a.Hq * D;   // floats between partitions
-      // eight partitions' slices in flight at a time
       int j = 0;
+      if (pb == 0) {   // the slices loaded up front (zero past the count)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u));
+#pragma unroll
+          for (int e = 0; e < PER; ++e) num[e] += u < cnt ? wj * v0[u][e] : 0.f;
+        }
+        j = 8;
+      }
+      // eight partitions' slices in flight at a time
       for (; j + 8 <= cnt; j += 8) {
         float v[8][PER];
 #pragma unroll
