@@ -109,21 +109,11 @@ struct ChunkGeo {
   static constexpr int LOADS = KT * CPR / kThreads;  // 16-byte chunks per thread per tile
 };
 
-// Online-softmax state of one lane's query row.  Scores reach the softmax
-// already in log2 units and shifted: Q is pre-scaled by scale * log2(e) and
-// the q.k accumulator starts at -c (mneg holds -c in all 16 slots), so the
-// MFMA yields s * scale * log2(e) - c directly.  c is the reference the
-// exponentials use: the running max m_run once the row has seen a visible
-// key, 0 before.  thr is the rescale threshold relative to c: -inf until the
-// first visible key (forces the first update), then the slack.
 template <int D, int G>
 struct ChunkState {
   using Gm = ChunkGeo<D, G>;
   f32x16_t o[Gm::DB];
-  f32x16_t mneg;
   float m_run;
-  float c;
-  float thr;
   float l_run;
 };
 
@@ -133,15 +123,17 @@ typedef const __attribute__((address_space(3))) char* lds_cptr;
 // S^T = K Q^T for one 64-key tile: two 32-key halves, KSTEPS k-steps each.
 // The K fragments are read from the swizzled LDS tile two k-steps ahead of
 // the MFMAs that use them.
-// The first k-step adds the shift block -c, so the scores come out relative
-// to the row's reference max with no per-score arithmetic.
 template <int D, int G>
 __device__ __forceinline__ void chunk_qk(f32x16_t (&s)[2], lds_cptr kbuf,
                                          const u32x4_t (&qf)[ChunkGeo<D, G>::KSTEPS],
-                                         const int (&koff)[ChunkGeo<D, G>::KSTEPS],
-                                         const f32x16_t& mneg) {
+                                         const int (&koff)[ChunkGeo<D, G>::KSTEPS]) {
   using Gm = ChunkGeo<D, G>;
   constexpr int ROWB = Gm::ROWB, KSTEPS = Gm::KSTEPS;
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[sub][e] = 0.f;
+  }
 #pragma unroll
   for (int kk = 0; kk < KSTEPS; ++kk) {
 #pragma unroll
@@ -150,7 +142,7 @@ __device__ __forceinline__ void chunk_qk(f32x16_t (&s)[2], lds_cptr kbuf,
           kbuf + koff[kk] + sub * 32 * ROWB);
       s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kv),
                                                        __builtin_bit_cast(bf16x8_t, qf[kk]),
-                                                       kk == 0 ? mneg : s[sub], 0, 0, 0);
+                                                       s[sub], 0, 0, 0);
     }
   }
   __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -165,14 +157,14 @@ __device__ __forceinline__ void chunk_qk(f32x16_t (&s)[2], lds_cptr kbuf,
 __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
 
 // Mask (diagonal / segment-end tiles only), lazy online-softmax update and
-// the tile's probabilities as bf16 pairs in the MFMA operand order.  The
-// scores arrive shifted by -c in log2 units, so the exponent input is the
-// score itself; the row max is a three-input max tree plus one permlane32
-// swap with the partner lane that holds the row's other keys.
+// the tile's probabilities as bf16 pairs in the MFMA operand order.  The row
+// max is a three-input max tree over the lane's 32 scores plus one
+// permlane32 swap with the partner lane that holds the row's other keys; the
+// scale (times log2 e) is applied in fp32 in the exponent's argument.
 template <int D, int G>
 __device__ __forceinline__ void chunk_softmax(ChunkState<D, G>& st, f32x16_t (&s)[2],
                                               uint32_t (&pk)[2][8], int kt, int qpos, int k1,
-                                              int w_qpos_lo, int lane) {
+                                              int w_qpos_lo, float sl, int lane) {
   using Gm = ChunkGeo<D, G>;
   constexpr int DB = Gm::DB;
   const int grp = lane >> 5;
@@ -198,38 +190,28 @@ __device__ __forceinline__ void chunk_softmax(ChunkState<D, G>& st, f32x16_t (&s
                    max3f(t[6], t[7], fmaxf(t[8], fmaxf(t[9], t[10]))));
   {
     const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-    mx = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    mx = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1])) * sl;
   }
-  if (__builtin_amdgcn_ballot_w64(mx > st.thr)) {
-    // some row's max grew past the slack (or the row saw its first visible
-    // key): move every such row to its true max
-    const bool up = mx > st.thr;
-    const float m_abs = mx + st.c;                       // tile max, absolute
-    const float m_new = up ? fmaxf(st.m_run, m_abs) : st.m_run;
-    const float alpha = (!up || st.m_run == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(st.m_run - m_new);
-    const float c_new = m_new == kNegInf ? 0.f : m_new;
-    const float delta = c_new - st.c;
+  if (__builtin_amdgcn_ballot_w64(mx > st.m_run + kRescaleSlack)) {
+    // some row's max grew past the slack: move every row to its true max
+    const float m_new = fmaxf(st.m_run, mx);
+    const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(st.m_run - m_new);
     st.m_run = m_new;
-    st.c = c_new;
-    st.thr = m_new == kNegInf ? kNegInf : kRescaleSlack;
     st.l_run *= alpha;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int e = 0; e < 16; ++e) st.o[db][e] *= alpha;
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[sub][e] -= delta;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) st.mneg[e] = -c_new;
   }
+  const float m_use = st.m_run == kNegInf ? 0.f : st.m_run;
   float psum = 0.f;
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
     for (int e = 0; e < 16; e += 2) {
-      pk[sub][e >> 1] = pack_bf16(__builtin_amdgcn_exp2f(s[sub][e]), __builtin_amdgcn_exp2f(s[sub][e + 1]));
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][e], sl, -m_use));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][e + 1], sl, -m_use));
+      pk[sub][e >> 1] = pack_bf16(p0, p1);
       // row sum of the bf16-rounded probabilities (the ones p.v uses)
       psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[sub][e >> 1]),
                                              __builtin_bit_cast(bf16x2_t, 0x3F803F80u), psum, false);
@@ -272,11 +254,11 @@ __device__ __forceinline__ void chunk_tile(ChunkState<D, G>& st, lds_cptr kbuf, 
                                            const int (&koff)[ChunkGeo<D, G>::KSTEPS],
                                            const int (&voff)[ChunkGeo<D, G>::DB],
                                            const int (&voff8)[ChunkGeo<D, G>::DB], int kt,
-                                           int qpos, int k1, int w_qpos_lo, int lane) {
+                                           int qpos, int k1, int w_qpos_lo, float sl, int lane) {
   f32x16_t s[2];
   uint32_t pk[2][8];
-  chunk_qk<D, G>(s, kbuf, qf, koff, st.mneg);
-  chunk_softmax<D, G>(st, s, pk, kt, qpos, k1, w_qpos_lo, lane);
+  chunk_qk<D, G>(s, kbuf, qf, koff);
+  chunk_softmax<D, G>(st, s, pk, kt, qpos, k1, w_qpos_lo, sl, lane);
   chunk_pv<D, G>(st, vbuf, pk, voff, voff8);
 }
 
@@ -345,24 +327,14 @@ __global__ void __launch_bounds__(kThreads, 512 / kThreads) chunk_kernel(AttnArg
   const int w_qpos_lo = c + tok0 + w_tau_lo;
   const int w_qpos_hi = c + min(tok0 + w_tau_hi, q - 1);
 
-  // Q fragment (B operand of S^T = K Q^T): lane holds d = 16kk + 8(lane/32) .. +8,
-  // multiplied by scale * log2(e) in fp32 and rounded once to bf16, so the
-  // scores come out of the MFMA in log2 units
+  // Q fragment (B operand of S^T = K Q^T): lane holds d = 16kk + 8(lane/32) .. +8
   u32x4_t qf[KSTEPS];
   {
     const char* qrow = static_cast<const char*>(a.query) +
                        ((int64_t)(t0 + tok0 + tau) * a.Hq + hq) * ROWB + (lane >> 5) * 16;
-    const float sl = a.scale_log2;
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-      const u32x4_t raw = row_ok ? *reinterpret_cast<const u32x4_t*>(qrow + kk * 32) : u32x4_t{0, 0, 0, 0};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float lo = __uint_as_float(raw[j] << 16) * sl;
-        const float hi = __uint_as_float(raw[j] & 0xFFFF0000u) * sl;
-        qf[kk][j] = pack_bf16(lo, hi);
-      }
-    }
+    for (int kk = 0; kk < KSTEPS; ++kk)
+      qf[kk] = row_ok ? *reinterpret_cast<const u32x4_t*>(qrow + kk * 32) : u32x4_t{0, 0, 0, 0};
   }
   // lane-constant LDS read offsets within a tile buffer
   const int l32 = lane & 31, grp = lane >> 5, gam = lane >> 4, li = lane & 15;
@@ -450,11 +422,8 @@ __global__ void __launch_bounds__(kThreads, 512 / kThreads) chunk_kernel(AttnArg
 #pragma unroll
     for (int e = 0; e < 16; ++e) st.o[db][e] = 0.f;
   st.m_run = kNegInf;   // in log2 units (score * scale * log2 e)
-  st.c = 0.f;
-  st.thr = kNegInf;
   st.l_run = 0.f;       // this lane's share of the row sum
-#pragma unroll
-  for (int e = 0; e < 16; ++e) st.mneg[e] = 0.f;
+  const float sl = a.scale_log2;
 
   const int n_tiles = (k1 - k0 + KT - 1) / KT;
   const lds_cptr kb0 = (lds_cptr)k_lds0, kb1 = (lds_cptr)k_lds1;
@@ -471,7 +440,7 @@ __global__ void __launch_bounds__(kThreads, 512 / kThreads) chunk_kernel(AttnArg
       __syncthreads();
       if (ti + 1 < n_tiles) { PA_CK_DMA(kt + KT, k_lds1, v_lds1) }
       if (kt <= w_qpos_hi)
-        chunk_tile<D, G>(st, kb0, vb0, qf, koff, voff, voff8, kt, qpos, k1, w_qpos_lo, lane);
+        chunk_tile<D, G>(st, kb0, vb0, qf, koff, voff, voff8, kt, qpos, k1, w_qpos_lo, sl, lane);
     }
     if (ti + 1 < n_tiles) {  // odd tile: buffer 1
       const int kt = k0 + (ti + 1) * KT;
@@ -479,7 +448,7 @@ __global__ void __launch_bounds__(kThreads, 512 / kThreads) chunk_kernel(AttnArg
       __syncthreads();
       if (ti + 2 < n_tiles) { PA_CK_DMA(kt + KT, k_lds0, v_lds0) }
       if (kt <= w_qpos_hi)
-        chunk_tile<D, G>(st, kb1, vb1, qf, koff, voff, voff8, kt, qpos, k1, w_qpos_lo, lane);
+        chunk_tile<D, G>(st, kb1, vb1, qf, koff, voff, voff8, kt, qpos, k1, w_qpos_lo, sl, lane);
     }
   }
 #undef PA_CK_DMA
