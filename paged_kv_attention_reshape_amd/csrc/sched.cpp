@@ -222,6 +222,12 @@ struct pa_sched {
     return n;
   }
 
+  // a finished or cancelled request keeps only its id and counters
+  static void drop_storage(Req& r) {
+    std::vector<uint64_t>().swap(r.keys);
+    std::vector<int32_t>().swap(r.blocks);
+  }
+
   void preempt(int32_t slot) {
     Req& v = reqs[(size_t)slot];
     const int64_t held = v.num_computed;
@@ -365,6 +371,7 @@ struct pa_sched {
           if (r.generated >= r.output_len) {
             r.status = kFinished;
             release_all(r);
+            drop_storage(r);
             ++m.finished;
             done.push_back(r.id);
             continue;
@@ -638,6 +645,7 @@ pa_status pa_sched_cancel(pa_sched* s, int64_t request_id) {
                       s->copies.end());
   }
   r.status = kCancelled;
+  pa_sched::drop_storage(r);
   ++s->m.cancelled;
   return PA_OK;
 }
