@@ -146,17 +146,24 @@ def cpu_baseline(spec, d, budget_s):
                   f"({ck_s:.1f} s) of the same step; fp64 numpy oracle: slot mapping, write, gather, attention",
         "chunk_gflops": round(ck_flops / ck_s / 1e9, 3) if ck_s > 0 else None,
         "scheduler_us_per_step": scheduler_timing(product=False)["us_per_step"],
+        "scheduler_shared_prefix_us_per_step": scheduler_timing(product=False, shared=True)["us_per_step"],
         "host_cpus": len(os.sched_getaffinity(0)),
     }
 
 
-def scheduler_timing(product: bool, steps: int = 200):
+SHARED_TRACE = dict(shared_prompts=8, shared_len=1024, shared_frac=0.8)
+
+
+def scheduler_timing(product: bool, steps: int = 200, shared: bool = False):
     """Host time per planned step of the serving trace (2048 requests, 16384
     blocks of 16, budget 8192, chunk 512): schedule + copy of the step's
-    arrays + commit.  product=False times the reference scheduler (only the
+    arrays + commit.  shared=True gives 80 % of the requests one of 8 system
+    prompts of 1024 tokens, with prefix keys, so admissions attach cached
+    blocks.  product=False times the reference scheduler (only the
     CPU-baseline leg does that)."""
     from workloads import serving_trace as st
-    cfg = st.TraceConfig(steps=steps)
+    cfg = st.TraceConfig(steps=steps, **(SHARED_TRACE if shared else {}))
+    keys = st.block_keys(cfg)
     toks = 0
     if product:
         # the C ABI directly, with preallocated output arrays (what a serving
@@ -167,7 +174,7 @@ def scheduler_timing(product: bool, steps: int = 200):
         from paged_kv_attention_reshape_amd import _sched
         s = pa.Scheduler(**st.scheduler_args(cfg))
         for rid, p, o in st.requests(cfg):
-            s.add_request(rid, p, o)
+            s.add_request(rid, p, o, keys.get(rid, ()))
         L = pa.sched_lib()
         cap, M = cfg.max_num_seqs, -(-(cfg.prompt_max + 4096) // cfg.block_size)
         ids = np.zeros(cap, np.int64)
@@ -198,7 +205,7 @@ def scheduler_timing(product: bool, steps: int = 200):
         from oracle.sched_oracle import Scheduler as RefScheduler
         s = RefScheduler(**st.scheduler_args(cfg))
         for rid, p, o in st.requests(cfg):
-            s.add_request(rid, p, o)
+            s.add_request(rid, p, o, keys.get(rid, ()))
         t0 = time.perf_counter()
         for _ in range(cfg.steps):
             plan = s.schedule()
@@ -206,8 +213,13 @@ def scheduler_timing(product: bool, steps: int = 200):
             s.commit()
         dt = time.perf_counter() - t0
     m = s.metrics()
-    return {"us_per_step": round(dt / cfg.steps * 1e6, 1), "steps": cfg.steps,
-            "scheduled_tokens": toks, "preemptions": m["preemptions"]}
+    out = {"us_per_step": round(dt / cfg.steps * 1e6, 1), "steps": cfg.steps,
+           "scheduled_tokens": toks, "preemptions": m["preemptions"]}
+    if shared:
+        out.update({"prefix_hit_tokens": m["prefix_hit_tokens"], "evictions": m["evictions"],
+                    "cow_copies": m["cow_copies"], "cached_blocks": m["cached_blocks"],
+                    "trace": "as above, 80 % of requests start with one of 8 shared 1024-token system prompts"})
+    return out
 
 
 def swap_measurement(dev, reps: int = 10):
@@ -426,6 +438,7 @@ def main():
     sched_t = scheduler_timing(product=True)
     sched_t["trace"] = "2048 requests at step 0, 200 steps, 16384 blocks of 16, budget 8192, chunk 512"
     sched_t["includes"] = "pa_sched_schedule + pa_sched_plan_copy (block table rows at the step's own width) + pa_sched_commit, through ctypes"
+    sched_t["shared_prefix"] = scheduler_timing(product=True, shared=True)
 
     dec_bytes = spec.decode_bytes()
     chunk_fl = spec.chunk_flops()
