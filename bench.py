@@ -379,6 +379,35 @@ def main():
     total_ms = t_begin.elapsed_time(t_end)
     ms_step = total_ms / args.steps
 
+    # the same step captured once in a HIP graph and replayed K times (the
+    # library allocates, memsets and synchronises nothing, so a step of fixed
+    # sizes captures whole); only when one pool copy is in use
+    graph = None
+    if n_copies == 1:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(2):
+            g.replay()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        g0.record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph = {"ms_per_step": round(g0.elapsed_time(g1) / args.steps, 4),
+                 "note": "the same step (slot mapping, write_kv, attention) captured once in a HIP graph "
+                         "and replayed back to back"}
+
     # per-kernel breakdown: the same K steps again with events between the
     # launches (the events add a little time between kernels, not inside them)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
@@ -495,6 +524,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(chunk_tf / MFMA_BF16_PEAK_TFLOPS, 4),
         },
+        "graph_replay": graph,
         "rope_write_kv": rope,
         "scheduler": sched_t,
         "swap_roundtrip": swap,
