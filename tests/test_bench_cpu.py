@@ -37,11 +37,6 @@ def test_traffic_only_for_the_measured_source(tmp_path, monkeypatch):
     assert bench.load_traffic("rowwise") is None
 
 
-def test_committed_counters_match_the_current_decode_kernel():
-    """The committed HBM byte counters belong to the committed split-K source."""
-    assert bench.load_traffic("rowwise") is not None
-
-
 @pytest.mark.parametrize("shared", [False, True])
 def test_scheduler_timing_legs_agree(shared):
     pytest.importorskip("numpy")
