@@ -197,6 +197,25 @@ def test_forced_partition_sizes(split, monkeypatch):
     say(f"split {split} err {err:.2e}")
 
 
+@pytest.mark.parametrize("case", [
+    # (query lens, computed counts, Hq, Hkv, D, B): long chunks that span many
+    # key segments and q-tiles, beside short decodes
+    ([16384, 1, 4096], [0, 9000, 12288], 32, 8, 128, 16),
+    ([8192, 2048, 1], [8192, 0, 30000], 64, 8, 128, 32),
+], ids=["16k-prompt+4k-after-12k", "g8-8k-after-8k"])
+def test_long_chunks_sampled(case):
+    """Chunks of thousands of tokens (many segments merged by log-sum-exp,
+    long q-tile lists, large workspaces): 40 sampled rows of every request,
+    including the first and last, against the oracle; caches bit-exact."""
+    ql, comp, Hq, Hkv, D, B = case
+    spec = _small("bf16", Hq, Hkv, D, B, ql, comp, seed=23 + len(ql), pool_factor=1.1)
+    d, out, _ = run_step(spec, pa)
+    torch.cuda.synchronize()
+    err = check_requests(spec, out, d["key_cache"], d["value_cache"], range(spec.R), rows_per_req=40,
+                         what=f"long {ql}")
+    say(f"long chunks {ql} after {comp}: err {err:.2e}")
+
+
 def test_chunked_prefill_equals_full_prefill_on_gpu():
     """A 300-token prompt run as five chunks of 64 (each chunk a step that
     reads the cache the earlier chunks wrote) matches the one-shot prefill."""
