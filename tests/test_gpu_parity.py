@@ -216,6 +216,18 @@ def test_long_chunks_sampled(case):
     say(f"long chunks {ql} after {comp}: err {err:.2e}")
 
 
+def test_fp32_prefill_rows_on_the_split_k_path():
+    """fp32 chunk rows run on the split-K kernel (one row per wavefront and
+    key partition, merged by log-sum-exp): a 700-token prompt, a 300-token
+    chunk after 1500 tokens and decodes, every row against the oracle at the
+    fp32 tolerance."""
+    spec = _small("f32", 32, 8, 128, 16, [700, 1, 300, 1], [0, 2000, 1500, 33], seed=41)
+    d, out, _ = run_step(spec, pa)
+    torch.cuda.synchronize()
+    err = check_requests(spec, out, d["key_cache"], d["value_cache"], range(spec.R), what="fp32 prefill")
+    say(f"fp32 prefill rows err {err:.2e}")
+
+
 def test_chunked_prefill_equals_full_prefill_on_gpu():
     """A 300-token prompt run as five chunks of 64 (each chunk a step that
     reads the cache the earlier chunks wrote) matches the one-shot prefill."""
