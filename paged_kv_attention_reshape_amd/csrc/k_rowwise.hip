@@ -500,24 +500,59 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnArgs a) {
 }  // namespace
 
 // Query rows go to LDS when that lowers the register footprint enough to
-// matter (large GQA groups); PA_DECODE_QLDS=0/1 overrides for measurement.
-static bool use_qlds(const AttnArgs& a) {
+// matter (GQA groups of 4 and more: three waves per SIMD instead of two, so
+// more K/V loads in flight); PA_DECODE_QLDS=0/1 overrides for measurement.
+static bool use_qlds(int32_t G) {
   const char* e = getenv("PA_DECODE_QLDS");
   if (e != nullptr && *e) return atoi(e) != 0;
-  return (a.Hq / a.Hkv) >= 8;
+  return G >= 4;
+}
+
+static hipError_t rowwise_kernel_for(bool bf16, int32_t D, int32_t G, const void** out) {
+  AttnArgs a{};
+  a.bf16 = bf16;
+  a.D = D;
+  a.Hkv = 1;
+  a.Hq = G;
+  const void* kern = nullptr;
+  if (use_qlds(G)) {
+    PA_SELECT_Q(rowwise_kernel, true)
+  } else {
+    PA_SELECT_Q(rowwise_kernel, false)
+  }
+  *out = kern;
+  return hipSuccess;
 }
 
 hipError_t launch_rowwise(const AttnArgs& a, hipStream_t s) {
   if (a.ps.n_rw == 0) return hipSuccess;
   const void* kern = nullptr;
-  if (use_qlds(a)) {
-    PA_SELECT_Q(rowwise_kernel, true)
-  } else {
-    PA_SELECT_Q(rowwise_kernel, false)
-  }
+  const hipError_t e = rowwise_kernel_for(a.bf16, a.D, a.Hq / a.Hkv, &kern);
+  if (e != hipSuccess) return e;
   AttnArgs args = a;
   void* params[] = {&args};
   return hipLaunchKernel(kern, dim3(a.ps.n_rw, a.Hkv), dim3(64), params, 0, s);
+}
+
+int64_t rowwise_resident_waves(bool bf16, int32_t D, int32_t G) {
+  // the split-K kernel's wavefronts the current device holds at once
+  // (occupancy per compute unit x compute units), cached per configuration
+  static thread_local int64_t cache[2][2][9][2] = {};
+  const int qi = use_qlds(G) ? 1 : 0;
+  const int di = D == 128 ? 1 : 0;
+  if (G < 1 || G > 8) return 0;
+  int64_t& c = cache[bf16 ? 1 : 0][di][G][qi];
+  if (c == 0) {
+    const void* kern = nullptr;
+    int dev = 0, cus = 0, per_cu = 0;
+    if (rowwise_kernel_for(bf16, D, G, &kern) != hipSuccess || hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64, 0) != hipSuccess || cus <= 0 ||
+        per_cu <= 0)
+      return 0;
+    c = (int64_t)cus * per_cu;
+  }
+  return c;
 }
 
 hipError_t launch_merge(const AttnArgs& a, hipStream_t s) {

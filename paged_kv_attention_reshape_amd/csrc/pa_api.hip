@@ -63,10 +63,31 @@ pa_status check_geometry(int32_t Hq, int32_t Hkv, int32_t D, int32_t B, int32_t 
 
 int64_t gcd64(int64_t a, int64_t b) { return b == 0 ? a : gcd64(b, a % b); }
 
+// Row-wise wavefronts of a step (all kv heads) at partition length S.
+int64_t rowwise_waves(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R, int32_t M,
+                      int32_t Hkv, pa::PlanShape ps, int32_t S) {
+  ps.S = S;
+  int64_t n = 0;
+  for (int32_t r = 0; r < R; ++r) {
+    int32_t q = h_qsl[r + 1] - h_qsl[r];
+    int32_t L = h_seq_lens[r];
+    pa::sanitize(q, L, M, ps.B);
+    if (q > 0 && pa::goes_rowwise(q, ps)) n += pa::request_counts(q, L, ps).rw;
+  }
+  return n * Hkv;
+}
+
 // Row-wise partition length: a power-of-two multiple of lcm(64, B), at most
-// 64 blocks (one block id per lane of the wavefront) and 1024 keys, chosen so
-// that the grid holds roughly 32 wavefronts per compute unit.
-int32_t choose_split(int64_t rowwise_keys, int32_t Hkv, int32_t B) {
+// 64 blocks (one block id per lane of the wavefront) and 1024 keys.  When the
+// whole split-K grid fits on the device at once at some length (resident =
+// wavefronts the device holds for this kernel, 0 if unknown), the shortest
+// such length is taken: one round of waves, each as short as that allows.
+// Otherwise the length is chosen so that the grid holds roughly 32
+// wavefronts per compute unit (many rounds; the order of the items keeps
+// the tail short).
+int32_t choose_split(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R, int32_t M,
+                     int64_t rowwise_keys, int32_t Hkv, int64_t resident, const pa::PlanShape& ps) {
+  const int32_t B = ps.B;
   const int64_t unit = 64 / gcd64(64, B) * B;
   const int64_t cap = std::max<int64_t>(unit, (int64_t)64 * B);
   const int forced = env_int("PA_SPLIT_TOKENS", 0);
@@ -74,10 +95,19 @@ int32_t choose_split(int64_t rowwise_keys, int32_t Hkv, int32_t B) {
     int64_t s = (forced + unit - 1) / unit * unit;
     return (int32_t)std::min(s, cap / unit * unit);
   }
+  int64_t top = unit;
+  while (top * 2 <= cap && top * 2 <= 1024) top *= 2;
+  if (resident > 0 && rowwise_keys > 0 && env_int("PA_SPLIT_ONE_ROUND", 1) != 0 &&
+      rowwise_waves(h_qsl, h_seq_lens, R, M, Hkv, ps, (int32_t)top) <= resident) {
+    int64_t s = top;
+    while (s / 2 >= unit && rowwise_waves(h_qsl, h_seq_lens, R, M, Hkv, ps, (int32_t)(s / 2)) <= resident)
+      s /= 2;
+    return (int32_t)s;
+  }
   const int64_t target_waves = 256 * 32;
   const int64_t want = rowwise_keys * Hkv / target_waves;
   int64_t s = unit;
-  while (s < want && s * 2 <= cap && s * 2 <= 1024) s *= 2;
+  while (s < want && s * 2 <= top) s *= 2;
   return (int32_t)s;
 }
 
@@ -144,7 +174,8 @@ pa_status make_plan(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R, 
       rowwise_keys += q * (c + 1) + (int64_t)q * (q - 1) / 2;
     }
   }
-  ps.S = choose_split(rowwise_keys, Hkv, B);
+  const int64_t resident = rowwise_keys > 0 ? pa::rowwise_resident_waves(bf16, D, G) : 0;
+  ps.S = choose_split(h_qsl, h_seq_lens, R, M, rowwise_keys, Hkv, resident, ps);
   ps.SEG = choose_segment(h_qsl, h_seq_lens, R, M, B, Hkv, ps);
   int64_t n_rw = 0, n_ck = 0, n_mg = 0, n_parts = 0;
   for (int32_t r = 0; r < R; ++r) {

@@ -198,6 +198,9 @@ struct RopeArgs {
 hipError_t launch_rope_write_kv(const RopeArgs& a, bool bf16, int32_t D, bool neox, hipStream_t s);
 
 hipError_t launch_rowwise(const AttnArgs& a, hipStream_t s);
+// Split-K wavefronts the current device holds at once for this configuration
+// (0 when the device cannot be queried).
+int64_t rowwise_resident_waves(bool bf16, int32_t D, int32_t G);
 hipError_t launch_chunk(const AttnArgs& a, hipStream_t s);
 hipError_t launch_merge(const AttnArgs& a, hipStream_t s);
 bool chunk_kernel_supports(bool bf16, int32_t D, int32_t G, int32_t B);
