@@ -46,7 +46,7 @@ def source_hash(rel: str) -> str:
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="c3", choices=["c2", "c3", "c4"])
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -417,10 +417,17 @@ def main():
 
     names = ["slot_mapping", "write_kv", "launch_gap", "plan", "rowwise", "chunk", "merge"]
     acc = {k: 0.0 for k in names}
+    per_step = {k: [] for k in ("rowwise", "chunk", "merge", "step")}
     for e in ev:
         for k, (a, b) in zip(names, [(0, 1), (1, 2), (2, 3), (3, 4), (4, 5), (5, 6), (6, 7)]):
-            acc[k] += e[a].elapsed_time(e[b])
+            t = e[a].elapsed_time(e[b])
+            acc[k] += t
+            if k in per_step:
+                per_step[k].append(1e3 * t)
+        per_step["step"].append(1e3 * e[0].elapsed_time(e[7]))
     us = {k: 1e3 * v / args.steps for k, v in acc.items()}
+    us_pct = {k: [round(float(x), 2) for x in np.percentile(v, [10, 50, 90])]
+              for k, v in per_step.items()}
 
     # fused rotary embedding + cache write on the same step's tokens (timed on
     # its own: Q rotated in place on a copy, K/V into the first pool copy)
@@ -503,6 +510,7 @@ def main():
         "chunk_frac_mfma": round(chunk_tf / MFMA_BF16_PEAK_TFLOPS, 4),
         "tokens_per_s": round(spec.T / (ms_step * 1e-3), 1),
         "kernel_us": {k: round(v, 2) for k, v in us.items()},
+        "kernel_us_p10_p50_p90": us_pct,
         "decode_bytes_per_step": dec_bytes,
         "chunk_flops_per_step": chunk_fl,
         "write_kv_gbs": round(spec.write_bytes() / (us["write_kv"] * 1e-6) / 1e9, 1) if us["write_kv"] > 0 else None,
