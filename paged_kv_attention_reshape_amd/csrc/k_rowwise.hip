@@ -520,7 +520,23 @@ static bool use_qlds(int32_t G) {
   return G >= 4;
 }
 
+// bf16 caches with GQA groups of 8 go to the matrix-core kernel: there the
+// vector kernel's v_dot2 loops cost about as much time as the K/V stream
+// (measured: 5.2 -> 5.6 TB/s on 16 x 32K + 240 short contexts).  With groups
+// of 4 the vector kernel, at three waves per SIMD, is as fast or faster.
+// PA_DECODE_MFMA=0/1 overrides (groups of 4 and 8) for measurement.
+static bool use_mfma(bool bf16, int32_t D, int32_t G) {
+  if (!bf16 || rowwise_mfma_kernel_for(D, G) == nullptr) return false;
+  const char* e = getenv("PA_DECODE_MFMA");
+  if (e != nullptr && *e) return atoi(e) != 0;
+  return G >= 8;
+}
+
 static hipError_t rowwise_kernel_for(bool bf16, int32_t D, int32_t G, const void** out) {
+  if (use_mfma(bf16, D, G)) {
+    *out = rowwise_mfma_kernel_for(D, G);
+    return hipSuccess;
+  }
   AttnArgs a{};
   a.bf16 = bf16;
   a.D = D;
@@ -549,8 +565,8 @@ hipError_t launch_rowwise(const AttnArgs& a, hipStream_t s) {
 int64_t rowwise_resident_waves(bool bf16, int32_t D, int32_t G) {
   // the split-K kernel's wavefronts the current device holds at once
   // (occupancy per compute unit x compute units), cached per configuration
-  static thread_local int64_t cache[2][2][9][2] = {};
-  const int qi = use_qlds(G) ? 1 : 0;
+  static thread_local int64_t cache[2][2][9][3] = {};
+  const int qi = use_mfma(bf16, D, G) ? 2 : (use_qlds(G) ? 1 : 0);
   const int di = D == 128 ? 1 : 0;
   if (G < 1 || G > 8) return 0;
   int64_t& c = cache[bf16 ? 1 : 0][di][G][qi];

@@ -1,0 +1,327 @@
+// Split-K row-wise attention on the matrix cores, for bf16 caches and GQA
+// groups of 4 or 8 query heads per kv head.
+//
+// Method: "AI Infra入门干货总结：大模型是如何高效推理的", section "Attention
+// Module": the G query heads that share a kv head read one K/V stream through
+// the block table; online softmax (running max and sum) fuses q.k, softmax
+// and p.v; section "总结": Flash-Decoding splits the keys of a row into
+// partitions that a log-sum-exp pass merges.  The plan gives each work item
+// one query row and its key range [kb, ke) (the causal limit of "Chunked
+// Prefill 与 Preemption", equation M_{i,j}, is already in ke).
+//
+// Why matrix cores for a bandwidth-bound pass: with 8 query heads per kv head
+// the q.k and p.v dot products of the vector-ALU kernel (v_dot2, 16 tokens x
+// G heads per lane group) take about as long as streaming the keys and
+// values, so the kernel runs below the HBM rate.  Here every 32-key tile is
+// 16 MFMAs (v_mfma_f32_16x16x32_bf16, query heads padded to 16 columns) and
+// about 40 vector instructions of softmax per wave, far below the time the
+// tile's 16 KB take to arrive.
+//
+// One wavefront per (row, key partition, kv head); lane l = (grp = l / 16,
+// li = l % 16):
+//   S^T = K Q^T : A = K rows of the tile straight from global memory (lane
+//                 holds key li of a 16-key half, d 32s + 8grp .. +7), B = the
+//                 query heads (column li, zero for li >= G) held in registers;
+//                 the accumulator gives lane l the scores of head li for keys
+//                 4grp + r and 16 + 4grp + r, r < 4.
+//   softmax     : per head over those 8 keys and the 4 lane groups (two
+//                 cross-group shuffles); running max raised lazily (only past
+//                 a 2^8 slack), probabilities rounded to bf16 in place.
+//   O^T = V^T P^T: B = the lane's own 8 probabilities (the MFMA k-slot order
+//                 is permuted to the score layout, so P never moves), A = V^T
+//                 by ds_read_b64_tr_b16 transposed reads of the V tile, which
+//                 the wave writes into an XOR-swizzled LDS buffer (1 KB per
+//                 ds_write_b128 instruction).  O^T keeps head li per lane, so
+//                 the rescale is lane-local.
+// K and V are streamed into registers with the nontemporal hint (each byte is
+// read once per step); the next tile's loads are issued right after the
+// current tile's q.k, so they are in flight during its softmax and p.v.  V
+// goes through registers rather than a global->LDS DMA: with only ordinary
+// loads in flight the compiler's vmcnt waits stay exact (mixing in LDS DMA
+// makes it wait for every outstanding load).  Partial results use the same
+// layout as the vector kernel's, so the merge pass is shared.
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef const __attribute__((address_space(3))) char* lds_cptr;
+
+constexpr int KT = 32;  // keys per tile
+constexpr float kNegInf = -__builtin_huge_valf();
+// lazy rescale threshold (log2 units): probabilities stay below 2^8
+constexpr float kSlack = 8.f;
+
+template <int D>
+struct MGeo {
+  static constexpr int ROWB = D * 2;              // bytes of one head row
+  static constexpr int CPR = ROWB / 16;           // 16-byte chunks per row
+  static constexpr int KSTEPS = D / 32;           // k-steps of q.k
+  static constexpr int NB = D / 16;               // 16-wide d blocks of O^T
+  static constexpr int TILE_BYTES = KT * ROWB;    // one V tile
+  static constexpr int VL = TILE_BYTES / 1024;    // 16-byte V loads per lane per tile
+  static constexpr int RPV = 1024 / ROWB;         // V rows per wave load instruction
+};
+
+// V tile swizzle: 16-byte chunk c of row k sits at chunk c ^ vswz(k).  A
+// transposed read covers 16 rows x 32 bytes (chunks 2n, 2n+1); with 256-byte
+// rows vswz = 2 (k & 7) spreads rows k, k + 8 over all 16 bank groups twice,
+// with 128-byte rows (two rows per 256-byte bank row) vswz = 2 ((k >> 1) & 3).
+template <int CPR>
+__device__ __forceinline__ int vswz(int k) {
+  if constexpr (CPR == 16) return (k & 7) << 1;
+  else return ((k >> 1) & 3) << 1;
+}
+
+__device__ __forceinline__ u32x4_t load_once(const char* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const f32x2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
+
+__device__ __forceinline__ float xor32(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? p[0] : p[1]);
+}
+
+__device__ __forceinline__ float xor16(float x) { return __shfl_xor(x, 16, 64); }
+
+template <int D, int G>
+__global__ void __launch_bounds__(64, 2) rowwise_mfma_kernel(AttnArgs a) {
+  using Gm = MGeo<D>;
+  constexpr int ROWB = Gm::ROWB, CPR = Gm::CPR, KSTEPS = Gm::KSTEPS, NB = Gm::NB;
+  constexpr int TILE_BYTES = Gm::TILE_BYTES, VL = Gm::VL, RPV = Gm::RPV;
+  static_assert(G >= 1 && G <= 16, "query heads per kv head must fit 16 MFMA columns");
+
+  // one V tile; a wave's LDS accesses execute in order, so the next tile's
+  // writes cannot overtake this tile's reads
+  __shared__ __attribute__((aligned(1024))) char v_lds[TILE_BYTES];
+
+  const int lane = threadIdx.x;
+  const int li = lane & 15, grp = lane >> 4;
+  const int4 it = a.items_rw[blockIdx.x];
+  const int r = it.x;
+  if (r < 0 || r >= a.R) return;
+  const int g = blockIdx.y;
+  const int t = it.y;
+  const int kb = it.z;
+  const int ke = it.w & 0x7FFFFFFF;
+  const bool direct = (it.w & kDirect) != 0;
+  const int slot = direct ? 0 : a.rw_slot[blockIdx.x];
+  if (ke <= kb) return;
+
+  // Q^T fragments (B operand of S^T = K Q^T): column li = query head g*G + li
+  u32x4_t qf[KSTEPS];
+  {
+    const int hh = li < G ? li : G - 1;
+    const char* qrow = static_cast<const char*>(a.query) + ((int64_t)t * a.Hq + g * G + hh) * ROWB + grp * 16;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
+      qf[s] = li < G ? *reinterpret_cast<const u32x4_t*>(qrow + s * 64) : u32x4_t{0, 0, 0, 0};
+  }
+
+  // physical block ids of the partition: lane i holds block kb / B + i
+  const int blk0 = kb / a.B;
+  const int nblk = (ke - 1) / a.B - blk0 + 1;
+  int myblk = 0;
+  if (lane < nblk) {
+    myblk = a.block_table[(int64_t)r * a.M + blk0 + lane];
+    myblk = myblk < 0 ? 0 : (myblk >= a.num_blocks ? a.num_blocks - 1 : myblk);
+  }
+  const char* kcache = static_cast<const char*>(a.kcache) + (int64_t)g * ROWB;
+  const char* vcache = static_cast<const char*>(a.vcache) + (int64_t)g * ROWB;
+  const uint32_t slot_stride = (uint32_t)a.Hkv * ROWB;
+
+  // byte offset (from the head's base) of key `key` of the partition, which
+  // lies in physical block `blk`; `key` must lie in [kb, ke)
+  auto key_off = [&](int key, int blk) -> int64_t {
+    return ((int64_t)blk * a.B + key % a.B) * slot_stride;
+  };
+  // lane-constant offsets within a 16-row half of a full tile
+  uint32_t koff[KSTEPS];
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) koff[s] = li * slot_stride + (4 * s + grp) * 16;
+  // V load i of a lane: the 16 bytes that belong at LDS byte 1024 i + 16 lane
+  // (physical row RPV i + lane / CPR, physical chunk lane % CPR, which holds
+  // logical chunk (lane % CPR) ^ vswz(row))
+  uint32_t vgoff[VL];
+#pragma unroll
+  for (int i = 0; i < VL; ++i) {
+    const int pr = RPV * i + lane / CPR;
+    const int lc = (lane % CPR) ^ vswz<CPR>(pr);
+    vgoff[i] = (pr & 15) * slot_stride + lc * 16;
+  }
+  // transposed-read offsets: rows 4 grp + li / 4 (and + 16), d 16n + 4 (li % 4)
+  int voff[NB];
+  {
+    const int row = 4 * grp + (li >> 2);
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      const int d0 = 16 * n + 4 * (li & 3);
+      voff[n] = row * ROWB + (((d0 >> 3) ^ vswz<CPR>(row)) << 4) + (d0 & 7) * 2;
+    }
+  }
+
+  // K rows (A operand: key li of half h) and V chunks of a tile into
+  // registers.  A full tile uses one scalar base per 16-key half (a half
+  // never crosses a block: B and the tile start are multiples of 16); the
+  // last, partial tile clamps its rows to key ke - 1 (finite data; those keys
+  // are masked and get zero probability).  Both paths issue the same loads.
+  auto load_tile = [&](int start, u32x4_t (&kr)[2][KSTEPS], u32x4_t (&vr)[VL]) {
+    if (start + KT <= ke) {
+      const int64_t base0 = key_off(start, __builtin_amdgcn_readlane(myblk, start / a.B - blk0));
+      const int64_t base1 = key_off(start + 16, __builtin_amdgcn_readlane(myblk, (start + 16) / a.B - blk0));
+#pragma unroll
+      for (int k = 0; k < KSTEPS; ++k) {
+        kr[0][k] = load_once(kcache + base0 + koff[k]);
+        kr[1][k] = load_once(kcache + base1 + koff[k]);
+      }
+#pragma unroll
+      for (int i = 0; i < VL; ++i) vr[i] = load_once(vcache + ((RPV * i < 16) ? base0 : base1) + vgoff[i]);
+    } else {
+      auto row_off = [&](int row) -> int64_t {
+        const int key = min(start + row, ke - 1);
+        const int blk = __shfl(myblk, key / a.B - blk0, 64);
+        return key_off(key, blk);
+      };
+      const int64_t o0 = row_off(li), o1 = row_off(16 + li);
+#pragma unroll
+      for (int k = 0; k < KSTEPS; ++k) {
+        kr[0][k] = load_once(kcache + o0 + (4 * k + grp) * 16);
+        kr[1][k] = load_once(kcache + o1 + (4 * k + grp) * 16);
+      }
+#pragma unroll
+      for (int i = 0; i < VL; ++i) {
+        const int pr = RPV * i + lane / CPR;
+        const int lc = (lane % CPR) ^ vswz<CPR>(pr);
+        vr[i] = load_once(vcache + row_off(pr) + lc * 16);
+      }
+    }
+  };
+
+  const float sl = a.scale_log2;
+  float m_run = kNegInf, l_run = 0.f;
+  f32x4_t o[NB];
+#pragma unroll
+  for (int n = 0; n < NB; ++n) o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int n_tiles = (ke - kb + KT - 1) / KT;
+  u32x4_t kr[2][KSTEPS], vr[VL];
+  load_tile(kb, kr, vr);
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    const int start = kb + tile * KT;
+    // V tile into LDS (swizzled; 1 KB per instruction, conflict-free)
+#pragma unroll
+    for (int i = 0; i < VL; ++i)
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(
+          (__attribute__((address_space(3))) char*)v_lds + i * 1024 + lane * 16) = vr[i];
+    // S^T = K Q^T
+    f32x4_t s[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      s[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < KSTEPS; ++k)
+        s[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[h][k]),
+                                                       __builtin_bit_cast(bf16x8_t, qf[k]), s[h], 0, 0, 0);
+    }
+    // next tile's loads, in flight during this tile's softmax and p.v
+    if (tile + 1 < n_tiles) load_tile(start + KT, kr, vr);
+    if (start + KT > ke) {
+      // element r of half h is key 16h + 4grp + r of the tile
+      const int lim = ke - start - 4 * grp;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[h][e] = (16 * h + e) < lim ? s[h][e] : kNegInf;
+    }
+    float mx = max3f(max3f(s[0][0], s[0][1], s[0][2]), max3f(s[0][3], s[1][0], s[1][1]),
+                     fmaxf(s[1][2], s[1][3]));
+    mx = fmaxf(mx, xor16(mx));
+    mx = fmaxf(mx, xor32(mx)) * sl;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kSlack)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int n = 0; n < NB; ++n) o[n] *= alpha;
+    }
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
+    uint32_t pk[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; e += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[h][e], sl, -m_use));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[h][e + 1], sl, -m_use));
+        pk[2 * h + (e >> 1)] = pack_bf16(p0, p1);
+        // the sum takes the bf16-rounded probabilities that p.v uses
+        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[2 * h + (e >> 1)]),
+                                               __builtin_bit_cast(bf16x2_t, 0x3F803F80u), psum, false);
+      }
+    l_run += psum;
+    // O^T += V^T P^T
+    const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
+    lds_cptr vb = (lds_cptr)v_lds;
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vb + voff[n]));
+      const s16x4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vb + voff[n] + 16 * ROWB));
+      const s16x8_t vv = __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
+      o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vv), pf, o[n], 0, 0, 0);
+    }
+  }
+
+  // ---- finish ------------------------------------------------------------------
+  float l_tot = l_run + xor16(l_run);
+  l_tot += xor32(l_tot);
+  if (li >= G) return;
+  const int hq = g * G + li;
+  if (direct) {
+    const float inv = 1.f / l_tot;
+    char* orow = static_cast<char*>(a.out) + ((int64_t)t * a.Hq + hq) * ROWB;
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      const int d = 16 * n + 4 * grp;
+      *reinterpret_cast<uint2*>(orow + d * 2) =
+          make_uint2(pack_bf16(o[n][0] * inv, o[n][1] * inv), pack_bf16(o[n][2] * inv, o[n][3] * inv));
+    }
+  } else {
+    float* op = a.o_part + ((int64_t)slot * a.Hq + hq) * D;
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+      *reinterpret_cast<float4*>(op + 16 * n + 4 * grp) = make_float4(o[n][0], o[n][1], o[n][2], o[n][3]);
+    if (grp == 0) {
+      float* mp = a.ml_part + ((int64_t)slot * a.Hq + hq) * 2;
+      mp[0] = m_run;
+      mp[1] = l_tot;
+    }
+  }
+}
+
+}  // namespace
+
+const void* rowwise_mfma_kernel_for(int32_t D, int32_t G) {
+  if (D == 64 && G == 4) return (const void*)rowwise_mfma_kernel<64, 4>;
+  if (D == 64 && G == 8) return (const void*)rowwise_mfma_kernel<64, 8>;
+  if (D == 128 && G == 4) return (const void*)rowwise_mfma_kernel<128, 4>;
+  if (D == 128 && G == 8) return (const void*)rowwise_mfma_kernel<128, 8>;
+  return nullptr;
+}
+
+}  // namespace pa

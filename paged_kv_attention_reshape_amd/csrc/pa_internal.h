@@ -198,6 +198,9 @@ struct RopeArgs {
 hipError_t launch_rope_write_kv(const RopeArgs& a, bool bf16, int32_t D, bool neox, hipStream_t s);
 
 hipError_t launch_rowwise(const AttnArgs& a, hipStream_t s);
+// Matrix-core split-K kernel for bf16 caches (same items, partials and
+// launch shape as the vector kernel); nullptr where it has no instance.
+const void* rowwise_mfma_kernel_for(int32_t D, int32_t G);
 // Split-K wavefronts the current device holds at once for this configuration
 // (0 when the device cannot be queried).
 int64_t rowwise_resident_waves(bool bf16, int32_t D, int32_t G);
