@@ -33,14 +33,19 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 MALL_ROTATE_BYTES = 1 << 30      # footprint rotated through when a step's pools are small
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak, published
 KERNEL_SOURCES = {
-    "rowwise": "paged_kv_attention_reshape_amd/csrc/k_rowwise.hip",
-    "chunk": "paged_kv_attention_reshape_amd/csrc/k_chunk.hip",
+    "rowwise": ["paged_kv_attention_reshape_amd/csrc/k_rowwise.hip",
+                "paged_kv_attention_reshape_amd/csrc/k_rowwise_mfma.hip"],
+    "chunk": ["paged_kv_attention_reshape_amd/csrc/k_chunk.hip"],
 }
 
 
-def source_hash(rel: str) -> str:
-    with open(os.path.join(ROOT, rel), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(rels) -> str:
+    """sha256 prefix over the concatenated source files (one path or a list)."""
+    h = hashlib.sha256()
+    for rel in ([rels] if isinstance(rels, str) else rels):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def parse():

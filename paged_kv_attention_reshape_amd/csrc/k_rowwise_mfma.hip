@@ -56,6 +56,7 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef const __attribute__((address_space(3))) char* lds_cptr;
 
 constexpr int KT = 32;  // keys per tile
+constexpr int kLdsPerWave = 20 * 1024;
 constexpr float kNegInf = -__builtin_huge_valf();
 // lazy rescale threshold (log2 units): probabilities stay below 2^8
 constexpr float kSlack = 8.f;
@@ -106,9 +107,13 @@ __global__ void __launch_bounds__(64, 2) rowwise_mfma_kernel(AttnArgs a) {
   constexpr int TILE_BYTES = Gm::TILE_BYTES, VL = Gm::VL, RPV = Gm::RPV;
   static_assert(G >= 1 && G <= 16, "query heads per kv head must fit 16 MFMA columns");
 
-  // one V tile; a wave's LDS accesses execute in order, so the next tile's
-  // writes cannot overtake this tile's reads
-  __shared__ __attribute__((aligned(1024))) char v_lds[TILE_BYTES];
+  // one V tile (the first TILE_BYTES); a wave's LDS accesses execute in
+  // order, so the next tile's writes cannot overtake this tile's reads.  The
+  // array is sized to kLdsPerWave so that at most eight of these waves share
+  // a compute unit (160 KB of LDS): measured faster than the twelve its
+  // 168 registers would allow (fewer concurrent K/V streams per HBM channel).
+  __shared__ __attribute__((aligned(1024))) char v_lds[kLdsPerWave];
+  static_assert(TILE_BYTES <= kLdsPerWave, "V tile does not fit");
 
   const int lane = threadIdx.x;
   const int li = lane & 15, grp = lane >> 4;
@@ -150,47 +155,48 @@ __global__ void __launch_bounds__(64, 2) rowwise_mfma_kernel(AttnArgs a) {
   auto key_off = [&](int key, int blk) -> int64_t {
     return ((int64_t)blk * a.B + key % a.B) * slot_stride;
   };
-  // lane-constant offsets within a 16-row half of a full tile
-  uint32_t koff[KSTEPS];
-#pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) koff[s] = li * slot_stride + (4 * s + grp) * 16;
+  // lane offset of K chunk 4k + grp of row li within a 16-row half: koff + 64 k
+  const uint32_t koff = li * slot_stride + grp * 16;
   // V load i of a lane: the 16 bytes that belong at LDS byte 1024 i + 16 lane
   // (physical row RPV i + lane / CPR, physical chunk lane % CPR, which holds
-  // logical chunk (lane % CPR) ^ vswz(row))
-  uint32_t vgoff[VL];
+  // logical chunk (lane % CPR) ^ vswz(row)).  The swizzle of row RPV i + x
+  // repeats with period VP in i, so the lane part takes VP registers and the
+  // rest, ((RPV i) mod 16) rows, is a constant.
+  constexpr int VP = CPR == 16 ? 2 : 1;
+  uint32_t vlane[VP];
 #pragma unroll
-  for (int i = 0; i < VL; ++i) {
-    const int pr = RPV * i + lane / CPR;
-    const int lc = (lane % CPR) ^ vswz<CPR>(pr);
-    vgoff[i] = (pr & 15) * slot_stride + lc * 16;
+  for (int j = 0; j < VP; ++j) {
+    const int pr = RPV * j + lane / CPR;
+    vlane[j] = (lane / CPR) * slot_stride + (((lane % CPR) ^ vswz<CPR>(pr)) << 4);
   }
-  // transposed-read offsets: rows 4 grp + li / 4 (and + 16), d 16n + 4 (li % 4)
-  int voff[NB];
-  {
-    const int row = 4 * grp + (li >> 2);
-#pragma unroll
-    for (int n = 0; n < NB; ++n) {
-      const int d0 = 16 * n + 4 * (li & 3);
-      voff[n] = row * ROWB + (((d0 >> 3) ^ vswz<CPR>(row)) << 4) + (d0 & 7) * 2;
-    }
-  }
+  auto vgoff = [&](int i) -> uint32_t { return ((RPV * i) & 15) * slot_stride + vlane[i % VP]; };
+  // transposed reads: row 4 grp + li / 4 (and + 16), d 16n + 4 (li % 4), i.e.
+  // chunk 2n + (li / 2) % 2 (swizzled) and byte 8 (li % 2) within it; the
+  // swizzle is even, so chunk 2n + b lands at 2 (n ^ sw / 2) + b
+  const int vrow = 4 * grp + (li >> 2);
+  const int vsw = vswz<CPR>(vrow) >> 1;
+  const int vbase = vrow * ROWB + ((li >> 1) & 1) * 16 + (li & 1) * 8;
+  auto voff = [&](int n) -> int { return vbase + ((n ^ vsw) << 5); };
 
   // K rows (A operand: key li of half h) and V chunks of a tile into
   // registers.  A full tile uses one scalar base per 16-key half (a half
   // never crosses a block: B and the tile start are multiples of 16); the
   // last, partial tile clamps its rows to key ke - 1 (finite data; those keys
   // are masked and get zero probability).  Both paths issue the same loads.
+  auto load_full = [&](int start, u32x4_t (&kr)[2][KSTEPS], u32x4_t (&vr)[VL]) {
+    const int64_t base0 = key_off(start, __builtin_amdgcn_readlane(myblk, start / a.B - blk0));
+    const int64_t base1 = key_off(start + 16, __builtin_amdgcn_readlane(myblk, (start + 16) / a.B - blk0));
+#pragma unroll
+    for (int k = 0; k < KSTEPS; ++k) {
+      kr[0][k] = load_once(kcache + base0 + koff + 64 * k);
+      kr[1][k] = load_once(kcache + base1 + koff + 64 * k);
+    }
+#pragma unroll
+    for (int i = 0; i < VL; ++i) vr[i] = load_once(vcache + ((RPV * i < 16) ? base0 : base1) + vgoff(i));
+  };
   auto load_tile = [&](int start, u32x4_t (&kr)[2][KSTEPS], u32x4_t (&vr)[VL]) {
     if (start + KT <= ke) {
-      const int64_t base0 = key_off(start, __builtin_amdgcn_readlane(myblk, start / a.B - blk0));
-      const int64_t base1 = key_off(start + 16, __builtin_amdgcn_readlane(myblk, (start + 16) / a.B - blk0));
-#pragma unroll
-      for (int k = 0; k < KSTEPS; ++k) {
-        kr[0][k] = load_once(kcache + base0 + koff[k]);
-        kr[1][k] = load_once(kcache + base1 + koff[k]);
-      }
-#pragma unroll
-      for (int i = 0; i < VL; ++i) vr[i] = load_once(vcache + ((RPV * i < 16) ? base0 : base1) + vgoff[i]);
+      load_full(start, kr, vr);
     } else {
       auto row_off = [&](int row) -> int64_t {
         const int key = min(start + row, ke - 1);
@@ -218,11 +224,13 @@ __global__ void __launch_bounds__(64, 2) rowwise_mfma_kernel(AttnArgs a) {
 #pragma unroll
   for (int n = 0; n < NB; ++n) o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // The steady-state loop prefetches full tiles only and unconditionally,
+  // so the compiler's vmcnt waits stay exact and the two load paths are not
+  // merged into one with per-lane 64-bit addresses; the last two tiles (the
+  // partial one among them) follow straight-line.
   const int n_tiles = (ke - kb + KT - 1) / KT;
   u32x4_t kr[2][KSTEPS], vr[VL];
-  load_tile(kb, kr, vr);
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    const int start = kb + tile * KT;
+  auto tile_step = [&](int start, auto&& prefetch) {
     // V tile into LDS (swizzled; 1 KB per instruction, conflict-free)
 #pragma unroll
     for (int i = 0; i < VL; ++i)
@@ -239,7 +247,7 @@ __global__ void __launch_bounds__(64, 2) rowwise_mfma_kernel(AttnArgs a) {
                                                        __builtin_bit_cast(bf16x8_t, qf[k]), s[h], 0, 0, 0);
     }
     // next tile's loads, in flight during this tile's softmax and p.v
-    if (tile + 1 < n_tiles) load_tile(start + KT, kr, vr);
+    prefetch();
     if (start + KT > ke) {
       // element r of half h is key 16h + 4grp + r of the tile
       const int lim = ke - start - 4 * grp;
@@ -280,11 +288,24 @@ __global__ void __launch_bounds__(64, 2) rowwise_mfma_kernel(AttnArgs a) {
     lds_cptr vb = (lds_cptr)v_lds;
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
-      const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vb + voff[n]));
-      const s16x4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vb + voff[n] + 16 * ROWB));
+      const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vb + voff(n)));
+      const s16x4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vb + voff(n) + 16 * ROWB));
       const s16x8_t vv = __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
       o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vv), pf, o[n], 0, 0, 0);
     }
+    };
+  load_tile(kb, kr, vr);
+  int tile = 0;
+  for (; tile + 2 < n_tiles; ++tile) {
+    const int s0 = kb + tile * KT;
+    tile_step(s0, [&] { load_full(s0 + KT, kr, vr); });
+  }
+  const int s0 = kb + tile * KT;
+  if (tile + 1 < n_tiles) {
+    tile_step(s0, [&] { load_tile(s0 + KT, kr, vr); });
+    tile_step(s0 + KT, [] {});
+  } else {
+    tile_step(s0, [] {});
   }
 
   // ---- finish ------------------------------------------------------------------

@@ -35,6 +35,14 @@ def test_traffic_only_for_the_measured_source(tmp_path, monkeypatch):
     assert bench.load_traffic("rowwise") == 12345
     src.write_text("kernel source B\n")                         # the kernel changed since
     assert bench.load_traffic("rowwise") is None
+    # a kernel built from two sources: a change in either one drops the figure
+    (tmp_path / "k2.hip").write_text("second source\n")
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", {"rowwise": ["k.hip", "k2.hip"]})
+    js["source_hash"] = bench.source_hash(["k.hip", "k2.hip"])
+    (prof / "rowwise_c3_counters.json").write_text(json.dumps(js))
+    assert bench.load_traffic("rowwise") == 12345
+    (tmp_path / "k2.hip").write_text("second source, changed\n")
+    assert bench.load_traffic("rowwise") is None
 
 
 @pytest.mark.parametrize("shared", [False, True])
