@@ -77,12 +77,13 @@ int64_t rowwise_waves(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R
   return n * Hkv;
 }
 
-// Row-wise partition length: a power-of-two multiple of lcm(64, B), at most
-// 64 blocks (one block id per lane of the wavefront) and 1024 keys.  When the
-// whole split-K grid fits on the device at once at some length (resident =
-// wavefronts the device holds for this kernel, 0 if unknown), the shortest
-// such length is taken: one round of waves, each as short as that allows.
-// Otherwise the length is chosen so that the grid holds roughly 32
+// Row-wise partition length: a multiple of lcm(64, B), at most 64 blocks (one
+// block id per lane of the wavefront) and 1024 keys.  When the whole split-K
+// grid fits on the device at once at some length (resident = wavefronts the
+// device holds for this kernel, 0 if unknown), the shortest such length is
+// taken (any multiple of the unit: the grid then fills nearly every wave
+// slot, each wave as short as that allows).  Otherwise a power-of-two
+// multiple of the unit is chosen so that the grid holds roughly 32
 // wavefronts per compute unit (many rounds; the order of the items keeps
 // the tail short).
 int32_t choose_split(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R, int32_t M,
@@ -99,10 +100,15 @@ int32_t choose_split(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R,
   while (top * 2 <= cap && top * 2 <= 1024) top *= 2;
   if (resident > 0 && rowwise_keys > 0 && env_int("PA_SPLIT_ONE_ROUND", 1) != 0 &&
       rowwise_waves(h_qsl, h_seq_lens, R, M, Hkv, ps, (int32_t)top) <= resident) {
-    int64_t s = top;
-    while (s / 2 >= unit && rowwise_waves(h_qsl, h_seq_lens, R, M, Hkv, ps, (int32_t)(s / 2)) <= resident)
-      s /= 2;
-    return (int32_t)s;
+    // the wave count does not grow with the length: binary search for the
+    // smallest multiple of the unit that fits
+    int64_t lo = 1, hi = top / unit;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi) / 2;
+      if (rowwise_waves(h_qsl, h_seq_lens, R, M, Hkv, ps, (int32_t)(mid * unit)) <= resident) hi = mid;
+      else lo = mid + 1;
+    }
+    return (int32_t)(lo * unit);
   }
   const int64_t target_waves = 256 * 32;
   const int64_t want = rowwise_keys * Hkv / target_waves;
