@@ -1,0 +1,91 @@
+"""GPU parity over the support matrix and over very long contexts.
+
+* A seeded sweep of random steps: dtype, GQA group, kv heads, head_dim and
+  block size drawn from the supported set, a random mix of decode rows and
+  chunks with random histories; every request is checked against the fp64
+  oracle (caches bit-exact, outputs within the dtype's tolerance).
+* Rows with more than 64 split-K partitions (the merge pass then makes
+  several passes over the partitions): forced 64-key partitions over
+  contexts of thousands of keys, and genuinely long contexts (70 000 keys)
+  at the default partition length.
+"""
+import numpy as np
+import pytest
+
+from helpers import check_requests, run_step, say
+from workloads import configs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import paged_kv_attention_reshape_amd as pa  # noqa: E402
+
+
+def _random_case(i):
+    g = np.random.default_rng(4000 + i)
+    dtype = ["bf16", "f32"][int(g.integers(0, 2))]
+    G = int(g.choice([1, 2, 4, 8]))
+    Hkv = int(g.choice([1, 2, 4, 8]))
+    D = int(g.choice([64, 128]))
+    B = int(g.choice([16, 32, 48, 64]))
+    R = int(g.integers(1, 9))
+    qlens, comp = [], []
+    for _ in range(R):
+        if g.random() < 0.65:
+            qlens.append(1)
+        else:
+            qlens.append(int(g.integers(2, 301)))
+        comp.append(int(g.integers(0, 3001)))
+    return dtype, G * Hkv, Hkv, D, B, qlens, comp
+
+
+CASES = [_random_case(i) for i in range(16)]
+
+
+@pytest.mark.parametrize("i", range(len(CASES)), ids=[f"rand{i}" for i in range(len(CASES))])
+def test_random_steps_match_oracle(i):
+    dtype, Hq, Hkv, D, B, qlens, comp = CASES[i]
+    say(f"\n[gpu-test] random step {i}: {CASES[i]}")
+    spec = configs.custom(f"rand{i}", dtype, Hq, Hkv, D, B, qlens, comp, seed=500 + i, pool_factor=1.4)
+    d, out, _ = run_step(spec, pa)
+    torch.cuda.synchronize()
+    err = check_requests(spec, out, d["key_cache"], d["value_cache"], range(spec.R),
+                         rows_per_req=24, what=f"random step {i}")
+    say(f"random step {i}: worst abs err {err:.2e}")
+
+
+@pytest.mark.parametrize("kernel", ["matrix", "vector"])
+@pytest.mark.parametrize("shape", [(32, 8, 128, 16), (64, 8, 128, 32), (16, 8, 64, 16)],
+                         ids=["g4-d128-b16", "g8-d128-b32", "g2-d64-b16"])
+def test_more_than_64_partitions_forced(kernel, shape, monkeypatch):
+    """64-key partitions over up to 9000 keys: up to 141 partials per row.
+    (With 2 q heads per kv head both settings run the vector kernel, the only
+    one with that instance.)"""
+    Hq, Hkv, D, B = shape
+    monkeypatch.setenv("PA_DECODE_MFMA", "1" if kernel == "matrix" else "0")
+    monkeypatch.setenv("PA_SPLIT_TOKENS", "64")
+    qlens = [1, 1, 1, 1]
+    comp = [4095, 4096 + 63, 8999, 130]
+    spec = configs.custom(f"p64-{kernel}-{Hq}", "bf16", Hq, Hkv, D, B, qlens, comp,
+                          seed=71 + Hq, pool_factor=1.2)
+    d, out, _ = run_step(spec, pa)
+    torch.cuda.synchronize()
+    err = check_requests(spec, out, d["key_cache"], d["value_cache"], range(spec.R),
+                         what=f"{kernel} {shape} split 64")
+    say(f"{kernel} {shape} split 64: worst abs err {err:.2e}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_seventy_thousand_key_contexts(dtype):
+    """Decode rows over 70 000 keys at the default partition length (more
+    than 64 partitions of 1024 keys), beside a short decode and a chunk."""
+    spec = configs.custom(f"long70k-{dtype}", dtype, 8, 2, 128, 16, [1, 1, 1, 40],
+                          [69999, 70500, 17, 900], seed=88, pool_factor=1.05)
+    d, out, _ = run_step(spec, pa)
+    torch.cuda.synchronize()
+    err = check_requests(spec, out, d["key_cache"], d["value_cache"], range(spec.R),
+                         rows_per_req=12, what=f"70k {dtype}")
+    say(f"70k-key contexts {dtype}: worst abs err {err:.2e}")
