@@ -520,16 +520,17 @@ static bool use_qlds(int32_t G) {
   return G >= 4;
 }
 
-// bf16 caches with GQA groups of 4 and 8 go to the matrix-core kernel.  With
-// groups of 8 the vector kernel's v_dot2 loops cost about as much time as the
-// K/V stream (measured: 5.2 -> 5.7 TB/s on 16 x 32K + 240 short contexts);
-// with groups of 4 the two are within 1 %, the matrix-core one ahead.
-// PA_DECODE_MFMA=0/1 overrides for measurement.
+// Decode is bandwidth-bound; the matrix cores are used for it only where the
+// vector kernel's arithmetic measurably limits the stream: bf16 caches with
+// GQA groups of 8, where the v_dot2 loops cost about as much time as the K/V
+// reads (measured: 5.2 -> 5.7 TB/s on 16 x 32K + 240 short contexts).  With
+// groups of 4 the two kernels are within noise of each other, and the
+// vector kernel stays.  PA_DECODE_MFMA=0/1 overrides (groups of 4 and 8).
 static bool use_mfma(bool bf16, int32_t D, int32_t G) {
   if (!bf16 || rowwise_mfma_kernel_for(D, G) == nullptr) return false;
   const char* e = getenv("PA_DECODE_MFMA");
   if (e != nullptr && *e) return atoi(e) != 0;
-  return true;
+  return G >= 8;
 }
 
 static hipError_t rowwise_kernel_for(bool bf16, int32_t D, int32_t G, const void** out) {

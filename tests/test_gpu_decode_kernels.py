@@ -1,8 +1,8 @@
 """GPU parity of the two split-K decode kernels against the fp64 oracle.
 
-bf16 caches with 4 or 8 query heads per kv head run the matrix-core kernel
-by default; PA_DECODE_MFMA=0 selects the vector-ALU kernel for the same
-shapes (it also serves fp32 and groups of 1 and 2).  Both are checked on context lengths around every tile and partition
+bf16 caches with 8 query heads per kv head run the matrix-core kernel by
+default, every other case the vector-ALU kernel; PA_DECODE_MFMA=1/0 selects
+either kernel for groups of 4 and 8.  Both are checked on context lengths around every tile and partition
 edge (1, 15..17, 31..33, partition lengths +-1), with head_dim 64 and 128,
 block sizes 16, 32 and 48 (a size that is not a power of two: 16-key halves
 of a 32-key tile fall in different blocks), and several partition lengths
