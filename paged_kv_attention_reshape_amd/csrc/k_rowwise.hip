@@ -32,6 +32,8 @@
 // fp32 caches use the same structure with plain FMAs.
 #include <stdlib.h>
 
+#include <algorithm>
+
 #include "pa_internal.h"
 
 namespace pa {
@@ -563,9 +565,13 @@ hipError_t launch_rowwise(const AttnArgs& a, hipStream_t s) {
   return hipLaunchKernel(kern, dim3(a.ps.n_rw, a.Hkv), dim3(64), params, 0, s);
 }
 
-int64_t rowwise_resident_waves(bool bf16, int32_t D, int32_t G) {
-  // the split-K kernel's wavefronts the current device holds at once
-  // (occupancy per compute unit x compute units), cached per configuration
+int64_t rowwise_round_slots(bool bf16, int32_t D, int32_t G) {
+  // wave slots of one round of the split-K grid: the kernel's occupancy per
+  // compute unit, at most 8 (two per SIMD), times the compute units; cached
+  // per configuration.  A grid that fits in one round streams faster with
+  // about 8 waves per compute unit than with the 12 the vector kernel could
+  // hold (measured on 64 contexts of 512..4096 keys: 107 against 116 us;
+  // fewer concurrent K/V streams per HBM channel)
   static thread_local int64_t cache[2][2][9][3] = {};
   const int qi = use_mfma(bf16, D, G) ? 2 : (use_qlds(G) ? 1 : 0);
   const int di = D == 128 ? 1 : 0;
@@ -579,7 +585,7 @@ int64_t rowwise_resident_waves(bool bf16, int32_t D, int32_t G) {
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64, 0) != hipSuccess || cus <= 0 ||
         per_cu <= 0)
       return 0;
-    c = (int64_t)cus * per_cu;
+    c = (int64_t)cus * std::min(per_cu, 8);
   }
   return c;
 }

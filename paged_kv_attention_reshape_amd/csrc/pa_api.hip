@@ -79,10 +79,10 @@ int64_t rowwise_waves(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R
 
 // Row-wise partition length: a multiple of lcm(64, B), at most 64 blocks (one
 // block id per lane of the wavefront) and 1024 keys.  When the whole split-K
-// grid fits on the device at once at some length (resident = wavefronts the
-// device holds for this kernel, 0 if unknown), the shortest such length is
-// taken (any multiple of the unit: the grid then fills nearly every wave
-// slot, each wave as short as that allows).  Otherwise a power-of-two
+// grid fits in one round at some length (resident = the round's wave slots
+// for this kernel, at most 8 per compute unit; 0 if unknown), the shortest
+// such length is taken (any multiple of the unit: the grid then fills nearly
+// every slot, each wave as short as that allows).  Otherwise a power-of-two
 // multiple of the unit is chosen so that the grid holds roughly 32
 // wavefronts per compute unit (many rounds; the order of the items keeps
 // the tail short).
@@ -180,7 +180,7 @@ pa_status make_plan(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R, 
       rowwise_keys += q * (c + 1) + (int64_t)q * (q - 1) / 2;
     }
   }
-  const int64_t resident = rowwise_keys > 0 ? pa::rowwise_resident_waves(bf16, D, G) : 0;
+  const int64_t resident = rowwise_keys > 0 ? pa::rowwise_round_slots(bf16, D, G) : 0;
   ps.S = choose_split(h_qsl, h_seq_lens, R, M, rowwise_keys, Hkv, resident, ps);
   ps.SEG = choose_segment(h_qsl, h_seq_lens, R, M, B, Hkv, ps);
   int64_t n_rw = 0, n_ck = 0, n_mg = 0, n_parts = 0;

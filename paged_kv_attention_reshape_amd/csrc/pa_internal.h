@@ -201,9 +201,9 @@ hipError_t launch_rowwise(const AttnArgs& a, hipStream_t s);
 // Matrix-core split-K kernel for bf16 caches (same items, partials and
 // launch shape as the vector kernel); nullptr where it has no instance.
 const void* rowwise_mfma_kernel_for(int32_t D, int32_t G);
-// Split-K wavefronts the current device holds at once for this configuration
-// (0 when the device cannot be queried).
-int64_t rowwise_resident_waves(bool bf16, int32_t D, int32_t G);
+// Wave slots of one round of the split-K grid on the current device for this
+// configuration (0 when the device cannot be queried).
+int64_t rowwise_round_slots(bool bf16, int32_t D, int32_t G);
 hipError_t launch_chunk(const AttnArgs& a, hipStream_t s);
 hipError_t launch_merge(const AttnArgs& a, hipStream_t s);
 bool chunk_kernel_supports(bool bf16, int32_t D, int32_t G, int32_t B);
