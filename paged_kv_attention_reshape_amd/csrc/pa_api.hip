@@ -78,14 +78,19 @@ int64_t rowwise_waves(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R
 }
 
 // Row-wise partition length: a multiple of lcm(64, B), at most 64 blocks (one
-// block id per lane of the wavefront) and 1024 keys.  When the whole split-K
-// grid fits in one round at some length (resident = the round's wave slots
-// for this kernel, at most 8 per compute unit; 0 if unknown), the shortest
-// such length is taken (any multiple of the unit: the grid then fills nearly
-// every slot, each wave as short as that allows).  Otherwise a power-of-two
-// multiple of the unit is chosen so that the grid holds roughly 32
-// wavefronts per compute unit (many rounds; the order of the items keeps
-// the tail short).
+// block id per lane of the wavefront) and 2048 keys.  With the round's wave
+// slots known (resident = min(occupancy, 8) waves per compute unit x compute
+// units; 0 if unknown):
+//  * when the whole split-K grid fits in one round at some length, the
+//    shortest such length (any multiple of the unit: the grid then fills
+//    nearly every slot, each wave as short as that allows);
+//  * otherwise several rounds run, and longest-first list scheduling ends
+//    near max(keys per slot, longest item): every length up to the keys per
+//    slot is as good by that bound, and the longest of them makes the fewest
+//    items, partial results and merges (measured on 16 x 32K + 240 short
+//    contexts: 2048-key partitions 651 us, 1024 674 us, 512 729 us).
+// Without the slot count: a power-of-two multiple of the unit (<= 1024 keys)
+// that gives the grid roughly 32 wavefronts per compute unit.
 int32_t choose_split(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R, int32_t M,
                      int64_t rowwise_keys, int32_t Hkv, int64_t resident, const pa::PlanShape& ps) {
   const int32_t B = ps.B;
@@ -96,20 +101,24 @@ int32_t choose_split(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R,
     int64_t s = (forced + unit - 1) / unit * unit;
     return (int32_t)std::min(s, cap / unit * unit);
   }
+  if (resident > 0 && rowwise_keys > 0 && env_int("PA_SPLIT_ONE_ROUND", 1) != 0) {
+    const int64_t longest = std::max<int64_t>(1, std::min<int64_t>(cap, 2048) / unit) * unit;
+    if (rowwise_waves(h_qsl, h_seq_lens, R, M, Hkv, ps, (int32_t)longest) <= resident) {
+      // the wave count does not grow with the length: binary search for the
+      // smallest multiple of the unit that fits
+      int64_t lo = 1, hi = longest / unit;
+      while (lo < hi) {
+        const int64_t mid = (lo + hi) / 2;
+        if (rowwise_waves(h_qsl, h_seq_lens, R, M, Hkv, ps, (int32_t)(mid * unit)) <= resident) hi = mid;
+        else lo = mid + 1;
+      }
+      return (int32_t)(lo * unit);
+    }
+    const int64_t per_slot = rowwise_keys * Hkv / resident;
+    return (int32_t)std::min(longest, std::max(unit, per_slot / unit * unit));
+  }
   int64_t top = unit;
   while (top * 2 <= cap && top * 2 <= 1024) top *= 2;
-  if (resident > 0 && rowwise_keys > 0 && env_int("PA_SPLIT_ONE_ROUND", 1) != 0 &&
-      rowwise_waves(h_qsl, h_seq_lens, R, M, Hkv, ps, (int32_t)top) <= resident) {
-    // the wave count does not grow with the length: binary search for the
-    // smallest multiple of the unit that fits
-    int64_t lo = 1, hi = top / unit;
-    while (lo < hi) {
-      const int64_t mid = (lo + hi) / 2;
-      if (rowwise_waves(h_qsl, h_seq_lens, R, M, Hkv, ps, (int32_t)(mid * unit)) <= resident) hi = mid;
-      else lo = mid + 1;
-    }
-    return (int32_t)(lo * unit);
-  }
   const int64_t target_waves = 256 * 32;
   const int64_t want = rowwise_keys * Hkv / target_waves;
   int64_t s = unit;
