@@ -41,92 +41,51 @@ __device__ __forceinline__ int32_t min32(int32_t a, int32_t b) { return a < b ? 
 // j-th row-wise item of a request; item index k (also its partial slot)
 __device__ void emit_rowwise(const ReqView& v, int32_t j, int32_t k, const PlanShape& ps,
                              int4* items_rw) {
-  int32_t i = 0;
-  int32_t parts = cdiv(v.c + 1, ps.S);
-  while (j >= parts && i + 1 < v.q) {  // multi-token requests only (fp32 chunks)
-    j -= parts;
-    ++i;
-    parts = cdiv(v.c + i + 1, ps.S);
-  }
+  const int32_t i = rw_row_of_item(v.c, v.q, j, ps.S);
+  const int32_t jj = (int32_t)(j - rw_items_before(v.c, i, ps.S));
   const int32_t keys = v.c + i + 1;
-  const int32_t kb = j * ps.S;
+  const int32_t parts = cdiv(keys, ps.S);
+  const int32_t kb = jj * ps.S;
   const int32_t ke = min32(kb + ps.S, keys);
   if (k < ps.n_rw) items_rw[k] = make_int4(v.r, v.t0 + i, kb, ke | (parts == 1 ? kDirect : 0));
 }
 
-// j-th merge record of a row-wise request whose first item is k_first
+// j-th merge record of a row-wise request whose first item is k_first: the
+// j-th row with more than one partition
 __device__ void emit_merge_rowwise(const ReqView& v, int32_t j, int32_t k_first, int32_t m,
                                    const PlanShape& ps, int4* merge) {
-  int32_t item = k_first;
-  for (int32_t i = 0; i < v.q; ++i) {
-    const int32_t parts = cdiv(v.c + i + 1, ps.S);
-    if (parts > 1) {
-      if (j == 0) {
-        if (m < ps.n_mg)
-          merge[m] = item + parts <= ps.n_rw ? make_int4(v.t0 + i, item, parts, (1 << 16) | 1)
-                                             : make_int4(-1, 0, 0, 0);
-        return;
-      }
-      --j;
-    }
-    item += parts;
-  }
+  if (m >= ps.n_mg) return;
+  const int32_t i = rw_first_split_row(v.c, ps.S) + j;
+  const int64_t item = k_first + rw_items_before(v.c, i, ps.S);
+  const int32_t parts = cdiv(v.c + i + 1, ps.S);
+  merge[m] = i < v.q && item + parts <= ps.n_rw ? make_int4(v.t0 + i, (int32_t)item, parts, (1 << 16) | 1)
+                                                : make_int4(-1, 0, 0, 0);
 }
 
-// j-th chunk item of a chunk request whose partial slots start at pbase.
-// Items are ordered segment-major, (seg, qt descending): the q-tiles that
-// read the same key segment are consecutive, so the XCD-aware launch keeps
-// them on one L2, and within a segment the longer (later) q-tiles come
-// first.  A q-tile's segment count grows with qt, so the q-tiles that have
-// segment s form a suffix of the tile range.
+// j-th chunk item of a chunk request whose partial slots start at pbase
+// (order: chunk_item_of).  Segment-major order keeps the q-tiles that read the
+// same key segment consecutive, so the XCD-aware launch keeps them on one L2.
 __device__ void emit_chunk(const ReqView& v, int32_t j, int32_t k, int32_t pbase,
                            const PlanShape& ps, int4* items_ck) {
-  const int32_t nqt = cdiv(v.q, ps.TQ);
-  const int32_t max_seg = cdiv(v.c + v.q, ps.SEG);
-  for (int32_t sg = 0; sg < max_seg; ++sg) {
-    int32_t first_qt = nqt;
-    for (int32_t qt = 0; qt < nqt; ++qt)
-      if (cdiv(v.c + min32((qt + 1) * ps.TQ, v.q), ps.SEG) > sg) { first_qt = qt; break; }
-    const int32_t count = nqt - first_qt;
-    if (j < count) {
-      const int32_t qt = nqt - 1 - j;
-      const int32_t nseg = cdiv(v.c + min32((qt + 1) * ps.TQ, v.q), ps.SEG);
-      int32_t pb = pbase;  // partial slots of earlier split tiles
-      for (int32_t t = 0; t < qt; ++t) {
-        const int32_t ns = cdiv(v.c + min32((t + 1) * ps.TQ, v.q), ps.SEG);
-        if (ns > 1) pb += ns * ps.TQ;
-      }
-      const bool split = nseg > 1 && pb + nseg * ps.TQ <= ps.n_rw + ps.n_ck_parts;
-      if (k < ps.n_ck) items_ck[k] = make_int4(v.r, qt, sg, split ? pb : -1);
-      return;
-    }
-    j -= count;
-  }
+  const ChunkItem it = chunk_item_of(v.c, v.q, j, ps.TQ, ps.SEG);
+  if (it.qt < 0 || k >= ps.n_ck) return;
+  const int64_t pb = pbase + it.slots_before;
+  const bool split = it.nseg > 1 && pb + (int64_t)it.nseg * ps.TQ <= (int64_t)ps.n_rw + ps.n_ck_parts;
+  items_ck[k] = make_int4(v.r, it.qt, it.seg, split ? (int32_t)pb : -1);
 }
 
-// j-th merge record of a chunk request (groups of MT tokens of split tiles)
+// j-th merge record of a chunk request (chunk_merge_of)
 __device__ void emit_merge_chunk(const ReqView& v, int32_t j, int32_t m, int32_t pbase,
                                  const PlanShape& ps, int4* merge) {
-  const int32_t nqt = cdiv(v.q, ps.TQ);
-  for (int32_t qt = 0; qt < nqt; ++qt) {
-    const int32_t tok_end = min32((qt + 1) * ps.TQ, v.q);
-    const int32_t nseg = cdiv(v.c + tok_end, ps.SEG);
-    if (nseg > 1) {
-      const int32_t ntok = tok_end - qt * ps.TQ;
-      const int32_t ngrp = cdiv(ntok, ps.MT);
-      if (j < ngrp) {
-        const int32_t tau0 = j * ps.MT;
-        const int32_t n = min32(ps.MT, ntok - tau0);
-        const bool split = pbase + nseg * ps.TQ <= ps.n_rw + ps.n_ck_parts;
-        if (m < ps.n_mg)
-          merge[m] = split ? make_int4(v.t0 + qt * ps.TQ + tau0, pbase + tau0, nseg, (n << 16) | ps.TQ)
-                           : make_int4(-1, 0, 0, 0);
-        return;
-      }
-      j -= ngrp;
-      pbase += nseg * ps.TQ;
-    }
+  if (m >= ps.n_mg) return;
+  const ChunkMerge r = chunk_merge_of(v.c, v.q, j, ps.TQ, ps.SEG, ps.MT);
+  int4 rec = make_int4(-1, 0, 0, 0);
+  if (r.qt >= 0) {
+    const int64_t pb = pbase + r.slots_before;
+    if (pb + (int64_t)r.nseg * ps.TQ <= (int64_t)ps.n_rw + ps.n_ck_parts)
+      rec = make_int4(v.t0 + r.qt * ps.TQ + r.tau0, (int32_t)(pb + r.tau0), r.nseg, (r.n << 16) | ps.TQ);
   }
+  merge[m] = rec;
 }
 
 // Sort key of a chunk item: the 64-key tiles of its key segment for the

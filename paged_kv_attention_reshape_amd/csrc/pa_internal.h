@@ -91,26 +91,146 @@ __host__ __device__ inline bool goes_rowwise(int32_t q, const PlanShape& ps) {
   return q == 1 || (q > 1 && ps.rowwise_all);
 }
 
+// ---- per-request plan arithmetic in closed form ---------------------------
+// Every count and every record index below is O(1) or O(segments) per
+// request, so a long prefill chunk (hundreds of q-tiles, thousands of rows)
+// costs the planner no more than a short one.
+
+// sum_{k=1..n} cdiv(k, S) for n >= 0: with n = a S + b, S (1 + ... + a) + b (a + 1)
+__host__ __device__ inline int64_t ceil_sum(int64_t n, int64_t S) {
+  const int64_t a = n / S, b = n % S;
+  return S * a * (a + 1) / 2 + b * (a + 1);
+}
+
+// Row-wise request (history c): row i sees keys c + i + 1, cdiv(c + i + 1, S)
+// partitions.  Items of rows 0 .. i-1:
+__host__ __device__ inline int64_t rw_items_before(int32_t c, int32_t i, int32_t S) {
+  return ceil_sum((int64_t)c + i, S) - ceil_sum(c, S);
+}
+// rows with more than one partition are rows i >= rw_first_split_row
+__host__ __device__ inline int32_t rw_first_split_row(int32_t c, int32_t S) {
+  return S - c > 0 ? S - c : 0;
+}
+// row of item j (0 <= j < items of the request): the last row i < q with
+// rw_items_before(i) <= j
+__host__ __device__ inline int32_t rw_row_of_item(int32_t c, int32_t q, int64_t j, int32_t S) {
+  int32_t lo = 0, hi = q - 1;
+  while (lo < hi) {
+    const int32_t mid = lo + (hi - lo + 1) / 2;
+    if (rw_items_before(c, mid, S) <= j) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Chunk request (history c, q tokens, nqt = cdiv(q, TQ) q-tiles): q-tile t
+// reads keys up to c + tok_end(t) and is cut into nseg(t) = cdiv(c +
+// tok_end(t), SEG) key segments; nseg is non-decreasing in t and the last
+// tile has the most, max_seg = cdiv(c + q, SEG).  The first tile with more
+// than s segments (s < max_seg): tiles before the last satisfy
+// c + (t + 1) TQ > s SEG exactly when t >= floor((s SEG - c) / TQ), and the
+// last tile always does.
+__host__ __device__ inline int32_t chunk_first_tile(int32_t c, int32_t nqt, int32_t s, int32_t TQ, int32_t SEG) {
+  const int64_t x = (int64_t)s * SEG - c;
+  if (x < 0) return 0;
+  const int64_t t = x / TQ;
+  return t < nqt - 1 ? (int32_t)t : nqt - 1;
+}
+__host__ __device__ inline int32_t chunk_nseg(int32_t c, int32_t q, int32_t t, int32_t TQ, int32_t SEG) {
+  const int32_t tok_end = (t + 1) * TQ < q ? (t + 1) * TQ : q;
+  return cdiv(c + tok_end, SEG);
+}
+// partial slots (nseg TQ per split tile) of the split tiles before tile t
+__host__ __device__ inline int64_t chunk_slots_before(int32_t c, int32_t q, int32_t t, int32_t TQ, int32_t SEG) {
+  const int32_t nqt = cdiv(q, TQ), max_seg = cdiv(c + q, SEG);
+  int64_t n = 0;
+  int32_t lo = max_seg > 1 ? chunk_first_tile(c, nqt, 1, TQ, SEG) : nqt;  // first tile with 2+ segments
+  for (int32_t k = 2; k <= max_seg && lo < t; ++k) {
+    const int32_t hi = k < max_seg ? chunk_first_tile(c, nqt, k, TQ, SEG) : nqt;  // tiles [lo, hi) have k
+    const int32_t e = hi < t ? hi : t;
+    if (e > lo) n += (int64_t)k * TQ * (e - lo);
+    lo = hi;
+  }
+  return n;
+}
+
+// Chunk item j of a request (0 <= j < its item count): items are ordered
+// segment-major, (segment, q-tile descending); the q-tiles that have segment
+// s are tiles chunk_first_tile(s) .. nqt - 1.  slots_before = partial slots of
+// the request's split tiles before this one.
+struct ChunkItem {
+  int32_t qt, seg, nseg;
+  int64_t slots_before;
+};
+__host__ __device__ inline ChunkItem chunk_item_of(int32_t c, int32_t q, int32_t j, int32_t TQ, int32_t SEG) {
+  const int32_t nqt = cdiv(q, TQ), max_seg = cdiv(c + q, SEG);
+  ChunkItem it{-1, -1, 0, 0};
+  for (int32_t sg = 0; sg < max_seg; ++sg) {
+    const int32_t count = nqt - chunk_first_tile(c, nqt, sg, TQ, SEG);
+    if (j < count) {
+      it.qt = nqt - 1 - j;
+      it.seg = sg;
+      it.nseg = chunk_nseg(c, q, it.qt, TQ, SEG);
+      it.slots_before = chunk_slots_before(c, q, it.qt, TQ, SEG);
+      return it;
+    }
+    j -= count;
+  }
+  return it;
+}
+
+// Chunk merge record j of a request: groups of MT tokens of the split tiles
+// (tiles chunk_first_tile(1) .. nqt - 1), cdiv(TQ, MT) records per tile and
+// cdiv(tokens of the last tile, MT) for the last one.  qt < 0: no such record.
+struct ChunkMerge {
+  int32_t qt, tau0, n, nseg;
+  int64_t slots_before;
+};
+__host__ __device__ inline ChunkMerge chunk_merge_of(int32_t c, int32_t q, int32_t j, int32_t TQ, int32_t SEG,
+                                                     int32_t MT) {
+  const int32_t nqt = cdiv(q, TQ), max_seg = cdiv(c + q, SEG);
+  ChunkMerge r{-1, 0, 0, 0, 0};
+  if (max_seg <= 1 || j < 0) return r;
+  const int32_t f1 = chunk_first_tile(c, nqt, 1, TQ, SEG);
+  const int32_t rec_full = cdiv(TQ, MT);
+  int32_t qt = f1 + j / rec_full, jj = j % rec_full;
+  if (qt >= nqt - 1) {  // the last tile (possibly fewer tokens)
+    jj = j - (nqt - 1 - f1) * rec_full;
+    qt = nqt - 1;
+  }
+  const int32_t ntok = (qt + 1) * TQ < q ? TQ : q - qt * TQ;
+  const int32_t tau0 = jj * MT;
+  if (tau0 >= ntok) return r;
+  r.qt = qt;
+  r.tau0 = tau0;
+  r.n = MT < ntok - tau0 ? MT : ntok - tau0;
+  r.nseg = chunk_nseg(c, q, qt, TQ, SEG);
+  r.slots_before = chunk_slots_before(c, q, qt, TQ, SEG);
+  return r;
+}
+
 __host__ __device__ inline ReqCounts request_counts(int32_t q, int32_t L, const PlanShape& ps) {
   ReqCounts n{0, 0, 0, 0};
   if (q <= 0) return n;
   const int32_t c = L - q;
   if (goes_rowwise(q, ps)) {
-    for (int32_t i = 0; i < q; ++i) {
-      const int32_t parts = cdiv(c + i + 1, ps.S);
-      n.rw += parts;
-      if (parts > 1) n.mg += 1;
-    }
+    n.rw = (int32_t)rw_items_before(c, q, ps.S);
+    const int32_t f = rw_first_split_row(c, ps.S);
+    n.mg = q > f ? q - f : 0;
   } else {
-    const int32_t nqt = cdiv(q, ps.TQ);
-    for (int32_t qt = 0; qt < nqt; ++qt) {
-      const int32_t tok_end = (qt + 1) * ps.TQ < q ? (qt + 1) * ps.TQ : q;
-      const int32_t nseg = cdiv(c + tok_end, ps.SEG);
-      n.ck += nseg;
-      if (nseg > 1) {
-        n.ck_parts += nseg * ps.TQ;
-        n.mg += cdiv(tok_end - qt * ps.TQ, ps.MT);
+    const int32_t TQ = ps.TQ, SEG = ps.SEG;
+    const int32_t nqt = cdiv(q, TQ), max_seg = cdiv(c + q, SEG);
+    const int32_t rec_full = cdiv(TQ, ps.MT), rec_last = cdiv(q - (nqt - 1) * TQ, ps.MT);
+    int32_t lo = 0;
+    for (int32_t k = 1; k <= max_seg; ++k) {  // tiles [lo, hi) have k segments
+      const int32_t hi = k < max_seg ? chunk_first_tile(c, nqt, k, TQ, SEG) : nqt;
+      const int32_t cnt = hi - lo;
+      n.ck += k * cnt;
+      if (k > 1 && cnt > 0) {
+        n.ck_parts += k * TQ * cnt;
+        n.mg += hi == nqt ? (cnt - 1) * rec_full + rec_last : cnt * rec_full;
       }
+      lo = hi;
     }
   }
   return n;
