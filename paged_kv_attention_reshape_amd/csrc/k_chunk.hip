@@ -44,7 +44,7 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 constexpr int kThreads = kChunkRows * 2;  // one wave per 32 rows
 constexpr int kWaves = kThreads / 64;
 constexpr int KT = 64;         // keys per tile
-constexpr int kMaxSegBlocks = 512;
+constexpr int kMaxSegBlocks = 1024;
 constexpr int kXcds = 8;       // accelerator complex dies of an MI355X
 constexpr float kNegInf = -__builtin_huge_valf();
 

@@ -148,9 +148,12 @@ int32_t choose_segment(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t 
     }
   }
   const int64_t target_items = 256 * 2;
-  const int64_t per_item = std::max<int64_t>(1, tiles * Hkv / target_items);
+  const int64_t target = std::max<int64_t>(1, tiles * Hkv / target_items) * 64;
+  // the power of two nearest the target (in ratio), or the limit when the
+  // target is well above the largest power of two that fits
   int64_t seg = 512;
-  while (seg < per_item * 64 && seg * 2 <= limit) seg *= 2;
+  while (seg * 2 <= limit && target * target > 2 * seg * seg) seg *= 2;
+  if (seg * 2 > limit && target * target > 2 * seg * seg) seg = limit;
   return (int32_t)std::min(seg, limit);
 }
 
