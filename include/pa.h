@@ -229,7 +229,10 @@ pa_status pa_copy_blocks(const void* src_pools, void* dst_pools, const int32_t* 
  * pa_attention_workspace_size -- bytes of device workspace pa_attention needs
  * for this step (plan tables plus split-K partial results).  Takes the same
  * host mirrors pa_attention plans from; returns 0 and sets pa_last_error() if
- * they are invalid.  The size depends only on these arguments.
+ * they are invalid.  The size depends on these arguments and on the current
+ * device (its compute units and the split-K kernel's occupancy set the
+ * partition length), so query it with the device current that pa_attention
+ * will run on.
  */
 size_t pa_attention_workspace_size(const int32_t* h_query_start_loc, const int32_t* h_seq_lens,
                                    int32_t R, int32_t num_heads, int32_t num_kv_heads,
