@@ -7,7 +7,9 @@
 // counts into offsets.  Phase 2: the threads emit the records in parallel,
 // record index idx going to the request whose scanned range contains idx
 // (binary search in LDS), so a request with many records does not serialise
-// the kernel.  Phase 3 puts the items in launch order, longest first (a
+// the kernel; a record's row, q-tile, segment and partial-slot offset come
+// from the closed forms of pa_internal.h (no loop over the request's rows or
+// q-tiles).  Phase 3 puts the items in launch order, longest first (a
 // counting sort in LDS): workgroups are dispatched in item order, and
 // longest-first list scheduling keeps the last, partly filled round of
 // workgroups short.  Row-wise items are sorted by their key count and keep
