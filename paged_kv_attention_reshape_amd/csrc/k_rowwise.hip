@@ -358,15 +358,23 @@ __global__ void __launch_bounds__(64) rowwise_kernel(AttnArgs a) {
 // pairs in turn.  For a pair, lane p loads partition p's (m, l) so the max
 // and the weighted sum of l are wave reductions, then every lane accumulates
 // its slice of the head dimension over the partitions.
+// Wave reductions: within each 16-lane row by DPP (quad swaps, then row
+// rotations by 4 and 8), across the four rows by two shuffles.
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) x = fmaxf(x, shfl_xor(x, m));
-  return x;
+  x = fmaxf(x, dpp<kQuadXor1>(x));
+  x = fmaxf(x, dpp<kQuadXor2>(x));
+  x = fmaxf(x, dpp<kRowRor4>(x));
+  x = fmaxf(x, dpp<kRowRor8>(x));
+  x = fmaxf(x, shfl_xor(x, 16));
+  return fmaxf(x, shfl_xor(x, 32));
 }
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) x += shfl_xor(x, m);
-  return x;
+  x += dpp<kQuadXor1>(x);
+  x += dpp<kQuadXor2>(x);
+  x += dpp<kRowRor4>(x);
+  x += dpp<kRowRor8>(x);
+  x += shfl_xor(x, 16);
+  return x + shfl_xor(x, 32);
 }
 
 template <bool BF16, int D, int G>
