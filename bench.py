@@ -60,6 +60,8 @@ def parse():
                    help="skip the swap-out / swap-in round-trip measurement")
     p.add_argument("--no-rope", dest="rope", action="store_false",
                    help="skip the separate timing of the fused rotary + cache-write kernel")
+    p.add_argument("--no-serving", dest="serving", action="store_false",
+                   help="skip the 32-layer serving-trace throughput measurement")
     p.add_argument("--copy-calibration", action="store_true",
                    help="instead of the step, run a plain 1 GiB device copy a few times "
                         "(reference for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -225,6 +227,67 @@ def scheduler_timing(product: bool, steps: int = 200, shared: bool = False):
                     "cow_copies": m["cow_copies"], "cached_blocks": m["cached_blocks"],
                     "trace": "as above, 80 % of requests start with one of 8 shared 1024-token system prompts"})
     return out
+
+
+def serving_measurement(dev, first: int = 40, steps: int = 20, layers: int = 32):
+    """GPU throughput on the serving trace: the steps the C++ scheduler plans
+    for 2048 requests (prompts lognormal median 1500, chunk 512, budget 8192,
+    recompute preemption), each run as write_kv + attention over every layer
+    of a 32-layer, 16384-block cache (32 GiB, Llama-3-8B attention geometry).
+    Steps first .. first + steps - 1 (past the ramp-up) are timed with HIP
+    events around all their layers; inputs are device-resident and filled
+    once per step (not timed)."""
+    import numpy as np
+    import torch
+    import paged_kv_attention_reshape_amd as pa
+    from workloads import serving_trace as st
+    cfg = st.TraceConfig()
+    plans = st.drive(pa.Scheduler(**st.scheduler_args(cfg)), cfg)
+    sel = [p for p in plans[first:first + steps] if p["sched"]]
+    HQ, HKV, D, B = 32, 8, 128, cfg.block_size
+    kc = torch.zeros((layers, cfg.num_blocks, B, HKV, D), dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    ws = pa.Workspace(dev)
+    stream = torch.cuda.current_stream()
+    gen = torch.Generator(device=dev).manual_seed(5)
+    total_ms, total_tok, n_dec, n_chunk_tok = 0.0, 0, 0, 0
+    per_step = []
+    for p in sel:
+        ql, cp, bt, _, _ = st.step_arrays(p, B)
+        T = int(ql.sum())
+        qsl, sl, sm = pa.build_step_metadata(ql, cp, bt, B, cfg.num_blocks)
+        d = {k: torch.from_numpy(v).to(dev) for k, v in
+             {"bt": bt, "qsl": qsl, "sl": sl, "nc": cp, "sm": sm}.items()}
+        q = torch.randn((T, HQ, D), generator=gen, device=dev).to(torch.bfloat16)
+        k = torch.randn((T, HKV, D), generator=gen, device=dev).to(torch.bfloat16)
+        v = torch.randn((T, HKV, D), generator=gen, device=dev).to(torch.bfloat16)
+        out = torch.empty_like(q)
+        ws.get(pa.attention_workspace_size(qsl, sl, HQ, HKV, D, B, pa.PA_BF16))
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for layer in range(layers):
+            pa.write_kv(k, v, kc[layer], vc[layer], d["sm"])
+            pa.attention(out, q, kc[layer], vc[layer], d["bt"], d["qsl"], d["sl"], d["nc"], qsl, sl,
+                         1.0 / np.sqrt(D), workspace=ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        total_ms += ms
+        total_tok += T
+        n_dec += int(np.sum(ql == 1))
+        n_chunk_tok += int(np.sum(ql[ql > 1]))
+        per_step.append(round(ms, 3))
+    del kc, vc
+    torch.cuda.empty_cache()
+    return {"steps": len(sel), "first_step": first, "layers": layers, "tokens": total_tok,
+            "decode_rows": n_dec, "chunk_tokens": n_chunk_tok,
+            "ms_per_step": round(total_ms / max(1, len(sel)), 3),
+            "tokens_per_s": round(total_tok / (total_ms * 1e-3), 1) if total_ms > 0 else None,
+            "step_ms_p10_p50_p90": [round(float(x), 3) for x in np.percentile(per_step, [10, 50, 90])],
+            "trace": "2048 requests at step 0, prompts lognormal median 1500, outputs geometric mean 256, "
+                     "chunk 512, budget 8192, 16384 blocks of 16; Hq 32, Hkv 8, D 128",
+            "includes": "write_kv + attention (slot mapping built on the host) for every layer of the step"}
 
 
 def swap_measurement(dev, reps: int = 10):
@@ -474,6 +537,7 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(rope_gbs / HBM_PEAK_GBS, 4)}
 
     swap = swap_measurement(dev) if args.swap else None
+    serving = serving_measurement(dev) if args.serving else None
 
     # host scheduler / block allocator (C++) on the serving trace
     sched_t = scheduler_timing(product=True)
@@ -541,6 +605,7 @@ def main():
         "rope_write_kv": rope,
         "scheduler": sched_t,
         "swap_roundtrip": swap,
+        "serving_trace": serving,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
