@@ -4,6 +4,10 @@
   block size drawn from the supported set, a random mix of decode rows and
   chunks with random histories; every request is checked against the fp64
   oracle (caches bit-exact, outputs within the dtype's tolerance).
+* A wider seeded sweep: up to 12 requests with histories up to 20 000 keys
+  and chunks up to 700 tokens, with the decode kernel (matrix-core or
+  vector) and the partition length (64, 128 or 512 keys, or the automatic
+  rule) drawn per case.
 * Rows with more than 64 split-K partitions (the merge pass then makes
   several passes over the partitions): forced 64-key partitions over
   contexts of thousands of keys, and genuinely long contexts (70 000 keys)
@@ -55,6 +59,46 @@ def test_random_steps_match_oracle(i):
     err = check_requests(spec, out, d["key_cache"], d["value_cache"], range(spec.R),
                          rows_per_req=24, what=f"random step {i}")
     say(f"random step {i}: worst abs err {err:.2e}")
+
+
+def _wide_case(i):
+    g = np.random.default_rng(10000 + i)
+    dtype = ["bf16", "f32"][int(g.integers(0, 2))]
+    G = int(g.choice([1, 2, 4, 8]))
+    Hkv = int(g.choice([1, 2, 4, 8]))
+    D = int(g.choice([64, 128]))
+    B = int(g.choice([16, 32, 48, 64]))
+    R = int(g.integers(1, 13))
+    qlens, comp = [], []
+    for _ in range(R):
+        u = g.random()
+        qlens.append(1 if u < 0.6 else int(g.integers(2, 40)) if u < 0.8 else int(g.integers(40, 700)))
+        comp.append(int(g.choice([0, int(g.integers(0, 64)), int(g.integers(0, 5000)),
+                                  int(g.integers(5000, 20000))], p=[0.1, 0.2, 0.5, 0.2])))
+    mfma = ["0", "1", None][int(g.integers(0, 3))]
+    split = [None, "64", "128", "512"][int(g.integers(0, 4))]
+    return dtype, G * Hkv, Hkv, D, B, qlens, comp, mfma, split
+
+
+WIDE = [_wide_case(i) for i in range(64)]
+
+
+@pytest.mark.parametrize("i", range(len(WIDE)), ids=[f"wide{i}" for i in range(len(WIDE))])
+def test_wide_random_steps_match_oracle(i, monkeypatch):
+    dtype, Hq, Hkv, D, B, qlens, comp, mfma, split = WIDE[i]
+    monkeypatch.delenv("PA_DECODE_MFMA", raising=False)
+    monkeypatch.delenv("PA_SPLIT_TOKENS", raising=False)
+    if mfma is not None:
+        monkeypatch.setenv("PA_DECODE_MFMA", mfma)
+    if split is not None:
+        monkeypatch.setenv("PA_SPLIT_TOKENS", split)
+    say(f"\n[gpu-test] wide random step {i}: {WIDE[i]}")
+    spec = configs.custom(f"wide{i}", dtype, Hq, Hkv, D, B, qlens, comp, seed=20000 + i, pool_factor=1.3)
+    d, out, _ = run_step(spec, pa)
+    torch.cuda.synchronize()
+    err = check_requests(spec, out, d["key_cache"], d["value_cache"], range(spec.R),
+                         rows_per_req=6, what=f"wide random step {i}")
+    say(f"wide random step {i}: worst abs err {err:.2e}")
 
 
 @pytest.mark.parametrize("kernel", ["matrix", "vector"])
