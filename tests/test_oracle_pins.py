@@ -457,6 +457,124 @@ def test_merge_partials_equals_full_softmax():
         assert np.allclose(got, full, atol=1e-13)
 
 
+# ----------------------------------------------------------------------------
+# attention_rows: the per-request checker of the large GPU parity cases
+# ----------------------------------------------------------------------------
+def _bf16_scalar(bits16):
+    """One bf16 pattern -> Python float, by building the float32 word."""
+    return float(np.array([int(bits16) << 16], dtype=np.uint32).view(np.float32)[0])
+
+
+def _brute_rows(Q, K, V, qpos, scale, dtype, head_map):
+    """Scalar loops over gathered rows: query row i at absolute position
+    qpos[i] sees keys 0 .. qpos[i]; query head h reads kv head head_map(h)."""
+    conv = _bf16_scalar if dtype == "bf16" else float
+    n, Hq, D = Q.shape
+    out = np.zeros((n, Hq, D))
+    for i in range(n):
+        for h in range(Hq):
+            g = head_map(h)
+            sc = []
+            for j in range(int(qpos[i]) + 1):
+                sc.append(scale * sum(conv(Q[i, h, d]) * conv(K[j, g, d]) for d in range(D)))
+            mx = max(sc)
+            w = [math.exp(x - mx) for x in sc]
+            tot = sum(w)
+            for d in range(D):
+                out[i, h, d] = sum(w[j] * conv(V[j, g, d]) for j in range(len(w))) / tot
+    return out
+
+
+def _rows_case(rng, G, dtype, Hkv=2, D=6, L=33, n=5):
+    Hq = G * Hkv
+    if dtype == "f32":
+        Q = rng.standard_normal((n, Hq, D)).astype(np.float32)
+        K = rng.standard_normal((L, Hkv, D)).astype(np.float32)
+        V = rng.standard_normal((L, Hkv, D)).astype(np.float32)
+    else:
+        f = lambda shape: (rng.standard_normal(shape).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        Q, K, V = f((n, Hq, D)), f((L, Hkv, D)), f((L, Hkv, D))
+    # rows at scattered absolute positions, the last key included; nonzero history
+    qpos = np.sort(rng.choice(L, n, replace=False))
+    qpos[-1] = L - 1
+    return Q, K, V, qpos, 1 / math.sqrt(D)
+
+
+def _rows_err(fn, G, dtype, seed):
+    rng = np.random.default_rng(seed)
+    Q, K, V, qpos, scale = _rows_case(rng, G, dtype)
+    got, _ = fn(Q, K, V, qpos, scale, dtype)
+    want = _brute_rows(Q, K, V, qpos, scale, dtype, lambda h: h // G)
+    err = np.abs(np.asarray(got, np.float64) - want)
+    return float(err.max()) if np.all(np.isfinite(err)) else math.inf
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_attention_rows_brute_force(G, dtype):
+    """Absolute query positions, contiguous GQA groups and the bf16 widening
+    of attention_rows against scalar loops (independent bf16 conversion)."""
+    assert _rows_err(oracle.attention_rows, G, dtype, 300 + G) <= 1e-12
+
+
+def test_attention_rows_pin_catches_planted_slips():
+    """The brute-force pin above fails for the plausible slips in
+    attention_rows: a query position off by one, and the kv head taken as
+    h % Hkv instead of h // G (the two maps differ once G, Hkv >= 2)."""
+    from oracle import pa_oracle as po
+
+    def shifted_qpos(Q, K, V, qpos, scale, dtype):
+        return oracle.attention_rows(Q, K, V, np.asarray(qpos) - 1, scale, dtype)
+
+    def modulo_heads(Q, K, V, qpos, scale, dtype):
+        Qf, Kf, Vf = (oracle.as_f64(x, dtype) for x in (Q, K, V))
+        out = np.empty(Qf.shape)
+        Hkv = Kf.shape[1]
+        for h in range(Qf.shape[1]):
+            out[:, h], _ = po._softmax_attend(Qf[:, h], Kf[:, h % Hkv], Vf[:, h % Hkv],
+                                              np.asarray(qpos), scale)
+        return out, None
+
+    for G in (2, 4):
+        for dtype in ("f32", "bf16"):
+            assert _rows_err(shifted_qpos, G, dtype, 300 + G) > 1e-3
+            assert _rows_err(modulo_heads, G, dtype, 300 + G) > 1e-3
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_attention_rows_equals_paged_attention(G, dtype):
+    """attention_rows on a request's gathered history gives the rows that
+    oracle.attention computes through the block table: decode rows, rows in
+    the middle of a chunk and a chunk's last row."""
+    rng = np.random.default_rng(400 + G)
+    Hkv, D, B = 2, 8, 4
+    Hq = G * Hkv
+    st = _random_step(rng, 4, Hq, Hkv, D, B, 45, dtype=dtype)
+    st["qlens"][0] = 1                    # one decode row at least
+    st["comp"][0] = st["lens"][0] - 1
+    st["qsl"] = np.concatenate([[0], np.cumsum(st["qlens"])]).astype(np.int32)
+    T = int(st["qsl"][-1])
+    if dtype == "f32":
+        st["q"] = rng.standard_normal((T, Hq, D)).astype(np.float32)
+    else:
+        st["q"] = (rng.standard_normal((T, Hq, D)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    scale = 1 / math.sqrt(D)
+    full, full_lse = oracle.attention(st["q"], st["kc"], st["vc"], st["bt"], st["qsl"], st["lens"],
+                                      st["comp"], scale, B, dtype)
+    checked = 0
+    for r in range(4):
+        a, q, L, c = int(st["qsl"][r]), st["qlens"][r], st["lens"][r], st["comp"][r]
+        rows = np.unique([0, q // 2, q - 1])
+        K = oracle.gather_kv(st["kc"], st["bt"][r], L, B)
+        V = oracle.gather_kv(st["vc"], st["bt"][r], L, B)
+        o, lse = oracle.attention_rows(st["q"][a + rows], K, V, c + rows, scale, dtype)
+        assert np.allclose(o, full[a + rows], rtol=0, atol=1e-12)
+        assert np.allclose(lse, full_lse[a + rows], rtol=0, atol=1e-12)
+        checked += len(rows)
+    assert checked >= 6
+
+
 def test_bf16_widening_exact():
     # patterns of exactly representable values
     vals = np.array([1.0, -2.5, 0.0, 3.140625, -0.0078125, 65280.0], dtype=np.float32)
