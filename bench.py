@@ -247,7 +247,9 @@ def serving_measurement(dev, first: int = 40, steps: int = 20, layers: int = 32)
     HQ, HKV, D, B = 32, 8, 128, cfg.block_size
     kc = torch.zeros((layers, cfg.num_blocks, B, HKV, D), dtype=torch.bfloat16, device=dev)
     vc = torch.zeros_like(kc)
-    ws = pa.Workspace(dev)
+    # one workspace for the whole trace, sized by the scheduler's limits
+    ws = pa.alloc_workspace(pa.attention_workspace_bound(cfg.max_num_seqs, cfg.max_num_batched_tokens,
+                                                         st.max_seq_len(cfg), HQ, HKV, D, B, pa.PA_BF16), dev)
     stream = torch.cuda.current_stream()
     gen = torch.Generator(device=dev).manual_seed(5)
     total_ms, total_tok, n_dec, n_chunk_tok = 0.0, 0, 0, 0
@@ -262,14 +264,15 @@ def serving_measurement(dev, first: int = 40, steps: int = 20, layers: int = 32)
         k = torch.randn((T, HKV, D), generator=gen, device=dev).to(torch.bfloat16)
         v = torch.randn((T, HKV, D), generator=gen, device=dev).to(torch.bfloat16)
         out = torch.empty_like(q)
-        ws.get(pa.attention_workspace_size(qsl, sl, HQ, HKV, D, B, pa.PA_BF16))
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
+        # planned once per step (the metadata has no layer dimension), run per layer
+        plan = pa.attention_plan(d["bt"], d["qsl"], d["sl"], d["nc"], qsl, sl, HQ, kc.shape[1:],
+                                 pa.PA_BF16, ws)
         for layer in range(layers):
             pa.write_kv(k, v, kc[layer], vc[layer], d["sm"])
-            pa.attention(out, q, kc[layer], vc[layer], d["bt"], d["qsl"], d["sl"], d["nc"], qsl, sl,
-                         1.0 / np.sqrt(D), workspace=ws)
+            pa.attention_run(plan, out, q, kc[layer], vc[layer], 1.0 / np.sqrt(D))
         e1.record(stream)
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1)
@@ -403,9 +406,8 @@ def main():
     qsl_h, sl_h = spec.query_start_loc, spec.seq_lens
     out = torch.empty_like(d["query"])
     slot_mapping = torch.empty((spec.T,), dtype=torch.int64, device=dev)
-    ws = pa.Workspace(dev)
-    ws.get(pa.attention_workspace_size(qsl_h, sl_h, spec.Hq, spec.Hkv, spec.D, spec.B,
-                                       pa.PA_BF16 if spec.dtype == "bf16" else pa.PA_F32))
+    ws = pa.alloc_workspace(pa.attention_workspace_size(qsl_h, sl_h, spec.Hq, spec.Hkv, spec.D, spec.B,
+                                                        pa.PA_BF16 if spec.dtype == "bf16" else pa.PA_F32), dev)
     stream = torch.cuda.current_stream()
 
     step_no = [0]

@@ -226,6 +226,28 @@ pa_status pa_copy_blocks(const void* src_pools, void* dst_pools, const int32_t* 
                          int64_t block_bytes, void* stream);
 
 /*
+ * pa_attention_workspace_bound -- bytes of device workspace that cover every
+ * step within the given limits, so that a server can allocate the workspace
+ * once ([P1] "Paged Attention": the step's tables are sized by static maxima,
+ * block_table being [max_num_reqs, max_num_blocks_per_req]).
+ *
+ *   max_num_reqs     most requests in one step (R)
+ *   max_num_tokens   most flattened query rows in one step (T)
+ *   max_seq_len      longest seq_len of any request in a step
+ * Returns a size >= pa_attention_workspace_size(...) for every step with
+ * R <= max_num_reqs, T <= max_num_tokens and every seq_len <= max_seq_len,
+ * for the given geometry on the current device (with the tuning overrides of
+ * pa_set_tuning in force at the time of the call).  The bound follows from
+ * the partition and segment rules (it is not a measured maximum) and is
+ * largest for long prefill chunks deep into long prompts, whose key segments
+ * each need their own partial results.  Returns 0 and sets pa_last_error()
+ * for unsupported geometry or negative limits.
+ */
+size_t pa_attention_workspace_bound(int32_t max_num_reqs, int64_t max_num_tokens,
+                                   int32_t max_seq_len, int32_t num_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, pa_dtype dtype);
+
+/*
  * pa_attention_workspace_size -- bytes of device workspace pa_attention needs
  * for this step (plan tables plus split-K partial results).  Takes the same
  * host mirrors pa_attention plans from; returns 0 and sets pa_last_error() if
@@ -283,6 +305,89 @@ pa_status pa_attention(void* out, const void* query, const void* key_cache,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_attention_plan / pa_attention_run -- pa_attention in two calls, so that
+ * a step is planned once and attended layer by layer.
+ *
+ * [P1] "Paged Attention": slot_mapping and block_table have no layer
+ * dimension -- every layer of a step uses the same metadata -- so the work
+ * plan of a step is the same for all its layers; only the query, the output
+ * and the layer's caches change.
+ *
+ * pa_attention_plan checks the step exactly as pa_attention does, enqueues
+ * the device planner on stream (it writes the work tables into the
+ * workspace) and fills *plan on the host.  pa_attention_run enqueues the
+ * attention of one layer with that plan.  pa_attention(...) is the same as
+ * pa_attention_plan followed by one pa_attention_run on the same stream.
+ *
+ *   plan   caller-owned record; its contents are private to the library (copy
+ *          it only as a whole).  It holds the device pointers block_table,
+ *          query_start_loc, seq_lens, num_computed_tokens and workspace given
+ *          to pa_attention_plan: they must stay valid and unchanged until the
+ *          last pa_attention_run with this plan has executed.
+ * Every pa_attention_run of a plan must be ordered after its
+ * pa_attention_plan on the device (same stream, or joined by an event), and
+ * no other plan may be written into the same workspace until the runs have
+ * executed; runs that share a workspace must not overlap each other (they
+ * reuse its partial-result space), so enqueue them on one stream.  The
+ * arguments of pa_attention_plan mean what they mean for pa_attention; those
+ * of pa_attention_run are the per-layer ones (out, query, key_cache,
+ * value_cache with the planned geometry, and scale).
+ */
+typedef struct pa_step_plan { int64_t words[48]; } pa_step_plan;
+
+pa_status pa_attention_plan(pa_step_plan* plan, const int32_t* block_table,
+                            int32_t max_blocks_per_req, const int32_t* query_start_loc,
+                            const int32_t* seq_lens, const int32_t* num_computed_tokens,
+                            const int32_t* h_query_start_loc, const int32_t* h_seq_lens,
+                            int32_t R, int64_t T, int32_t num_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                            pa_dtype dtype, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+pa_status pa_attention_run(const pa_step_plan* plan, void* out, const void* query,
+                           const void* key_cache, const void* value_cache, float scale,
+                           void* stream);
+
+/*
+ * pa_set_tuning / pa_get_tuning -- overrides of the library's own kernel and
+ * partition choices, for tests and measurements.
+ *
+ * Every knob is 0 by default, which is the product behaviour; results differ
+ * only by rounding between settings.  The setting is process-wide and read
+ * when a step is planned (pa_attention, pa_attention_plan, the workspace
+ * queries), so set it before those calls and not while other threads plan.
+ *   PA_TUNE_DECODE_KERNEL       1: vector split-K kernel, 2: matrix-core
+ *                               split-K kernel (bf16 with 4 or 8 q heads per
+ *                               kv head; elsewhere the vector kernel runs)
+ *   PA_TUNE_DECODE_Q_PLACEMENT  1: query rows in registers, 2: in LDS
+ *                               (vector split-K kernel)
+ *   PA_TUNE_SPLIT_KEYS          n > 0: split-K partition length, rounded up
+ *                               to the partition unit and capped at 64 blocks
+ *   PA_TUNE_SPLIT_RULE          1: the device-independent partition rule
+ *                               (about 32 waves per compute unit) instead of
+ *                               the occupancy-based one
+ *   PA_TUNE_CHUNK_SEGMENT       n > 0: chunk key-segment length (rounded up
+ *                               to 64, capped at the kernel's limit)
+ *   PA_TUNE_CHUNK_PATH          1: every multi-token request takes the
+ *                               split-K path instead of the matrix-core
+ *                               chunk kernel
+ * pa_set_tuning returns PA_ERR_BAD_SHAPE for an unknown knob or a negative
+ * value; pa_get_tuning returns -1 for an unknown knob.
+ */
+typedef enum pa_tuning_knob {
+  PA_TUNE_DECODE_KERNEL = 0,
+  PA_TUNE_DECODE_Q_PLACEMENT = 1,
+  PA_TUNE_SPLIT_KEYS = 2,
+  PA_TUNE_SPLIT_RULE = 3,
+  PA_TUNE_CHUNK_SEGMENT = 4,
+  PA_TUNE_CHUNK_PATH = 5,
+  PA_TUNE_COUNT = 6
+} pa_tuning_knob;
+
+pa_status pa_set_tuning(int32_t knob, int32_t value);
+int32_t pa_get_tuning(int32_t knob);
+
+/*
  * pa_set_profiling_events -- optional per-kernel timing hook (tests and
  * benchmarks).
  *
@@ -290,8 +395,10 @@ pa_status pa_attention(void* out, const void* query, const void* key_cache,
  * caller on the current device, or NULL / n_events == 0 to disable.  While set
  * on the calling thread, every pa_attention call records, on its stream,
  * events[0] before its first launch and events[1], [2], [3], [4] after the
- * plan, row-wise split-K, chunk and merge launches.  The library copies the
- * handles; the caller keeps ownership of the events.
+ * plan, row-wise split-K, chunk and merge launches (pa_attention_plan records
+ * events[0] and [1]; pa_attention_run records events[1] before its first
+ * launch, then [2], [3], [4]).  The library copies the handles; the caller
+ * keeps ownership of the events.
  */
 pa_status pa_set_profiling_events(void* const* events, int32_t n_events);
 

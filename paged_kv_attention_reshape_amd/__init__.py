@@ -6,8 +6,10 @@ include/pa_sched.h); this package only marshals arguments.  Importing it does no
 library; the first call does, and raises if it has not been built.
 """
 from ._lib import (  # noqa: F401
-    EXPORTS, LIB_PATH, PA_BF16, PA_F32, PAError, Workspace, abi_version, attention,
-    attention_workspace_size, build_step_metadata, compute_slot_mapping, set_profiling_events, last_error, lib, status_str,
-    validate_metadata, write_kv, rope_write_kv, copy_blocks,
+    EXPORTS, LIB_PATH, PA_BF16, PA_F32, TUNING, PAError, StepPlan, abi_version, alloc_workspace,
+    attention, attention_plan, attention_run, attention_workspace_bound, attention_workspace_size,
+    build_step_metadata, compute_slot_mapping, copy_blocks, get_tuning, last_error, lib,
+    rope_write_kv, set_profiling_events, set_tuning, status_str, tuning, validate_metadata,
+    write_kv,
 )
 from ._sched import SCHED_EXPORTS, SCHED_LIB_PATH, Scheduler, sched_lib  # noqa: F401,E402

@@ -28,9 +28,26 @@ STATUS = {
 
 EXPORTS = [
     "pa_abi_version", "pa_status_str", "pa_last_error", "pa_build_step_metadata",
-    "pa_compute_slot_mapping", "pa_write_kv", "pa_attention_workspace_size", "pa_attention",
-    "pa_set_profiling_events", "pa_validate_metadata", "pa_rope_write_kv", "pa_copy_blocks",
+    "pa_compute_slot_mapping", "pa_write_kv", "pa_attention_workspace_size",
+    "pa_attention_workspace_bound", "pa_attention", "pa_attention_plan", "pa_attention_run",
+    "pa_set_tuning", "pa_get_tuning", "pa_set_profiling_events", "pa_validate_metadata",
+    "pa_rope_write_kv", "pa_copy_blocks",
 ]
+
+# pa_tuning_knob
+TUNING = {
+    "decode_kernel": 0,        # 1 vector split-K kernel, 2 matrix-core split-K kernel
+    "decode_q_placement": 1,   # 1 query rows in registers, 2 in LDS
+    "split_keys": 2,           # n > 0: split-K partition length
+    "split_rule": 3,           # 1 device-independent partition rule
+    "chunk_segment": 4,        # n > 0: chunk key-segment length
+    "chunk_path": 5,           # 1 multi-token requests on the split-K path
+}
+
+
+class StepPlanRecord(ctypes.Structure):
+    """pa_step_plan: caller-owned, contents private to the library."""
+    _fields_ = [("words", ctypes.c_int64 * 48)]
 
 
 class PAError(RuntimeError):
@@ -84,6 +101,22 @@ def lib():
     L.pa_attention_workspace_size.argtypes = [_i32p, _i32p, ctypes.c_int32, ctypes.c_int32,
                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                               ctypes.c_int]
+    L.pa_attention_workspace_bound.restype = ctypes.c_size_t
+    L.pa_attention_workspace_bound.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.c_int32, ctypes.c_int]
+    L.pa_attention_plan.restype = ctypes.c_int
+    L.pa_attention_plan.argtypes = [ctypes.POINTER(StepPlanRecord), _vp, ctypes.c_int32, _vp, _vp,
+                                    _vp, _i32p, _i32p, ctypes.c_int32, ctypes.c_int64,
+                                    ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_int32, ctypes.c_int, _vp, ctypes.c_size_t, _vp]
+    L.pa_attention_run.restype = ctypes.c_int
+    L.pa_attention_run.argtypes = [ctypes.POINTER(StepPlanRecord), _vp, _vp, _vp, _vp,
+                                   ctypes.c_float, _vp]
+    L.pa_set_tuning.restype = ctypes.c_int
+    L.pa_set_tuning.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    L.pa_get_tuning.restype = ctypes.c_int32
+    L.pa_get_tuning.argtypes = [ctypes.c_int32]
     L.pa_attention.restype = ctypes.c_int
     L.pa_attention.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp, _i32p,
                                _i32p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
@@ -258,40 +291,122 @@ def attention_workspace_size(h_query_start_loc, h_seq_lens, num_heads: int, num_
     return int(n)
 
 
-class Workspace:
-    """Reusable device workspace (grows on demand, 256-byte aligned)."""
+def attention_workspace_bound(max_num_reqs: int, max_num_tokens: int, max_seq_len: int,
+                              num_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
+                              dtype_code: int) -> int:
+    """Workspace bytes that cover every step with at most max_num_reqs
+    requests, max_num_tokens query rows and sequences of at most max_seq_len
+    keys (pa_attention_workspace_bound)."""
+    n = lib().pa_attention_workspace_bound(max_num_reqs, max_num_tokens, max_seq_len, num_heads,
+                                           num_kv_heads, head_dim, block_size, dtype_code)
+    if n == 0 and last_error():
+        raise PAError(2, "pa_attention_workspace_bound", last_error())
+    return int(n)
 
-    def __init__(self, device="cuda"):
-        self.device = device
-        self.buf = None
 
-    def get(self, nbytes: int):
-        import torch
-        nbytes = max(int(nbytes), 256)
-        if self.buf is None or self.buf.numel() < nbytes:
-            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
-        return self.buf
+def alloc_workspace(nbytes: int, device="cuda"):
+    """A device workspace of nbytes (at least 256).  Allocating it is the
+    caller's own step, done once; attention() and attention_run() never
+    allocate."""
+    import torch
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def _workspace_arg(workspace):
+    import torch
+    if not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.uint8 or not workspace.is_cuda:
+        raise TypeError("workspace must be a device uint8 tensor (see alloc_workspace)")
+    return _ptr(workspace), workspace.numel()
 
 
 def attention(out, query, key_cache, value_cache, block_table, query_start_loc, seq_lens,
-              num_computed, h_query_start_loc, h_seq_lens, scale: float, workspace=None,
+              num_computed, h_query_start_loc, h_seq_lens, scale: float, workspace,
               stream=None) -> None:
     """out/query [T, Hq, D]; caches [N, B, Hkv, D]; block_table [R, M] int32;
     query_start_loc [R+1], seq_lens [R], num_computed [R] int32 device tensors;
-    h_query_start_loc / h_seq_lens host mirrors (numpy)."""
+    h_query_start_loc / h_seq_lens host mirrors (numpy); workspace a device
+    uint8 tensor of at least the step's workspace size (PA_ERR_WORKSPACE_TOO_SMALL
+    otherwise).  One C call: the library plans the step once."""
     T, Hq, D = query.shape
     N, B, Hkv, _ = key_cache.shape
     R = int(seq_lens.shape[0])
     qsl = _np_i32(h_query_start_loc)
     sl = _np_i32(h_seq_lens)
-    dt = _dtype_code(query)
-    need = attention_workspace_size(qsl, sl, Hq, Hkv, D, B, dt)
-    if workspace is None:
-        workspace = Workspace(query.device)
-    buf = workspace.get(need) if isinstance(workspace, Workspace) else workspace
+    wp, wn = _workspace_arg(workspace)
     M = block_table.shape[1] if block_table.dim() == 2 else 1
     _check(lib().pa_attention(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
                               _ptr(block_table), M, _ptr(query_start_loc), _ptr(seq_lens),
                               _ptr(num_computed), _p32(qsl), _p32(sl), R, T, Hq, Hkv, D, N, B,
-                              float(scale), dt, _ptr(buf), buf.numel(),
+                              float(scale), _dtype_code(query), wp, wn,
                               ctypes.c_void_p(_stream(stream))), "pa_attention")
+
+
+class StepPlan:
+    """A planned step (pa_attention_plan): the record plus references that
+    keep the device metadata and the workspace it names alive."""
+
+    def __init__(self, record, keep):
+        self.record = record
+        self._keep = keep
+
+
+def attention_plan(block_table, query_start_loc, seq_lens, num_computed, h_query_start_loc,
+                   h_seq_lens, num_heads: int, key_cache_shape, dtype_code: int, workspace,
+                   stream=None) -> StepPlan:
+    """Plan a step once for all its layers (pa_attention_plan).  key_cache_shape
+    is (num_blocks, block_size, num_kv_heads, head_dim) of every layer's cache."""
+    N, B, Hkv, D = (int(x) for x in key_cache_shape)
+    R = int(seq_lens.shape[0])
+    qsl = _np_i32(h_query_start_loc)
+    sl = _np_i32(h_seq_lens)
+    T = int(qsl[-1]) if len(qsl) else 0
+    wp, wn = _workspace_arg(workspace)
+    M = block_table.shape[1] if block_table.dim() == 2 else 1
+    rec = StepPlanRecord()
+    _check(lib().pa_attention_plan(ctypes.byref(rec), _ptr(block_table), M, _ptr(query_start_loc),
+                                   _ptr(seq_lens), _ptr(num_computed), _p32(qsl), _p32(sl), R, T,
+                                   num_heads, Hkv, D, N, B, dtype_code, wp, wn,
+                                   ctypes.c_void_p(_stream(stream))), "pa_attention_plan")
+    return StepPlan(rec, (block_table, query_start_loc, seq_lens, num_computed, workspace))
+
+
+def attention_run(plan: StepPlan, out, query, key_cache, value_cache, scale: float,
+                  stream=None) -> None:
+    """One layer's attention with a planned step (pa_attention_run)."""
+    _check(lib().pa_attention_run(ctypes.byref(plan.record), _ptr(out), _ptr(query), _ptr(key_cache),
+                                  _ptr(value_cache), float(scale), ctypes.c_void_p(_stream(stream))),
+           "pa_attention_run")
+
+
+def _knob(k) -> int:
+    return TUNING[k] if isinstance(k, str) else int(k)
+
+
+def set_tuning(knob, value: int) -> None:
+    """Override one of the library's own choices (tests and measurements);
+    0 restores the product behaviour.  Knob names: see TUNING."""
+    _check(lib().pa_set_tuning(_knob(knob), int(value)), "pa_set_tuning")
+
+
+def get_tuning(knob) -> int:
+    return int(lib().pa_get_tuning(_knob(knob)))
+
+
+class tuning:
+    """Context manager: `with tuning(split_keys=64, decode_kernel=2): ...`
+    sets the knobs and restores their previous values on exit."""
+
+    def __init__(self, **knobs):
+        self.knobs = {k: int(v) for k, v in knobs.items() if v is not None}
+        self.saved = {}
+
+    def __enter__(self):
+        for k, v in self.knobs.items():
+            self.saved[k] = get_tuning(k)
+            set_tuning(k, v)
+        return self
+
+    def __exit__(self, *exc):
+        for k, v in self.saved.items():
+            set_tuning(k, v)
+        return False

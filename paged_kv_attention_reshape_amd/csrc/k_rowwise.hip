@@ -385,6 +385,13 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnArgs a) {
   const int t_first = mr.x;
   if (t_first < 0) return;
   const int first = mr.y, n = mr.z, n_tok = mr.w >> 16, stride = mr.w & 0xFFFF;
+  // a record must name output rows of this step and partial slots of this
+  // workspace (the plan only writes such records; this keeps a table that
+  // disagrees with the launch sizes from reading or writing outside them)
+  const int64_t n_parts = (int64_t)a.ps.n_rw + a.ps.n_ck_parts;
+  if (n < 1 || n_tok < 1 || stride < 1 || first < 0 || (int64_t)t_first + n_tok > a.ps.T ||
+      (int64_t)first + (n_tok - 1) + (int64_t)(n - 1) * stride >= n_parts)
+    return;
   const int g = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -523,10 +530,11 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnArgs a) {
 
 // Query rows go to LDS when that lowers the register footprint enough to
 // matter (GQA groups of 4 and more: three waves per SIMD instead of two, so
-// more K/V loads in flight); PA_DECODE_QLDS=0/1 overrides for measurement.
+// more K/V loads in flight); PA_TUNE_DECODE_Q_PLACEMENT overrides.
 static bool use_qlds(int32_t G) {
-  const char* e = getenv("PA_DECODE_QLDS");
-  if (e != nullptr && *e) return atoi(e) != 0;
+  const int32_t t = tuning(PA_TUNE_DECODE_Q_PLACEMENT);
+  if (t == 1) return false;
+  if (t == 2) return true;
   return G >= 4;
 }
 
@@ -535,11 +543,12 @@ static bool use_qlds(int32_t G) {
 // GQA groups of 8, where the v_dot2 loops cost about as much time as the K/V
 // reads (measured: 5.2 -> 5.7 TB/s on 16 x 32K + 240 short contexts).  With
 // groups of 4 the two kernels are within noise of each other, and the
-// vector kernel stays.  PA_DECODE_MFMA=0/1 overrides (groups of 4 and 8).
+// vector kernel stays.  PA_TUNE_DECODE_KERNEL overrides (groups of 4 and 8).
 static bool use_mfma(bool bf16, int32_t D, int32_t G) {
   if (!bf16 || rowwise_mfma_kernel_for(D, G) == nullptr) return false;
-  const char* e = getenv("PA_DECODE_MFMA");
-  if (e != nullptr && *e) return atoi(e) != 0;
+  const int32_t t = tuning(PA_TUNE_DECODE_KERNEL);
+  if (t == 1) return false;
+  if (t == 2) return true;
   return G >= 8;
 }
 

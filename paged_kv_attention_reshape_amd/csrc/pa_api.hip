@@ -12,6 +12,8 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <atomic>
+#include <cstring>
 #include <string>
 #include <vector>
 
@@ -41,11 +43,7 @@ pa_status hip_fail(hipError_t e, const char* what) {
   return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  if (v == nullptr || *v == 0) return dflt;
-  return atoi(v);
-}
+std::atomic<int32_t> g_tune[PA_TUNE_COUNT];
 
 pa_status check_geometry(int32_t Hq, int32_t Hkv, int32_t D, int32_t B, int32_t num_blocks,
                          int dtype) {
@@ -62,6 +60,33 @@ pa_status check_geometry(int32_t Hq, int32_t Hkv, int32_t D, int32_t B, int32_t 
 }
 
 int64_t gcd64(int64_t a, int64_t b) { return b == 0 ? a : gcd64(b, a % b); }
+int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Partition lengths the split-K rule can choose for block size B: multiples of
+// unit = lcm(64, B) up to cap = 64 blocks (one block id per lane of the
+// wavefront); `longest` is the longest the occupancy-based rule picks (at most
+// 2048 keys) and `top` the longest the device-independent rule picks (a
+// power-of-two multiple of the unit, at most 1024 keys).
+struct SplitLengths {
+  int64_t unit, cap, longest, top;
+};
+SplitLengths split_lengths(int32_t B) {
+  SplitLengths s;
+  s.unit = 64 / gcd64(64, B) * B;
+  s.cap = std::max<int64_t>(s.unit, (int64_t)64 * B);
+  s.longest = std::max<int64_t>(1, std::min<int64_t>(s.cap, 2048) / s.unit) * s.unit;
+  s.top = s.unit;
+  while (s.top * 2 <= s.cap && s.top * 2 <= 1024) s.top *= 2;
+  return s;
+}
+
+// The forced partition length of PA_TUNE_SPLIT_KEYS (0 when not forced).
+int64_t forced_split(int32_t B) {
+  const int64_t f = pa::tuning(PA_TUNE_SPLIT_KEYS);
+  if (f <= 0) return 0;
+  const SplitLengths sl = split_lengths(B);
+  return std::min((f + sl.unit - 1) / sl.unit * sl.unit, sl.cap / sl.unit * sl.unit);
+}
 
 // Row-wise wavefronts of a step (all kv heads) at partition length S.
 int64_t rowwise_waves(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R, int32_t M,
@@ -93,16 +118,12 @@ int64_t rowwise_waves(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R
 // that gives the grid roughly 32 wavefronts per compute unit.
 int32_t choose_split(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R, int32_t M,
                      int64_t rowwise_keys, int32_t Hkv, int64_t resident, const pa::PlanShape& ps) {
-  const int32_t B = ps.B;
-  const int64_t unit = 64 / gcd64(64, B) * B;
-  const int64_t cap = std::max<int64_t>(unit, (int64_t)64 * B);
-  const int forced = env_int("PA_SPLIT_TOKENS", 0);
-  if (forced > 0) {
-    int64_t s = (forced + unit - 1) / unit * unit;
-    return (int32_t)std::min(s, cap / unit * unit);
-  }
-  if (resident > 0 && rowwise_keys > 0 && env_int("PA_SPLIT_ONE_ROUND", 1) != 0) {
-    const int64_t longest = std::max<int64_t>(1, std::min<int64_t>(cap, 2048) / unit) * unit;
+  const SplitLengths sl = split_lengths(ps.B);
+  const int64_t unit = sl.unit;
+  const int64_t forced = forced_split(ps.B);
+  if (forced > 0) return (int32_t)forced;
+  if (resident > 0 && rowwise_keys > 0 && pa::tuning(PA_TUNE_SPLIT_RULE) != 1) {
+    const int64_t longest = sl.longest;
     if (rowwise_waves(h_qsl, h_seq_lens, R, M, Hkv, ps, (int32_t)longest) <= resident) {
       // the wave count does not grow with the length: binary search for the
       // smallest multiple of the unit that fits
@@ -117,24 +138,32 @@ int32_t choose_split(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R,
     const int64_t per_slot = rowwise_keys * Hkv / resident;
     return (int32_t)std::min(longest, std::max(unit, per_slot / unit * unit));
   }
-  int64_t top = unit;
-  while (top * 2 <= cap && top * 2 <= 1024) top *= 2;
   const int64_t target_waves = 256 * 32;
   const int64_t want = rowwise_keys * Hkv / target_waves;
   int64_t s = unit;
-  while (s < want && s * 2 <= top) s *= 2;
+  while (s < want && s * 2 <= sl.top) s *= 2;
   return (int32_t)s;
 }
 
-// Key-segment length of the chunk kernel: a multiple of 64 keys between 512
-// and the kernel's limit, sized so the chunk work spreads over about two
-// workgroups per compute unit (long histories are cut into segments that the
-// merge pass recombines; longer segments mean fewer partials to merge).
+// Key-segment lengths of the chunk kernel: multiples of 64 keys between
+// kMinSegment and the kernel's limit.
+constexpr int64_t kMinSegment = 512;
+constexpr int64_t kSegmentItemsTarget = 256 * 2;
+int64_t segment_limit(int32_t B) { return pa::chunk_max_segment(B) / 64 * 64; }
+int64_t forced_segment(int32_t B) {
+  const int64_t f = pa::tuning(PA_TUNE_CHUNK_SEGMENT);
+  return f > 0 ? std::min<int64_t>(segment_limit(B), (f + 63) / 64 * 64) : 0;
+}
+
+// Key-segment length of the chunk kernel, sized so the chunk work spreads
+// over about two workgroups per compute unit (long histories are cut into
+// segments that the merge pass recombines; longer segments mean fewer
+// partials to merge).
 int32_t choose_segment(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R, int32_t M,
                        int32_t B, int32_t Hkv, const pa::PlanShape& ps) {
-  const int64_t limit = pa::chunk_max_segment(B) / 64 * 64;
-  const int forced = env_int("PA_CHUNK_SEG", 0);
-  if (forced > 0) return (int32_t)std::min<int64_t>(limit, (forced + 63) / 64 * 64);
+  const int64_t limit = segment_limit(B);
+  const int64_t forced = forced_segment(B);
+  if (forced > 0) return (int32_t)forced;
   int64_t tiles = 0;  // 64-key tiles of all chunk work items, one kv head
   for (int32_t r = 0; r < R; ++r) {
     int32_t q = h_qsl[r + 1] - h_qsl[r];
@@ -147,14 +176,17 @@ int32_t choose_segment(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t 
       tiles += (kmax + 63) / 64;
     }
   }
-  const int64_t target_items = 256 * 2;
-  const int64_t target = std::max<int64_t>(1, tiles * Hkv / target_items) * 64;
+  const int64_t target = std::max<int64_t>(1, tiles * Hkv / kSegmentItemsTarget) * 64;
   // the power of two nearest the target (in ratio), or the limit when the
   // target is well above the largest power of two that fits
-  int64_t seg = 512;
+  int64_t seg = kMinSegment;
   while (seg * 2 <= limit && target * target > 2 * seg * seg) seg *= 2;
   if (seg * 2 > limit && target * target > 2 * seg * seg) seg = limit;
   return (int32_t)std::min(seg, limit);
+}
+
+bool plan_rowwise_all(bool bf16, int32_t D, int32_t G, int32_t B) {
+  return !pa::chunk_kernel_supports(bf16, D, G, B) || pa::tuning(PA_TUNE_CHUNK_PATH) == 1;
 }
 
 // Validates the host mirrors and fills the plan shape (exact table sizes).
@@ -168,6 +200,7 @@ pa_status make_plan(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R, 
   if (R > 0 && h_qsl[0] != 0) return fail(PA_ERR_INCONSISTENT_METADATA, "query_start_loc[0]=%d != 0", h_qsl[0]);
   if (R > 0 && h_qsl[R] != T)
     return fail(PA_ERR_INCONSISTENT_METADATA, "query_start_loc[R]=%d != T=%lld", h_qsl[R], (long long)T);
+  if (R == 0 && T != 0) return fail(PA_ERR_INCONSISTENT_METADATA, "T=%lld with no requests", (long long)T);
   const int64_t cap_tokens = (int64_t)M * B;
   int64_t rowwise_keys = 0;
   const int G = Hq / Hkv;
@@ -176,7 +209,7 @@ pa_status make_plan(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R, 
   ps.T = (int32_t)T;
   ps.M = M;
   ps.B = B;
-  ps.rowwise_all = pa::chunk_kernel_supports(bf16, D, G, B) && env_int("PA_FORCE_ROWWISE", 0) == 0 ? 0 : 1;
+  ps.rowwise_all = plan_rowwise_all(bf16, D, G, B) ? 1 : 0;
   ps.TQ = pa::chunk_tile_tokens(G);
   ps.MT = pa::chunk_merge_tokens(G);
   ps.SEG = 1 << 30;
@@ -216,7 +249,235 @@ pa_status make_plan(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R, 
   return PA_OK;
 }
 
+// Upper bounds of the plan's table sizes over every step with at most
+// R_max requests, T_max query rows and sequences of at most L_max keys, for
+// the partition and segment rules above.  Derivation (N = row-wise rows, K =
+// their total keys, W = the chunk tiles' 64-key tiles of one kv head, Nqt =
+// chunk q-tiles):
+//  * row-wise items: a row of k keys has cdiv(k, S) <= k/S + 1 partitions, so
+//    n_rw <= K/S + N with N <= Nmax (decode rows: min(R, T); every row when
+//    multi-token requests go row-wise too) and K <= Nmax L_max.  K/S:
+//    forced S: K/S directly.  Occupancy rule with R slots of waves: a
+//    one-round grid has n_rw Hkv <= R; otherwise S = unit when the keys per
+//    slot K Hkv / R are below a unit (then K/S < R/Hkv), S = floor(keys per
+//    slot to the unit) >= half the keys per slot (K/S <= 2 R/Hkv * 64/63 <
+//    3 R/Hkv), or S = longest (K/S <= K/longest).  Device-independent rule:
+//    S >= want = floor(K Hkv / 8192) gives K/S < 16384/Hkv, else S = top.
+//  * chunk q-tiles: Nqt <= floor(T/TQ) + Rck with Rck <= min(R, T/2) chunk
+//    requests; a tile has cdiv(kmax, SEG) <= cdiv(L_max, SEG) segments and
+//    SEG >= 512 (or the forced length): n_ck <= Nqt cdiv(L_max, SEG_min).
+//  * chunk partial slots: a split tile (nseg >= 2) has nseg < 2 kmax / SEG, so
+//    the slots are < 2 TQ sum(kmax)/SEG <= 2 TQ 64 W / SEG.  The segment rule
+//    takes SEG = the limit, or SEG >= target / sqrt 2 with target =
+//    max(1, floor(W Hkv / 512)) 64 >= W Hkv / 16 when W Hkv >= 512, so
+//    64 W / SEG < 1449 / Hkv; when W Hkv < 512, SEG >= 512 and 64 W / SEG <
+//    64 / Hkv.  At the limit the tiles hold <= Nqt cdiv(L_max, limit)
+//    segments.  Every case is also <= Nqt cdiv(L_max, SEG_min) per TQ.
+//  * merge records: one per split row-wise row (<= Nmax) and at most
+//    cdiv(TQ, MT) per chunk tile.
+struct PlanBound {
+  int64_t n_rw, n_ck, n_mg, n_ck_parts;
+};
+PlanBound plan_bound(int64_t R_max, int64_t T_max, int64_t L_max, int32_t Hq, int32_t Hkv, int32_t D,
+                     int32_t B, bool bf16) {
+  PlanBound b{0, 0, 0, 0};
+  if (R_max <= 0 || T_max <= 0 || L_max <= 0) return b;
+  const int32_t G = Hq / Hkv;
+  const bool all_rw = plan_rowwise_all(bf16, D, G, B);
+  const int64_t n_rows = all_rw ? T_max : std::min(R_max, T_max);
+  const int64_t K = n_rows * L_max;
+  const SplitLengths sl = split_lengths(B);
+  const int64_t forced = forced_split(B);
+  int64_t k_over_s;
+  if (forced > 0) {
+    k_over_s = cdiv64(K, forced);
+  } else {
+    const int64_t resident = pa::rowwise_round_slots(bf16, D, G);
+    if (resident > 0 && pa::tuning(PA_TUNE_SPLIT_RULE) != 1)
+      k_over_s = std::max(3 * cdiv64(resident, Hkv), cdiv64(K, sl.longest));
+    else
+      k_over_s = std::max(cdiv64(16384, Hkv), cdiv64(K, sl.top));
+  }
+  b.n_rw = n_rows + k_over_s;
+  b.n_mg = n_rows;
+  if (!all_rw) {
+    const int64_t TQ = pa::chunk_tile_tokens(G), MT = pa::chunk_merge_tokens(G);
+    const int64_t r_ck = std::min(R_max, T_max / 2);
+    const int64_t nqt = T_max / TQ + r_ck;
+    const int64_t limit = segment_limit(B);
+    const int64_t fseg = forced_segment(B);
+    const int64_t seg_min = fseg > 0 ? fseg : kMinSegment;
+    const int64_t segs_any = nqt * cdiv64(L_max, seg_min);
+    int64_t split_segs = segs_any;
+    if (fseg == 0)
+      split_segs = std::min(segs_any, std::max(cdiv64(2 * 1449, Hkv), nqt * cdiv64(L_max, limit)));
+    b.n_ck = segs_any;
+    b.n_ck_parts = cdiv64(L_max, seg_min) > 1 ? TQ * split_segs : 0;
+    b.n_mg += nqt * cdiv64(TQ, MT);
+  }
+  return b;
+}
+
+// Private layout of pa_step_plan (caller-owned, opaque).
+constexpr uint32_t kPlanMagic = 0x50414E31u;  // "PAN1"
+struct PlanRecord {
+  uint32_t magic;
+  int32_t device;
+  pa::PlanShape ps;
+  pa::WorkspaceLayout wl;
+  const int32_t* block_table;
+  const int32_t* qsl;
+  const int32_t* seq_lens;
+  const int32_t* num_computed;
+  char* ws;
+  int32_t Hq, Hkv, D, num_blocks;
+  int32_t bf16;
+};
+static_assert(sizeof(PlanRecord) <= sizeof(pa_step_plan), "plan record exceeds pa_step_plan");
+
+// Checks a step and fills the plan record on the host (nothing is enqueued).
+pa_status prepare_plan(PlanRecord* pr, const int32_t* block_table, int32_t M, const int32_t* qsl,
+                       const int32_t* seq_lens, const int32_t* num_computed, const int32_t* h_qsl,
+                       const int32_t* h_seq_lens, int32_t R, int64_t T, int32_t Hq, int32_t Hkv,
+                       int32_t D, int32_t num_blocks, int32_t B, pa_dtype dtype, void* workspace,
+                       size_t workspace_bytes) {
+  std::memset(pr, 0, sizeof *pr);
+  pa_status st = check_geometry(Hq, Hkv, D, B, num_blocks, dtype);
+  if (st != PA_OK) return st;
+  if (M <= 0) return fail(PA_ERR_BAD_SHAPE, "max_blocks_per_req=%d", M);
+  const bool bf16 = dtype == PA_BF16;
+  pa::PlanShape ps;
+  st = make_plan(h_qsl, h_seq_lens, R, T, M, Hq, Hkv, D, B, bf16, &ps);
+  if (st != PA_OK) return st;
+  pr->ps = ps;
+  pr->Hq = Hq;
+  pr->Hkv = Hkv;
+  pr->D = D;
+  pr->num_blocks = num_blocks;
+  pr->bf16 = bf16 ? 1 : 0;
+  pr->device = -1;
+  if (ps.n_rw > 0 || ps.n_ck > 0) {
+    if (!block_table || !qsl || !seq_lens || !num_computed || !workspace)
+      return fail(PA_ERR_NULL_PTR, "NULL device pointer");
+    if ((uintptr_t)workspace & 255) return fail(PA_ERR_BAD_SHAPE, "workspace must be 256-byte aligned");
+    const pa::WorkspaceLayout wl = pa::workspace_layout(ps, Hq, D);
+    if (workspace_bytes < wl.total)
+      return fail(PA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < needed %zu bytes", workspace_bytes, wl.total);
+    pr->wl = wl;
+    pr->block_table = block_table;
+    pr->qsl = qsl;
+    pr->seq_lens = seq_lens;
+    pr->num_computed = num_computed;
+    pr->ws = static_cast<char*>(workspace);
+  }
+  pr->magic = kPlanMagic;
+  return PA_OK;
+}
+
+// Records the current device in a prepared plan that has work (after every
+// host check, so that argument errors are reported as such without a device).
+pa_status bind_device(PlanRecord* pr) {
+  if (pr->ps.n_rw == 0 && pr->ps.n_ck == 0) return PA_OK;
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  pr->device = dev;
+  return PA_OK;
+}
+
+// Enqueues the device planner of a prepared plan (it writes the work tables
+// into the workspace).
+pa_status enqueue_plan(const PlanRecord* pr, hipStream_t s) {
+  const pa::PlanShape& ps = pr->ps;
+  if (ps.n_rw == 0 && ps.n_ck == 0) return PA_OK;
+  const pa::WorkspaceLayout& wl = pr->wl;
+  char* ws = pr->ws;
+  prof_mark(0, s);
+  const hipError_t e = pa::launch_plan(pr->qsl, pr->seq_lens, ps, reinterpret_cast<int4*>(ws + wl.off_rw),
+                                       reinterpret_cast<int4*>(ws + wl.off_rws),
+                                       reinterpret_cast<int32_t*>(ws + wl.off_rwslot),
+                                       reinterpret_cast<int4*>(ws + wl.off_ck),
+                                       reinterpret_cast<int4*>(ws + wl.off_cks),
+                                       reinterpret_cast<int4*>(ws + wl.off_mg), s);
+  if (e != hipSuccess) return hip_fail(e, "plan launch");
+  prof_mark(1, s);
+  return PA_OK;
+}
+
+// Checks one layer's arguments against a plan (nothing is enqueued); with
+// same_device, also that the current device is the plan's.
+pa_status check_run(const PlanRecord* pr, const void* out, const void* query, const void* key_cache,
+                    const void* value_cache, float scale, bool same_device) {
+  if (pr == nullptr) return fail(PA_ERR_NULL_PTR, "plan is NULL");
+  if (pr->magic != kPlanMagic) return fail(PA_ERR_BAD_STATE, "plan was not filled by pa_attention_plan");
+  if (!(scale > 0.f) || !(scale < 1e30f)) return fail(PA_ERR_BAD_SHAPE, "scale must be positive and finite");
+  if (pr->ps.n_rw == 0 && pr->ps.n_ck == 0) return PA_OK;
+  if (!out || !query || !key_cache || !value_cache) return fail(PA_ERR_NULL_PTR, "NULL device pointer");
+  const uintptr_t mis = (uintptr_t)out | (uintptr_t)query | (uintptr_t)key_cache | (uintptr_t)value_cache;
+  if (mis & 15) return fail(PA_ERR_BAD_SHAPE, "tensors must be 16-byte aligned");
+  if (same_device) {
+    int dev = 0;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev != pr->device) return fail(PA_ERR_BAD_STATE, "plan made on device %d, current device %d", pr->device, dev);
+  }
+  return PA_OK;
+}
+
+// Enqueues one layer's attention with a checked plan: row-wise split-K, chunk
+// (matrix cores), merge.
+pa_status run_step(const PlanRecord* pr, void* out, const void* query, const void* key_cache,
+                   const void* value_cache, float scale, hipStream_t s) {
+  const pa::PlanShape& ps = pr->ps;
+  if (ps.n_rw == 0 && ps.n_ck == 0) return PA_OK;
+  const pa::WorkspaceLayout& wl = pr->wl;
+  char* ws = pr->ws;
+  pa::AttnArgs a{};
+  a.out = out;
+  a.query = query;
+  a.kcache = key_cache;
+  a.vcache = value_cache;
+  a.block_table = pr->block_table;
+  a.qsl = pr->qsl;
+  a.seq_lens = pr->seq_lens;
+  a.num_computed = pr->num_computed;
+  a.M = ps.M;
+  a.R = ps.R;
+  a.Hq = pr->Hq;
+  a.Hkv = pr->Hkv;
+  a.D = pr->D;
+  a.B = ps.B;
+  a.num_blocks = pr->num_blocks;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.bf16 = pr->bf16 != 0;
+  a.ps = ps;
+  a.items_rw = reinterpret_cast<int4*>(ws + wl.off_rw);
+  a.rw_slot = reinterpret_cast<const int32_t*>(ws + wl.off_rwslot);
+  a.items_ck = reinterpret_cast<int4*>(ws + wl.off_ck);
+  a.merge = reinterpret_cast<int4*>(ws + wl.off_mg);
+  a.ml_part = reinterpret_cast<float*>(ws + wl.off_ml);
+  a.o_part = reinterpret_cast<float*>(ws + wl.off_o);
+
+  prof_mark(1, s);
+  hipError_t e = pa::launch_rowwise(a, s);
+  if (e != hipSuccess) return hip_fail(e, "row-wise attention launch");
+  prof_mark(2, s);
+  e = pa::launch_chunk(a, s);
+  if (e != hipSuccess) return hip_fail(e, "chunk attention launch");
+  prof_mark(3, s);
+  e = pa::launch_merge(a, s);
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  prof_mark(4, s);
+  return PA_OK;
+}
+
 }  // namespace
+
+namespace pa {
+int32_t tuning(int32_t knob) {
+  return knob >= 0 && knob < PA_TUNE_COUNT ? g_tune[knob].load(std::memory_order_relaxed) : 0;
+}
+}  // namespace pa
 
 extern "C" {
 
@@ -404,6 +665,20 @@ pa_status pa_copy_blocks(const void* src_pools, void* dst_pools, const int32_t* 
   return PA_OK;
 }
 
+size_t pa_attention_workspace_bound(int32_t max_num_reqs, int64_t max_num_tokens,
+                                   int32_t max_seq_len, int32_t num_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, pa_dtype dtype) {
+  g_err.clear();
+  if (check_geometry(num_heads, num_kv_heads, head_dim, block_size, 1, dtype) != PA_OK) return 0;
+  if (max_num_reqs < 0 || max_num_tokens < 0 || max_seq_len < 0) {
+    fail(PA_ERR_BAD_SHAPE, "negative step limit");
+    return 0;
+  }
+  const PlanBound b = plan_bound(max_num_reqs, max_num_tokens, max_seq_len, num_heads, num_kv_heads,
+                                 head_dim, block_size, dtype == PA_BF16);
+  return pa::workspace_layout_counts(b.n_rw, b.n_ck, b.n_mg, b.n_ck_parts, num_heads, head_dim).total;
+}
+
 size_t pa_attention_workspace_size(const int32_t* h_query_start_loc, const int32_t* h_seq_lens,
                                    int32_t R, int32_t num_heads, int32_t num_kv_heads,
                                    int32_t head_dim, int32_t block_size, pa_dtype dtype) {
@@ -425,6 +700,37 @@ size_t pa_attention_workspace_size(const int32_t* h_query_start_loc, const int32
   return pa::workspace_layout(ps, num_heads, head_dim).total;
 }
 
+pa_status pa_attention_plan(pa_step_plan* plan, const int32_t* block_table,
+                            int32_t max_blocks_per_req, const int32_t* query_start_loc,
+                            const int32_t* seq_lens, const int32_t* num_computed_tokens,
+                            const int32_t* h_query_start_loc, const int32_t* h_seq_lens,
+                            int32_t R, int64_t T, int32_t num_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                            pa_dtype dtype, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  g_err.clear();
+  if (plan == nullptr) return fail(PA_ERR_NULL_PTR, "plan is NULL");
+  PlanRecord* pr = reinterpret_cast<PlanRecord*>(plan);
+  pa_status st = prepare_plan(pr, block_table, max_blocks_per_req, query_start_loc, seq_lens,
+                              num_computed_tokens, h_query_start_loc, h_seq_lens, R, T, num_heads,
+                              num_kv_heads, head_dim, num_blocks, block_size, dtype, workspace,
+                              workspace_bytes);
+  if (st == PA_OK) st = bind_device(pr);
+  if (st == PA_OK) st = enqueue_plan(pr, reinterpret_cast<hipStream_t>(stream));
+  if (st != PA_OK) pr->magic = 0;
+  return st;
+}
+
+pa_status pa_attention_run(const pa_step_plan* plan, void* out, const void* query,
+                           const void* key_cache, const void* value_cache, float scale,
+                           void* stream) {
+  g_err.clear();
+  const PlanRecord* pr = reinterpret_cast<const PlanRecord*>(plan);
+  pa_status st = check_run(pr, out, query, key_cache, value_cache, scale, true);
+  if (st != PA_OK) return st;
+  return run_step(pr, out, query, key_cache, value_cache, scale, reinterpret_cast<hipStream_t>(stream));
+}
+
 pa_status pa_attention(void* out, const void* query, const void* key_cache,
                        const void* value_cache, const int32_t* block_table,
                        int32_t max_blocks_per_req, const int32_t* query_start_loc,
@@ -434,73 +740,33 @@ pa_status pa_attention(void* out, const void* query, const void* key_cache,
                        int32_t num_blocks, int32_t block_size, float scale, pa_dtype dtype,
                        void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
-  pa_status st = check_geometry(num_heads, num_kv_heads, head_dim, block_size, num_blocks, dtype);
-  if (st != PA_OK) return st;
-  if (max_blocks_per_req <= 0) return fail(PA_ERR_BAD_SHAPE, "max_blocks_per_req=%d", max_blocks_per_req);
-  const bool bf16 = dtype == PA_BF16;
-  pa::PlanShape ps;
-  st = make_plan(h_query_start_loc, h_seq_lens, R, T, max_blocks_per_req, num_heads, num_kv_heads,
-                 head_dim, block_size, bf16, &ps);
-  if (st != PA_OK) return st;
-  if (ps.n_rw == 0 && ps.n_ck == 0) return PA_OK;
-  if (!out || !query || !key_cache || !value_cache || !block_table || !query_start_loc ||
-      !seq_lens || !num_computed_tokens || !workspace)
-    return fail(PA_ERR_NULL_PTR, "NULL device pointer");
-  const uintptr_t mis = (uintptr_t)out | (uintptr_t)query | (uintptr_t)key_cache | (uintptr_t)value_cache;
-  if (mis & 15) return fail(PA_ERR_BAD_SHAPE, "tensors must be 16-byte aligned");
-  if ((uintptr_t)workspace & 255) return fail(PA_ERR_BAD_SHAPE, "workspace must be 256-byte aligned");
-  const pa::WorkspaceLayout wl = pa::workspace_layout(ps, num_heads, head_dim);
-  if (workspace_bytes < wl.total)
-    return fail(PA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < needed %zu bytes", workspace_bytes, wl.total);
-  if (!(scale > 0.f) || !(scale < 1e30f)) return fail(PA_ERR_BAD_SHAPE, "scale must be positive and finite");
-
-  char* ws = static_cast<char*>(workspace);
-  pa::AttnArgs a{};
-  a.out = out;
-  a.query = query;
-  a.kcache = key_cache;
-  a.vcache = value_cache;
-  a.block_table = block_table;
-  a.qsl = query_start_loc;
-  a.seq_lens = seq_lens;
-  a.num_computed = num_computed_tokens;
-  a.M = max_blocks_per_req;
-  a.R = R;
-  a.Hq = num_heads;
-  a.Hkv = num_kv_heads;
-  a.D = head_dim;
-  a.B = block_size;
-  a.num_blocks = num_blocks;
-  a.scale_log2 = scale * 1.4426950408889634f;
-  a.bf16 = bf16;
-  a.ps = ps;
-  a.items_rw = reinterpret_cast<int4*>(ws + wl.off_rw);
-  a.rw_slot = reinterpret_cast<const int32_t*>(ws + wl.off_rwslot);
-  a.items_ck = reinterpret_cast<int4*>(ws + wl.off_ck);
-  a.merge = reinterpret_cast<int4*>(ws + wl.off_mg);
-  a.ml_part = reinterpret_cast<float*>(ws + wl.off_ml);
-  a.o_part = reinterpret_cast<float*>(ws + wl.off_o);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  PlanRecord pr;
+  pa_status st = prepare_plan(&pr, block_table, max_blocks_per_req, query_start_loc, seq_lens,
+                              num_computed_tokens, h_query_start_loc, h_seq_lens, R, T, num_heads,
+                              num_kv_heads, head_dim, num_blocks, block_size, dtype, workspace,
+                              workspace_bytes);
+  if (st != PA_OK) return st;
+  st = check_run(&pr, out, query, key_cache, value_cache, scale, false);
+  if (st != PA_OK) return st;
+  st = bind_device(&pr);
+  if (st != PA_OK) return st;
+  st = enqueue_plan(&pr, s);
+  if (st != PA_OK) return st;
+  return run_step(&pr, out, query, key_cache, value_cache, scale, s);
+}
 
-  prof_mark(0, s);
-  hipError_t e = pa::launch_plan(query_start_loc, seq_lens, ps, a.items_rw,
-                                  reinterpret_cast<int4*>(ws + wl.off_rws),
-                                  reinterpret_cast<int32_t*>(ws + wl.off_rwslot), a.items_ck,
-                                  reinterpret_cast<int4*>(ws + wl.off_cks), a.merge, s);
-  if (e != hipSuccess) return hip_fail(e, "plan launch");
-  prof_mark(1, s);
-  e = pa::launch_rowwise(a, s);
-  if (e != hipSuccess) return hip_fail(e, "row-wise attention launch");
-  prof_mark(2, s);
-  e = pa::launch_chunk(a, s);
-  if (e != hipSuccess) return hip_fail(e, "chunk attention launch");
-  prof_mark(3, s);
-  e = pa::launch_merge(a, s);
-  if (e != hipSuccess) return hip_fail(e, "merge launch");
-  prof_mark(4, s);
+pa_status pa_set_tuning(int32_t knob, int32_t value) {
+  g_err.clear();
+  if (knob < 0 || knob >= PA_TUNE_COUNT) return fail(PA_ERR_BAD_SHAPE, "unknown tuning knob %d", knob);
+  if (value < 0) return fail(PA_ERR_BAD_SHAPE, "tuning value %d < 0", value);
+  g_tune[knob].store(value, std::memory_order_relaxed);
   return PA_OK;
 }
 
+int32_t pa_get_tuning(int32_t knob) {
+  return knob >= 0 && knob < PA_TUNE_COUNT ? g_tune[knob].load(std::memory_order_relaxed) : -1;
+}
 pa_status pa_validate_metadata(const int32_t* h_query_start_loc, const int32_t* h_seq_lens,
                                const int32_t* h_num_computed, const int32_t* h_block_table,
                                int32_t max_blocks_per_req, const int64_t* h_slot_mapping,

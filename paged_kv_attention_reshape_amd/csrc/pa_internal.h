@@ -242,21 +242,34 @@ struct WorkspaceLayout {
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-inline WorkspaceLayout workspace_layout(const PlanShape& ps, int32_t Hq, int32_t D) {
+// Workspace layout for table sizes n_rw, n_ck, n_mg and n_ck_parts.
+inline WorkspaceLayout workspace_layout_counts(int64_t n_rw, int64_t n_ck, int64_t n_mg, int64_t n_ck_parts,
+                                               int32_t Hq, int32_t D) {
   WorkspaceLayout w;
   size_t o = 0;
-  w.off_rw = o; o = align256(o + sizeof(int4) * (size_t)ps.n_rw);
-  w.off_rws = o; o = align256(o + sizeof(int4) * (size_t)ps.n_rw);      // items in plan order
-  w.off_rwslot = o; o = align256(o + sizeof(int32_t) * (size_t)ps.n_rw);
-  w.off_ck = o; o = align256(o + sizeof(int4) * (size_t)ps.n_ck);
-  w.off_cks = o; o = align256(o + sizeof(int4) * (size_t)ps.n_ck);   // chunk items before sorting
-  w.off_mg = o; o = align256(o + sizeof(int4) * (size_t)ps.n_mg);
-  const size_t parts = (size_t)ps.n_rw + (size_t)ps.n_ck_parts;
+  w.off_rw = o; o = align256(o + sizeof(int4) * (size_t)n_rw);
+  w.off_rws = o; o = align256(o + sizeof(int4) * (size_t)n_rw);      // items in plan order
+  w.off_rwslot = o; o = align256(o + sizeof(int32_t) * (size_t)n_rw);
+  w.off_ck = o; o = align256(o + sizeof(int4) * (size_t)n_ck);
+  w.off_cks = o; o = align256(o + sizeof(int4) * (size_t)n_ck);   // chunk items before sorting
+  w.off_mg = o; o = align256(o + sizeof(int4) * (size_t)n_mg);
+  const size_t parts = (size_t)n_rw + (size_t)n_ck_parts;
   w.off_ml = o; o = align256(o + sizeof(float) * 2 * parts * Hq);
   w.off_o = o;  o = align256(o + sizeof(float) * parts * Hq * D);
   w.total = o;
   return w;
 }
+
+inline WorkspaceLayout workspace_layout(const PlanShape& ps, int32_t Hq, int32_t D) {
+  return workspace_layout_counts(ps.n_rw, ps.n_ck, ps.n_mg, ps.n_ck_parts, Hq, D);
+}
+
+// ---------------------------------------------------------------------------
+// Overrides of the library's own choices, set through pa_set_tuning (tests and
+// measurements).  Every knob is 0 by default, which is the product behaviour;
+// the values are process-wide.
+// ---------------------------------------------------------------------------
+int32_t tuning(int32_t knob);
 
 // ---------------------------------------------------------------------------
 // launchers (each returns the launch's hipError_t)

@@ -56,6 +56,11 @@ def run_step(spec, pa, dev_inputs=None, stream=None, workspace=None):
     d["slot_mapping"] = torch.from_numpy(sm).to(d["query"].device)
     pa.write_kv(d["key"], d["value"], d["key_cache"], d["value_cache"], d["slot_mapping"], stream=stream)
     out = torch.empty_like(d["query"])
+    if workspace is None:
+        workspace = pa.alloc_workspace(
+            pa.attention_workspace_size(qsl, sl, spec.Hq, spec.Hkv, spec.D, spec.B,
+                                        pa.PA_BF16 if spec.dtype == "bf16" else pa.PA_F32),
+            d["query"].device)
     pa.attention(out, d["query"], d["key_cache"], d["value_cache"], d["block_table"],
                  d["query_start_loc"], d["seq_lens"], d["num_computed"], qsl, sl, spec.scale,
                  workspace=workspace, stream=stream)

@@ -53,7 +53,7 @@ def test_fork_copy_on_write_then_attention():
     vc = torch.empty_like(kc)
     kc.view(torch.int16).fill_(0x7FC0)
     vc.view(torch.int16).fill_(0x7FC0)
-    ws = pa.Workspace("cuda")
+    ws = pa.alloc_workspace(pa.attention_workspace_bound(8, 256, nb * B, HQ, HKV, D, B, pa.PA_BF16))
     owner_of = {}          # (sequence, position) -> whose token values live there
     copies_seen = 0
     checked = 0

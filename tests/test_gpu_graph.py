@@ -38,9 +38,11 @@ def test_step_graph_capture_and_replay():
     d = spec.device_inputs(device=dev)
     kc0, vc0 = d["key_cache"].clone(), d["value_cache"].clone()   # pre-write pools
     slots = torch.empty((spec.T,), dtype=torch.int64, device=dev)
-    ws = pa.Workspace(dev)
-    ws.get(pa.attention_workspace_size(spec.query_start_loc, spec.seq_lens, spec.Hq, spec.Hkv,
-                                       spec.D, spec.B, pa.PA_BF16))
+    # a workspace sized once from the step limits (as a serving loop would)
+    ws = pa.alloc_workspace(pa.attention_workspace_bound(spec.R, spec.T, int(spec.seq_lens.max()), spec.Hq,
+                                                         spec.Hkv, spec.D, spec.B, pa.PA_BF16), dev)
+    assert ws.numel() >= pa.attention_workspace_size(spec.query_start_loc, spec.seq_lens, spec.Hq, spec.Hkv,
+                                                     spec.D, spec.B, pa.PA_BF16)
 
     # eager reference on the original inputs
     kc, vc = kc0.clone(), vc0.clone()

@@ -188,10 +188,10 @@ def test_edge_shapes(idx):
 
 
 @pytest.mark.parametrize("split", [64, 128, 1024])
-def test_forced_partition_sizes(split, monkeypatch):
-    monkeypatch.setenv("PA_SPLIT_TOKENS", str(split))
+def test_forced_partition_sizes(split):
     spec = _small("bf16", 32, 8, 128, 16, [1, 1, 1, 7], [3000, 64, 63, 700], seed=split)
-    d, out, _ = run_step(spec, pa)
+    with pa.tuning(split_keys=split):
+        d, out, _ = run_step(spec, pa)
     torch.cuda.synchronize()
     err = check_requests(spec, out, d["key_cache"], d["value_cache"], range(spec.R), what=f"split{split}")
     say(f"split {split} err {err:.2e}")
@@ -269,7 +269,8 @@ def test_empty_and_noop_steps():
     out = torch.empty((0, 8, 64), dtype=torch.bfloat16, device="cuda")
     z = torch.zeros(1, dtype=torch.int32, device="cuda")
     pa.attention(out, out, kc, kc, torch.zeros((1, 1), dtype=torch.int32, device="cuda"), z,
-                 z[:0], z[:0], np.zeros(1, np.int32), np.zeros(0, np.int32), 0.125)
+                 z[:0], z[:0], np.zeros(1, np.int32), np.zeros(0, np.int32), 0.125,
+                 pa.alloc_workspace(256))
 
 
 def test_write_kv_skips_negative_slots():
@@ -302,23 +303,22 @@ CHUNK_CASES = [
 
 
 @pytest.mark.parametrize("idx", range(len(CHUNK_CASES)), ids=[f"chunk{i}" for i in range(len(CHUNK_CASES))])
-def test_chunk_kernel_shapes(idx, monkeypatch):
+def test_chunk_kernel_shapes(idx):
     Hq, Hkv, D, B, ql, cp, seg = CHUNK_CASES[idx]
-    if seg:
-        monkeypatch.setenv("PA_CHUNK_SEG", str(seg))
     spec = _small("bf16", Hq, Hkv, D, B, ql, cp, seed=300 + idx)
-    d, out, _ = run_step(spec, pa)
+    with pa.tuning(chunk_segment=seg):
+        d, out, _ = run_step(spec, pa)
     torch.cuda.synchronize()
     err = check_requests(spec, out, d["key_cache"], d["value_cache"], range(spec.R), what=f"chunk{idx}")
     say(f"chunk case {idx} err {err:.2e}")
 
 
-def test_chunk_kernel_agrees_with_rowwise_path(monkeypatch):
+def test_chunk_kernel_agrees_with_rowwise_path():
     spec = _small("bf16", 32, 8, 128, 16, [200, 1, 64], [300, 40, 0], seed=77)
     d, out_ck, _ = run_step(spec, pa)
-    monkeypatch.setenv("PA_FORCE_ROWWISE", "1")
     fresh = spec.device_inputs()
-    _, out_rw, _ = run_step(spec, pa, dev_inputs=fresh)
+    with pa.tuning(chunk_path=1):
+        _, out_rw, _ = run_step(spec, pa, dev_inputs=fresh)
     torch.cuda.synchronize()
     a = oracle.as_f64(storage_np(out_ck), "bf16")
     b = oracle.as_f64(storage_np(out_rw), "bf16")

@@ -1,0 +1,115 @@
+"""GPU tests of the planning interface: the workspace bound on the device
+(where the partition rule uses the device's occupancy), a step planned once
+and run for several layers (bitwise equal to one pa_attention call per
+layer), and a step whose device metadata disagrees with the host mirrors
+(the device plan then has fewer merge records than the host sized: the
+unused records are sentinels, so no stale record of an earlier step touches
+the rows of requests whose metadata agree)."""
+import numpy as np
+import pytest
+
+from helpers import say
+from workloads import configs, serving_trace as st
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import paged_kv_attention_reshape_amd as pa  # noqa: E402
+import test_workspace_bound as wb  # noqa: E402
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    say(f"\n[gpu-test] {request.node.name}")
+    yield
+    torch.cuda.synchronize()
+
+
+def test_bound_covers_steps_with_device_occupancy():
+    torch.cuda.set_device(0)
+    for name in ("c1", "c2", "c3", "c4"):
+        wb.test_bound_covers_the_configurations(name)
+    wb.test_bound_covers_every_serving_trace_step()
+    for knobs in wb.KNOBS:
+        wb.test_bound_covers_corner_and_random_steps(knobs)
+
+
+def _layer_inputs(spec, d, n_layers):
+    """Per-layer query and caches: the step's tensors scaled per layer (any
+    distinct values serve; the comparison is between two call sequences)."""
+    qs, kcs, vcs = [], [], []
+    for l in range(n_layers):
+        f = 1.0 + 0.25 * l
+        qs.append((d["query"].float() * f).to(d["query"].dtype))
+        kcs.append((d["key_cache"].float() * (2.0 - 0.2 * l)).to(d["key_cache"].dtype))
+        vcs.append((d["value_cache"].float() * f).to(d["value_cache"].dtype))
+    return qs, kcs, vcs
+
+
+@pytest.mark.parametrize("name", ["mixed-bf16", "mixed-f32"])
+def test_plan_once_run_per_layer_matches_per_layer_calls(name):
+    dtype = "bf16" if name.endswith("bf16") else "f32"
+    spec = configs.custom(name, dtype, 32, 8, 128, 16, [1, 1, 200, 1, 64, 1],
+                          [3000, 17, 900, 700, 0, 1500], 41)
+    d = spec.device_inputs()
+    qsl, sl, sm = pa.build_step_metadata(spec.query_lens, spec.num_computed, spec.block_table,
+                                         spec.B, spec.num_blocks)
+    pa.write_kv(d["key"], d["value"], d["key_cache"], d["value_cache"], torch.from_numpy(sm).cuda())
+    n_layers = 3
+    qs, kcs, vcs = _layer_inputs(spec, d, n_layers)
+    dt = pa.PA_BF16 if dtype == "bf16" else pa.PA_F32
+    ws = pa.alloc_workspace(pa.attention_workspace_bound(spec.R, spec.T, int(spec.seq_lens.max()), spec.Hq,
+                                                         spec.Hkv, spec.D, spec.B, dt))
+    ref = []
+    for l in range(n_layers):
+        o = torch.empty_like(qs[l])
+        pa.attention(o, qs[l], kcs[l], vcs[l], d["block_table"], d["query_start_loc"], d["seq_lens"],
+                     d["num_computed"], qsl, sl, spec.scale, ws)
+        ref.append(o)
+    torch.cuda.synchronize()
+    plan = pa.attention_plan(d["block_table"], d["query_start_loc"], d["seq_lens"], d["num_computed"],
+                             qsl, sl, spec.Hq, kcs[0].shape, dt, ws)
+    outs = []
+    for l in range(n_layers):
+        o = torch.empty_like(qs[l])
+        pa.attention_run(plan, o, qs[l], kcs[l], vcs[l], spec.scale)
+        outs.append(o)
+    torch.cuda.synchronize()
+    iv = torch.int16 if dtype == "bf16" else torch.int32
+    for l in range(n_layers):
+        assert torch.equal(outs[l].view(iv), ref[l].view(iv)), f"layer {l} differs"
+    # the layers really differ (the runs did not all read layer 0)
+    assert not torch.equal(outs[0].view(iv), outs[1].view(iv))
+
+
+def test_device_metadata_shorter_than_mirrors_leaves_other_rows_intact():
+    """Request 0 (a decode of 3000 keys, split over several partitions) is cut
+    to 16 keys on the device only: the device plan then has one merge record
+    fewer than the host sized, in a workspace still holding the consistent
+    step's tables.  Rows of every other request equal the consistent step's
+    bit for bit."""
+    spec = configs.custom("short-dev", "bf16", 32, 8, 128, 16, [1, 1, 64, 1, 1, 40],
+                          [2999, 1500, 700, 2500, 60, 1200], 43)
+    d = spec.device_inputs()
+    qsl, sl, sm = pa.build_step_metadata(spec.query_lens, spec.num_computed, spec.block_table,
+                                         spec.B, spec.num_blocks)
+    pa.write_kv(d["key"], d["value"], d["key_cache"], d["value_cache"], torch.from_numpy(sm).cuda())
+    short = d["seq_lens"].clone()
+    short[0] = 16
+    ref = torch.empty_like(d["query"])
+    out = torch.full_like(d["query"], 7.0)
+    with pa.tuning(split_keys=256):       # request 0 splits at 3000 keys, not at 16
+        ws = pa.alloc_workspace(pa.attention_workspace_size(qsl, sl, spec.Hq, spec.Hkv, spec.D, spec.B,
+                                                            pa.PA_BF16))
+        pa.attention(ref, d["query"], d["key_cache"], d["value_cache"], d["block_table"], d["query_start_loc"],
+                     d["seq_lens"], d["num_computed"], qsl, sl, spec.scale, ws)
+        torch.cuda.synchronize()
+        pa.attention(out, d["query"], d["key_cache"], d["value_cache"], d["block_table"], d["query_start_loc"],
+                     short, d["num_computed"], qsl, sl, spec.scale, ws)
+    torch.cuda.synchronize()
+    t0 = int(spec.query_start_loc[1])
+    assert torch.equal(out[t0:].view(torch.int16), ref[t0:].view(torch.int16))
+    assert bool(torch.isfinite(out[0].float()).all())

@@ -162,8 +162,9 @@ def test_rope_then_attention_end_to_end():
     qsl, sl, _ = pa.build_step_metadata(spec.query_lens, spec.num_computed, spec.block_table,
                                         spec.B, spec.num_blocks)
     out = torch.empty_like(d["query"])
+    ws = pa.alloc_workspace(pa.attention_workspace_size(qsl, sl, spec.Hq, spec.Hkv, spec.D, spec.B, pa.PA_BF16))
     pa.attention(out, d["query"], d["key_cache"], d["value_cache"], d["block_table"],
-                 d["query_start_loc"], d["seq_lens"], d["num_computed"], qsl, sl, spec.scale)
+                 d["query_start_loc"], d["seq_lens"], d["num_computed"], qsl, sl, spec.scale, ws)
     torch.cuda.synchronize()
     # oracle: rotate the step's rows, store them as bf16 (the cache and the
     # query are bf16 tensors), write into the host pool, attend

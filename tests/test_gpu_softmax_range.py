@@ -97,7 +97,9 @@ def test_chunk_softmax_wide_dynamic_range(case):
     scale = 1.0 / np.sqrt(D)
     out = torch.empty_like(x["q"])
     pa.attention(out, x["q"], x["kc"], x["vc"], x["bt"], x["qsl"], x["sl"], x["comp"],
-                 x["h_qsl"], x["h_sl"], scale, workspace=pa.Workspace("cuda"))
+                 x["h_qsl"], x["h_sl"], scale,
+                 workspace=pa.alloc_workspace(pa.attention_workspace_size(x["h_qsl"], x["h_sl"], Hq, Hkv, D, B,
+                                                                          pa.PA_BF16)))
     torch.cuda.synchronize()
     kc, vc, q_all, o_all = storage_np(x["kc"]), storage_np(x["vc"]), storage_np(x["q"]), storage_np(out)
     worst = 0.0

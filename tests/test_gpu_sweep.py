@@ -84,17 +84,14 @@ WIDE = [_wide_case(i) for i in range(64)]
 
 
 @pytest.mark.parametrize("i", range(len(WIDE)), ids=[f"wide{i}" for i in range(len(WIDE))])
-def test_wide_random_steps_match_oracle(i, monkeypatch):
+def test_wide_random_steps_match_oracle(i):
     dtype, Hq, Hkv, D, B, qlens, comp, mfma, split = WIDE[i]
-    monkeypatch.delenv("PA_DECODE_MFMA", raising=False)
-    monkeypatch.delenv("PA_SPLIT_TOKENS", raising=False)
-    if mfma is not None:
-        monkeypatch.setenv("PA_DECODE_MFMA", mfma)
-    if split is not None:
-        monkeypatch.setenv("PA_SPLIT_TOKENS", split)
     say(f"\n[gpu-test] wide random step {i}: {WIDE[i]}")
     spec = configs.custom(f"wide{i}", dtype, Hq, Hkv, D, B, qlens, comp, seed=20000 + i, pool_factor=1.3)
-    d, out, _ = run_step(spec, pa)
+    knobs = {"decode_kernel": None if mfma is None else (2 if mfma == "1" else 1),
+             "split_keys": None if split is None else int(split)}
+    with pa.tuning(**knobs):
+        d, out, _ = run_step(spec, pa)
     torch.cuda.synchronize()
     err = check_requests(spec, out, d["key_cache"], d["value_cache"], range(spec.R),
                          rows_per_req=6, what=f"wide random step {i}")
@@ -104,18 +101,17 @@ def test_wide_random_steps_match_oracle(i, monkeypatch):
 @pytest.mark.parametrize("kernel", ["matrix", "vector"])
 @pytest.mark.parametrize("shape", [(32, 8, 128, 16), (64, 8, 128, 32), (16, 8, 64, 16)],
                          ids=["g4-d128-b16", "g8-d128-b32", "g2-d64-b16"])
-def test_more_than_64_partitions_forced(kernel, shape, monkeypatch):
+def test_more_than_64_partitions_forced(kernel, shape):
     """64-key partitions over up to 9000 keys: up to 141 partials per row.
     (With 2 q heads per kv head both settings run the vector kernel, the only
     one with that instance.)"""
     Hq, Hkv, D, B = shape
-    monkeypatch.setenv("PA_DECODE_MFMA", "1" if kernel == "matrix" else "0")
-    monkeypatch.setenv("PA_SPLIT_TOKENS", "64")
     qlens = [1, 1, 1, 1]
     comp = [4095, 4096 + 63, 8999, 130]
     spec = configs.custom(f"p64-{kernel}-{Hq}", "bf16", Hq, Hkv, D, B, qlens, comp,
                           seed=71 + Hq, pool_factor=1.2)
-    d, out, _ = run_step(spec, pa)
+    with pa.tuning(decode_kernel=2 if kernel == "matrix" else 1, split_keys=64):
+        d, out, _ = run_step(spec, pa)
     torch.cuda.synchronize()
     err = check_requests(spec, out, d["key_cache"], d["value_cache"], range(spec.R),
                          what=f"{kernel} {shape} split 64")

@@ -75,7 +75,9 @@ def test_serving_trace_200_steps_32_layers():
     vc = torch.empty_like(kc)
     kc.view(torch.int16).fill_(0x7FC0)   # NaN everywhere before the trace writes
     vc.view(torch.int16).fill_(0x7FC0)
-    ws = pa.Workspace("cuda")
+    # one workspace for the whole trace, sized by the scheduler's limits
+    ws = pa.alloc_workspace(pa.attention_workspace_bound(cfg.max_num_seqs, cfg.max_num_batched_tokens,
+                                                         st.max_seq_len(cfg), HQ, HKV, D, B, pa.PA_BF16))
     worst = 0.0
     n_checked = 0
     for p in plans:
@@ -93,13 +95,14 @@ def test_serving_trace_200_steps_32_layers():
         k = torch.empty((T, HKV, D), dtype=torch.bfloat16, device="cuda")
         v = torch.empty_like(k)
         out = torch.empty_like(q)
+        # the step is planned once; every layer runs with the same plan
+        plan = pa.attention_plan(d_bt, d_qsl, d_sl, d_nc, qsl, sl, HQ, kc.shape[1:], pa.PA_BF16, ws)
         for layer in range(LAYERS):
             _fill_rows(q, token_row_keys(cfg.seed, rng.TAG_Q, layer, rids, pos))
             _fill_rows(k, token_row_keys(cfg.seed, rng.TAG_K, layer, rids, pos))
             _fill_rows(v, token_row_keys(cfg.seed, rng.TAG_V, layer, rids, pos))
             pa.write_kv(k, v, kc[layer], vc[layer], d_sm)
-            pa.attention(out, q, kc[layer], vc[layer], d_bt, d_qsl, d_sl, d_nc, qsl, sl, scale,
-                         workspace=ws)
+            pa.attention_run(plan, out, q, kc[layer], vc[layer], scale)
             if layer in KEEP_LAYERS:
                 idx, keys = [], []
                 for i, (rid, c, n) in enumerate(p['sched']):

@@ -144,6 +144,12 @@ def token_row_keys(seed: int, tag: int, layer: int, rids, positions) -> np.ndarr
     return rng.derive(k, np.asarray(positions, dtype=np.uint64))
 
 
+def max_seq_len(cfg: TraceConfig) -> int:
+    """Longest sequence any step of the trace can hold: a request's length is
+    its prompt plus the tokens it has generated, at most one per step."""
+    return int(cfg.prompt_max + cfg.steps)
+
+
 def step_arrays(plan: dict, block_size: int):
     """Host arrays of one planned step: query lens, computed counts, block
     table [R, M] (-1 padded), request ids and token positions in flattened
