@@ -388,6 +388,34 @@ pa_status pa_set_tuning(int32_t knob, int32_t value);
 int32_t pa_get_tuning(int32_t knob);
 
 /*
+ * pa_attention_noalloc -- pa_attention without a caller workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).
+ *
+ * Same arguments, checks and results as pa_attention, minus workspace and
+ * workspace_bytes: the step's plan tables and partial results go to a static
+ * device array of PA_NOALLOC_SCRATCH_BYTES bytes that the library holds on
+ * every GPU it runs on until the process ends.  The call allocates nothing.
+ * A step whose workspace (pa_attention_workspace_size) exceeds
+ * PA_NOALLOC_SCRATCH_BYTES is refused with PA_ERR_WORKSPACE_TOO_SMALL before
+ * anything is enqueued.  Nothing in the scratch needs clearing between calls
+ * (every table is rewritten by each call's planner).  All calls on one GPU
+ * share its scratch: calls that overlap on one GPU (different streams or
+ * threads without ordering) race and give wrong results; order them on one
+ * stream.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+pa_status pa_attention_noalloc(void* out, const void* query, const void* key_cache,
+                               const void* value_cache, const int32_t* block_table,
+                               int32_t max_blocks_per_req, const int32_t* query_start_loc,
+                               const int32_t* seq_lens, const int32_t* num_computed_tokens,
+                               const int32_t* h_query_start_loc, const int32_t* h_seq_lens,
+                               int32_t R, int64_t T, int32_t num_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                               float scale, pa_dtype dtype, void* stream);
+
+/*
  * pa_set_profiling_events -- optional per-kernel timing hook (tests and
  * benchmarks).
  *

@@ -7,7 +7,8 @@ library; the first call does, and raises if it has not been built.
 """
 from ._lib import (  # noqa: F401
     EXPORTS, LIB_PATH, PA_BF16, PA_F32, TUNING, PAError, StepPlan, abi_version, alloc_workspace,
-    attention, attention_plan, attention_run, attention_workspace_bound, attention_workspace_size,
+    NOALLOC_SCRATCH_BYTES, attention, attention_noalloc, attention_plan, attention_run,
+    attention_workspace_bound, attention_workspace_size,
     build_step_metadata, compute_slot_mapping, copy_blocks, get_tuning, last_error, lib,
     rope_write_kv, set_profiling_events, set_tuning, status_str, tuning, validate_metadata,
     write_kv,

@@ -30,6 +30,7 @@ EXPORTS = [
     "pa_abi_version", "pa_status_str", "pa_last_error", "pa_build_step_metadata",
     "pa_compute_slot_mapping", "pa_write_kv", "pa_attention_workspace_size",
     "pa_attention_workspace_bound", "pa_attention", "pa_attention_plan", "pa_attention_run",
+    "pa_attention_noalloc",
     "pa_set_tuning", "pa_get_tuning", "pa_set_profiling_events", "pa_validate_metadata",
     "pa_rope_write_kv", "pa_copy_blocks",
 ]
@@ -122,6 +123,11 @@ def lib():
                                _i32p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                                ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                ctypes.c_float, ctypes.c_int, _vp, ctypes.c_size_t, _vp]
+    L.pa_attention_noalloc.restype = ctypes.c_int
+    L.pa_attention_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp, _i32p,
+                                       _i32p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_float, ctypes.c_int, _vp]
     L.pa_validate_metadata.restype = ctypes.c_int
     L.pa_validate_metadata.argtypes = [_i32p, _i32p, _i32p, _i32p, ctypes.c_int32, _i64p,
                                        ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
@@ -339,6 +345,26 @@ def attention(out, query, key_cache, value_cache, block_table, query_start_loc, 
                               _ptr(num_computed), _p32(qsl), _p32(sl), R, T, Hq, Hkv, D, N, B,
                               float(scale), _dtype_code(query), wp, wn,
                               ctypes.c_void_p(_stream(stream))), "pa_attention")
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20   # PA_NOALLOC_SCRATCH_BYTES
+
+
+def attention_noalloc(out, query, key_cache, value_cache, block_table, query_start_loc, seq_lens,
+                      num_computed, h_query_start_loc, h_seq_lens, scale: float, stream=None) -> None:
+    """attention() without a workspace argument (pa_attention_noalloc): the
+    library's static scratch holds the step's tables and partial results."""
+    T, Hq, D = query.shape
+    N, B, Hkv, _ = key_cache.shape
+    R = int(seq_lens.shape[0])
+    qsl = _np_i32(h_query_start_loc)
+    sl = _np_i32(h_seq_lens)
+    M = block_table.shape[1] if block_table.dim() == 2 else 1
+    _check(lib().pa_attention_noalloc(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
+                                      _ptr(block_table), M, _ptr(query_start_loc), _ptr(seq_lens),
+                                      _ptr(num_computed), _p32(qsl), _p32(sl), R, T, Hq, Hkv, D, N, B,
+                                      float(scale), _dtype_code(query), ctypes.c_void_p(_stream(stream))),
+           "pa_attention_noalloc")
 
 
 class StepPlan:

@@ -14,6 +14,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -44,6 +45,33 @@ pa_status hip_fail(hipError_t e, const char* what) {
 }
 
 std::atomic<int32_t> g_tune[PA_TUNE_COUNT];
+
+// Static scratch of pa_attention_noalloc.  In host code `scratch` names a
+// host-side stand-in, not device memory: the device address comes from
+// hipGetSymbolAddress, once per device (each GPU holds its own copy), and
+// only that address is ever passed to kernels.
+__device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (looked up on first use).
+pa_status scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(PA_ERR_UNSUPPORTED, "device %d beyond %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(PA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PA_OK;
+}
 
 pa_status check_geometry(int32_t Hq, int32_t Hkv, int32_t D, int32_t B, int32_t num_blocks,
                          int dtype) {
@@ -746,6 +774,37 @@ pa_status pa_attention(void* out, const void* query, const void* key_cache,
                               num_computed_tokens, h_query_start_loc, h_seq_lens, R, T, num_heads,
                               num_kv_heads, head_dim, num_blocks, block_size, dtype, workspace,
                               workspace_bytes);
+  if (st != PA_OK) return st;
+  st = check_run(&pr, out, query, key_cache, value_cache, scale, false);
+  if (st != PA_OK) return st;
+  st = bind_device(&pr);
+  if (st != PA_OK) return st;
+  st = enqueue_plan(&pr, s);
+  if (st != PA_OK) return st;
+  return run_step(&pr, out, query, key_cache, value_cache, scale, s);
+}
+
+pa_status pa_attention_noalloc(void* out, const void* query, const void* key_cache,
+                               const void* value_cache, const int32_t* block_table,
+                               int32_t max_blocks_per_req, const int32_t* query_start_loc,
+                               const int32_t* seq_lens, const int32_t* num_computed_tokens,
+                               const int32_t* h_query_start_loc, const int32_t* h_seq_lens,
+                               int32_t R, int64_t T, int32_t num_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                               float scale, pa_dtype dtype, void* stream) {
+  g_err.clear();
+  void* ws = nullptr;
+  pa_status st = scratch_address(&ws);
+  if (st != PA_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  PlanRecord pr;
+  st = prepare_plan(&pr, block_table, max_blocks_per_req, query_start_loc, seq_lens,
+                    num_computed_tokens, h_query_start_loc, h_seq_lens, R, T, num_heads, num_kv_heads,
+                    head_dim, num_blocks, block_size, dtype, ws, PA_NOALLOC_SCRATCH_BYTES);
+  if (st == PA_ERR_WORKSPACE_TOO_SMALL)
+    return fail(st, "the step needs %zu bytes of workspace, more than the %zu-byte static scratch of "
+                "pa_attention_noalloc (use pa_attention with a caller workspace)",
+                pa::workspace_layout(pr.ps, num_heads, head_dim).total, (size_t)PA_NOALLOC_SCRATCH_BYTES);
   if (st != PA_OK) return st;
   st = check_run(&pr, out, query, key_cache, value_cache, scale, false);
   if (st != PA_OK) return st;

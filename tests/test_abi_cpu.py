@@ -257,3 +257,9 @@ def test_generator_host_mirror_properties():
     hb = rng.f32_to_bf16_bits(x)
     back = oracle.bf16_bits_to_f64(hb)
     assert back.tolist() == [1.0, 1.0 + 4 * 2 ** -8, -1.5]   # ties to even
+
+
+def test_noalloc_scratch_size_matches_header():
+    txt = open(os.path.join(ROOT, "include", "pa.h")).read()
+    m = re.search(r"#define PA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", txt)
+    assert m and int(m.group(1)) << int(m.group(2)) == pa.NOALLOC_SCRATCH_BYTES
