@@ -132,3 +132,72 @@ def sample_requests(spec, n, seed=0, must=()):
             break
         pick.add(int(r))
     return sorted(pick)
+
+
+def check_full_step(spec, pre_k, pre_v, out_t, kc_t, vc_t, what="", spot_blocks=16):
+    """Whole-step parity.  pre_k / pre_v are device clones of the generator's
+    pools taken before the step (the device generator equals its host mirror
+    bit for bit; `spot_blocks` random blocks are re-checked against the host
+    mirror here).  For every request: the oracle's own slot mapping and write
+    on the request's pre-step blocks, then its attention for every query row;
+    the GPU rows must be within the dtype's tolerance and the request's blocks
+    after the step bit-exact.  Every slot outside the step's written slots
+    must be unchanged (compared on the device, in slabs).
+    Returns (worst abs err, rows checked, slots written)."""
+    import torch
+    dev = kc_t.device
+    g = np.random.default_rng(spec.seed)
+    spot = g.choice(spec.num_blocks, min(spot_blocks, spec.num_blocks), replace=False)
+    for which, pre in (("k", pre_k), ("v", pre_v)):
+        host = spec.host_pool_blocks(which, spot)
+        got = storage_np(pre.index_select(0, torch.from_numpy(spot.astype(np.int64)).to(dev)))
+        assert np.array_equal(bits(got), bits(host)), f"{what}: generator pool differs from its host mirror"
+    T = spec.T
+    rows = np.arange(T)
+    q_all = spec.host_rows("q", rows)
+    k_all = spec.host_rows("k", rows)
+    v_all = spec.host_rows("v", rows)
+    out_all = oracle.as_f64(storage_np(out_t), spec.dtype)
+    worst, n_rows = 0.0, 0
+    written = []
+    for r in range(spec.R):
+        q = int(spec.query_lens[r])
+        if q == 0:
+            continue
+        c = int(spec.num_computed[r])
+        L = q + c
+        B = spec.B
+        nblk = -(-L // B)
+        ids = spec.block_table[r, :nblk].astype(np.int64)
+        idx = torch.from_numpy(ids).to(dev)
+        kp = storage_np(pre_k.index_select(0, idx)).copy()
+        vp = storage_np(pre_v.index_select(0, idx)).copy()
+        t0 = int(spec.query_start_loc[r])
+        mini = np.arange(nblk, dtype=np.int32)[None]
+        slots = oracle.slot_mapping(mini, [q], [c], B)
+        oracle.write_kv(kp, vp, k_all[t0:t0 + q], v_all[t0:t0 + q], slots, B)
+        written.append(ids[slots // B] * B + slots % B)
+        assert np.array_equal(bits(storage_np(kc_t.index_select(0, idx))), bits(kp)), \
+            f"{what}: key cache blocks of request {r} differ"
+        assert np.array_equal(bits(storage_np(vc_t.index_select(0, idx))), bits(vp)), \
+            f"{what}: value cache blocks of request {r} differ"
+        K = oracle.gather_kv(kp, mini[0], L, B)
+        V = oracle.gather_kv(vp, mini[0], L, B)
+        want, _ = oracle.attention_rows(q_all[t0:t0 + q], K, V, c + np.arange(q), spec.scale, spec.dtype)
+        worst = max(worst, assert_close(out_all[t0:t0 + q], want, spec.dtype, f"{what} request {r}"))
+        n_rows += q
+    written = np.sort(np.concatenate(written)) if written else np.zeros(0, np.int64)
+    # every slot the step did not write keeps its pre-step bits
+    slot_w = spec.Hkv * spec.D
+    iv = torch.int16 if spec.dtype == "bf16" else torch.int32
+    for post, pre in ((kc_t, pre_k), (vc_t, pre_v)):
+        a = post.view(iv).reshape(-1, slot_w)
+        b = pre.view(iv).reshape(-1, slot_w)
+        changed = []
+        step = 1 << 20
+        for s0 in range(0, a.shape[0], step):
+            ch = torch.nonzero((a[s0:s0 + step] != b[s0:s0 + step]).any(dim=1)).flatten() + s0
+            changed.append(ch.cpu().numpy())
+        changed = np.concatenate(changed)
+        assert np.all(np.isin(changed, written)), f"{what}: slots outside the step's writes changed"
+    return worst, n_rows, len(written)

@@ -2,9 +2,10 @@
 
 Cache writes and slot mappings must match bit for bit; attention outputs
 within atol = rtol = 1e-5 (fp32) or 1e-2 (bf16), elementwise.  Inputs are the
-seeded synthetic steps of workloads.configs; large steps are checked on
-sampled requests (every cache block those requests own, and sampled query
-rows), which the oracle computes one request at a time.
+seeded synthetic steps of workloads.configs.  C1 is compared whole; C2, C3
+and C4 row by row over every request (the oracle computes one request at a
+time from the generator's pre-write pool blocks), with every written slot
+bit-exact and every other slot of the pools unchanged.
 """
 import math
 import os
@@ -13,7 +14,7 @@ import numpy as np
 import pytest
 
 import oracle
-from helpers import (assert_close, bits, check_requests, oracle_request, run_step,
+from helpers import (assert_close, bits, check_full_step, check_requests, oracle_request, run_step,
                      sample_requests, say, storage_np)
 from workloads import configs, rng
 
@@ -79,38 +80,30 @@ def test_c1_tiny_mixed_fp32_full():
     say(f"c1 max abs err {err:.2e}")
 
 
-def test_c2_decode_bf16_sampled():
-    spec = configs.c2()
-    d, out, _ = run_step(spec, pa)
+def _full(spec):
+    """Run the step with the generator's pre-write pools kept aside, then check
+    every row, every written slot and every untouched slot."""
+    d = spec.device_inputs()
+    pre_k, pre_v = d["key_cache"].clone(), d["value_cache"].clone()
+    d, out, _ = run_step(spec, pa, dev_inputs=d)
     torch.cuda.synchronize()
-    longest = int(np.argmax(spec.seq_lens))
-    reqs = sample_requests(spec, 12, seed=2, must=[longest, 0, spec.R - 1])
-    err = check_requests(spec, out, d["key_cache"], d["value_cache"], reqs, what="c2")
-    say(f"c2 requests {reqs} max abs err {err:.2e}")
+    err, n_rows, n_slots = check_full_step(spec, pre_k, pre_v, out, d["key_cache"], d["value_cache"],
+                                           what=spec.name)
+    say(f"{spec.name}: all {n_rows} rows of {spec.R} requests within tolerance (max abs err {err:.2e}); "
+        f"{n_slots} written slots bit-exact, every other slot unchanged")
+    assert n_rows == spec.T
 
 
-def test_c3_mixed_chunked_bf16_sampled():
-    spec = configs.c3()
-    d, out, _ = run_step(spec, pa)
-    torch.cuda.synchronize()
-    chunks = [int(r) for r in np.nonzero(spec.query_lens > 1)[0]]
-    longest_dec = int(np.argmax(np.where(spec.query_lens == 1, spec.seq_lens, 0)))
-    dec = sample_requests(spec, 10, seed=3, must=[longest_dec])
-    dec = [r for r in dec if spec.query_lens[r] == 1]
-    err = check_requests(spec, out, d["key_cache"], d["value_cache"], chunks, rows_per_req=20,
-                         what="c3 chunk")
-    err2 = check_requests(spec, out, d["key_cache"], d["value_cache"], dec, what="c3 decode")
-    say(f"c3 chunk reqs {chunks} offsets {spec.num_computed[chunks].tolist()} err {err:.2e}; decode err {err2:.2e}")
+def test_c2_decode_bf16_full():
+    _full(configs.c2())
 
 
-def test_c4_long_decode_bf16_sampled():
-    spec = configs.c4()
-    d, out, _ = run_step(spec, pa)
-    torch.cuda.synchronize()
-    longs = [int(r) for r in np.nonzero(spec.seq_lens == 32768)[0][:3]]
-    reqs = sample_requests(spec, 10, seed=4, must=longs)
-    err = check_requests(spec, out, d["key_cache"], d["value_cache"], reqs, what="c4")
-    say(f"c4 requests {reqs} max abs err {err:.2e}")
+def test_c3_mixed_chunked_bf16_full():
+    _full(configs.c3())
+
+
+def test_c4_long_decode_bf16_full():
+    _full(configs.c4())
 
 
 def test_determinism_bitwise():
