@@ -62,6 +62,10 @@ def parse():
                    help="skip the separate timing of the fused rotary + cache-write kernel")
     p.add_argument("--no-serving", dest="serving", action="store_false",
                    help="skip the 32-layer serving-trace throughput measurement")
+    p.add_argument("--no-extra", dest="extra", action="store_false",
+                   help="skip the pure-decode and long-context decode configurations and their oracle timings")
+    p.add_argument("--serving-only", action="store_true",
+                   help="run only the serving-trace measurement (for profiling runs)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="instead of the step, run a plain 1 GiB device copy a few times "
                         "(reference for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -84,6 +88,42 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
 
 
+def _host(t):
+    import numpy as np
+    import torch
+    t = t.detach().cpu()
+    return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+
+def oracle_request_seconds(spec, d, r) -> float:
+    """Time the fp64 oracle on request r of a step: its slot mapping, cache
+    write, gather and attention.  Inputs: the generator's pre-write pool
+    blocks of the request and its query / new K/V rows, copied from the
+    device before any step ran (not timed)."""
+    import numpy as np
+    import torch
+    import oracle
+    q = int(spec.query_lens[r])
+    L = int(spec.seq_lens[r])
+    c = L - q
+    nblk = -(-L // spec.B)
+    ids = torch.from_numpy(spec.block_table[r, :nblk].astype(np.int64)).to(d["key_cache"].device)
+    kp = _host(d["key_cache"].index_select(0, ids))
+    vp = _host(d["value_cache"].index_select(0, ids))
+    t = int(spec.query_start_loc[r])
+    qrows = _host(d["query"][t:t + q])
+    knew = _host(d["key"][t:t + q])
+    vnew = _host(d["value"][t:t + q])
+    mini = np.arange(nblk, dtype=np.int32)[None]
+    t0 = time.perf_counter()
+    sm = oracle.slot_mapping(mini, [q], [c], spec.B)
+    oracle.write_kv(kp, vp, knew, vnew, sm, spec.B)
+    K = oracle.gather_kv(kp, mini[0], L, spec.B)
+    V = oracle.gather_kv(vp, mini[0], L, spec.B)
+    oracle.attention_rows(qrows, K, V, c + np.arange(q), spec.scale, spec.dtype)
+    return time.perf_counter() - t0
+
+
 def cpu_baseline(spec, d, budget_s):
     """Time the fp64 oracle on a bounded sample of the same step: every decode
     request in flattened order (until the time budget is spent), then the
@@ -97,32 +137,8 @@ def cpu_baseline(spec, d, budget_s):
     import oracle
     from threadpoolctl import threadpool_info
 
-    def host(t):
-        t = t.detach().cpu()
-        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
-
-    qsl = spec.query_start_loc
-
     def run_request(r):
-        q = int(spec.query_lens[r])
-        L = int(spec.seq_lens[r])
-        c = L - q
-        nblk = -(-L // spec.B)
-        ids = torch.from_numpy(spec.block_table[r, :nblk].astype(np.int64)).to(d["key_cache"].device)
-        kp = host(d["key_cache"].index_select(0, ids))
-        vp = host(d["value_cache"].index_select(0, ids))
-        t = int(qsl[r])
-        qrows = host(d["query"][t:t + q])
-        knew = host(d["key"][t:t + q])
-        vnew = host(d["value"][t:t + q])
-        mini = np.arange(nblk, dtype=np.int32)[None]
-        t0 = time.perf_counter()
-        sm = oracle.slot_mapping(mini, [q], [c], spec.B)
-        oracle.write_kv(kp, vp, knew, vnew, sm, spec.B)
-        K = oracle.gather_kv(kp, mini[0], L, spec.B)
-        V = oracle.gather_kv(vp, mini[0], L, spec.B)
-        oracle.attention_rows(qrows, K, V, c + np.arange(q), spec.scale, spec.dtype)
-        return time.perf_counter() - t0
+        return oracle_request_seconds(spec, d, r)
 
     dec = [r for r in range(spec.R) if spec.query_lens[r] == 1]
     chunks = [r for r in range(spec.R) if spec.query_lens[r] > 1]
@@ -234,9 +250,12 @@ def serving_measurement(dev, first: int = 40, steps: int = 20, layers: int = 32)
     for 2048 requests (prompts lognormal median 1500, chunk 512, budget 8192,
     recompute preemption), each run as write_kv + attention over every layer
     of a 32-layer, 16384-block cache (32 GiB, Llama-3-8B attention geometry).
-    Steps first .. first + steps - 1 (past the ramp-up) are timed with HIP
-    events around all their layers; inputs are device-resident and filled
-    once per step (not timed)."""
+    Each step is planned once (pa_attention_plan: the metadata has no layer
+    dimension) and run per layer (pa_attention_run).  Steps first .. first +
+    steps - 1 (past the ramp-up) are timed with HIP events around all their
+    layers, then run again with the library's per-kernel events to split the
+    time into plan, split-K decode, chunk and merge; inputs are device-resident
+    and filled once per step (not timed)."""
     import numpy as np
     import torch
     import paged_kv_attention_reshape_amd as pa
@@ -248,12 +267,17 @@ def serving_measurement(dev, first: int = 40, steps: int = 20, layers: int = 32)
     kc = torch.zeros((layers, cfg.num_blocks, B, HKV, D), dtype=torch.bfloat16, device=dev)
     vc = torch.zeros_like(kc)
     # one workspace for the whole trace, sized by the scheduler's limits
-    ws = pa.alloc_workspace(pa.attention_workspace_bound(cfg.max_num_seqs, cfg.max_num_batched_tokens,
-                                                         st.max_seq_len(cfg), HQ, HKV, D, B, pa.PA_BF16), dev)
+    ws_bytes = pa.attention_workspace_bound(cfg.max_num_seqs, cfg.max_num_batched_tokens, st.max_seq_len(cfg),
+                                            HQ, HKV, D, B, pa.PA_BF16)
+    ws = pa.alloc_workspace(ws_bytes, dev)
     stream = torch.cuda.current_stream()
     gen = torch.Generator(device=dev).manual_seed(5)
+    scale = 1.0 / np.sqrt(D)
     total_ms, total_tok, n_dec, n_chunk_tok = 0.0, 0, 0, 0
+    dec_bytes, chunk_flops = 0, 0
+    acc = {"plan": 0.0, "write_kv": 0.0, "rowwise": 0.0, "chunk": 0.0, "merge": 0.0}
     per_step = []
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     for p in sel:
         ql, cp, bt, _, _ = st.step_arrays(p, B)
         T = int(ql.sum())
@@ -264,41 +288,85 @@ def serving_measurement(dev, first: int = 40, steps: int = 20, layers: int = 32)
         k = torch.randn((T, HKV, D), generator=gen, device=dev).to(torch.bfloat16)
         v = torch.randn((T, HKV, D), generator=gen, device=dev).to(torch.bfloat16)
         out = torch.empty_like(q)
+        dl = (ql == 1)
+        Ld = (ql + cp)[dl].astype(np.int64)
+        dec_bytes += layers * int(np.sum(Ld) * HKV * D * 2 * 2 + dl.sum() * 2 * HQ * D * 2
+                                  + 4 * np.sum(-(-Ld // B)) + 12 * dl.sum())
+        cq, cc = ql[~dl].astype(np.int64), cp[~dl].astype(np.int64)
+        chunk_flops += layers * int(np.sum(4 * D * HQ * (cq * cc + cq * (cq + 1) // 2)))
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = ev(), ev()
         e0.record(stream)
         # planned once per step (the metadata has no layer dimension), run per layer
-        plan = pa.attention_plan(d["bt"], d["qsl"], d["sl"], d["nc"], qsl, sl, HQ, kc.shape[1:],
-                                 pa.PA_BF16, ws)
+        plan = pa.attention_plan(d["bt"], d["qsl"], d["sl"], d["nc"], qsl, sl, HQ, kc.shape[1:], pa.PA_BF16, ws)
         for layer in range(layers):
             pa.write_kv(k, v, kc[layer], vc[layer], d["sm"])
-            pa.attention_run(plan, out, q, kc[layer], vc[layer], 1.0 / np.sqrt(D))
+            pa.attention_run(plan, out, q, kc[layer], vc[layer], scale)
         e1.record(stream)
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1)
+        # the same step again with per-kernel events (the events add small gaps between kernels)
+        pe = [ev() for _ in range(5)]
+        lay = [[ev() for _ in range(5)] for _ in range(layers)]
+        wk = [(ev(), ev()) for _ in range(layers)]
+        pa.set_profiling_events(pe)
+        plan = pa.attention_plan(d["bt"], d["qsl"], d["sl"], d["nc"], qsl, sl, HQ, kc.shape[1:], pa.PA_BF16, ws)
+        for layer in range(layers):
+            wk[layer][0].record(stream)
+            pa.write_kv(k, v, kc[layer], vc[layer], d["sm"])
+            wk[layer][1].record(stream)
+            pa.set_profiling_events(lay[layer])
+            pa.attention_run(plan, out, q, kc[layer], vc[layer], scale)
+        pa.set_profiling_events(None)
+        torch.cuda.synchronize()
+        acc["plan"] += pe[0].elapsed_time(pe[1])
+        for layer in range(layers):
+            e = lay[layer]
+            acc["write_kv"] += wk[layer][0].elapsed_time(wk[layer][1])
+            acc["rowwise"] += e[1].elapsed_time(e[2])
+            acc["chunk"] += e[2].elapsed_time(e[3])
+            acc["merge"] += e[3].elapsed_time(e[4])
         total_ms += ms
         total_tok += T
-        n_dec += int(np.sum(ql == 1))
-        n_chunk_tok += int(np.sum(ql[ql > 1]))
+        n_dec += int(dl.sum())
+        n_chunk_tok += int(np.sum(ql[~dl]))
         per_step.append(round(ms, 3))
     del kc, vc
     torch.cuda.empty_cache()
+    n = max(1, len(sel))
+    us = {k: round(1e3 * v / n, 2) for k, v in acc.items()}
+    dec_s = (acc["rowwise"] + acc["merge"]) * 1e-3
+    rw_s = acc["rowwise"] * 1e-3
+    ck_s = acc["chunk"] * 1e-3
+    dec_gbs = dec_bytes / dec_s / 1e9 if dec_s > 0 else None
+    rw_gbs = dec_bytes / rw_s / 1e9 if rw_s > 0 else None
+    ck_tf = chunk_flops / ck_s / 1e12 if ck_s > 0 else None
     return {"steps": len(sel), "first_step": first, "layers": layers, "tokens": total_tok,
             "decode_rows": n_dec, "chunk_tokens": n_chunk_tok,
-            "ms_per_step": round(total_ms / max(1, len(sel)), 3),
+            "ms_per_step": round(total_ms / n, 3),
             "tokens_per_s": round(total_tok / (total_ms * 1e-3), 1) if total_ms > 0 else None,
             "step_ms_p10_p50_p90": [round(float(x), 3) for x in np.percentile(per_step, [10, 50, 90])],
+            "kernel_us_per_step": us,
+            "decode_bytes_per_step": dec_bytes // n, "chunk_flops_per_step": chunk_flops // n,
+            "decode_gbs": round(dec_gbs, 1) if dec_gbs else None,
+            "decode_frac_hbm": round(dec_gbs / HBM_PEAK_GBS, 4) if dec_gbs else None,
+            "rowwise_gbs": round(rw_gbs, 1) if rw_gbs else None,
+            "chunk_tflops": round(ck_tf, 1) if ck_tf else None,
+            "chunk_frac_mfma": round(ck_tf / MFMA_BF16_PEAK_TFLOPS, 4) if ck_tf else None,
+            "workspace_bytes": ws_bytes,
             "trace": "2048 requests at step 0, prompts lognormal median 1500, outputs geometric mean 256, "
                      "chunk 512, budget 8192, 16384 blocks of 16; Hq 32, Hkv 8, D 128",
-            "includes": "write_kv + attention (slot mapping built on the host) for every layer of the step"}
+            "includes": "write_kv + attention (slot mapping built on the host) for every layer of the step; "
+                        "one plan per step, one attention run per layer"}
 
 
 def swap_measurement(dev, reps: int = 10):
     """Swap-out + swap-in of whole block columns (every layer's K and V
-    block) between the device cache and a pinned host pool with
-    pa_copy_blocks, in the geometry of the pages' worked swap example (512 KiB
-    of K/V per token: 32 layers, 32 kv heads, head_dim 128, bf16; block 16).
-    Returns the measured round trips and the pages' formula
+    block) between the device cache and a pinned host pool, in the geometry
+    of the pages' worked swap example (512 KiB of K/V per token: 32 layers,
+    32 kv heads, head_dim 128, bf16; block 16), on the copy engines
+    (pa_swap_blocks, the swap path) and with the copy kernel (pa_copy_blocks)
+    for comparison.  Returns the measured round trips and the pages' formula
     2 * payload / bandwidth beside them."""
     import numpy as np
     import torch
@@ -309,32 +377,48 @@ def swap_measurement(dev, reps: int = 10):
     pools = torch.zeros((2 * L, nb, B, HKV, D), dtype=torch.bfloat16, device=dev)
     host = torch.empty((2 * L, hb, B, HKV, D), dtype=torch.bfloat16, pin_memory=True)
     stream = torch.cuda.current_stream()
-    out = {}
-    for n in (1, 64):
-        g = np.random.default_rng(n)
-        src = g.choice(nb, n, replace=False).astype(np.int32)
-        dst = g.choice(hb, n, replace=False).astype(np.int32)
-        p_out = torch.from_numpy(np.stack([src, dst], 1)).to(dev)
-        p_in = torch.from_numpy(np.stack([dst, src], 1)).to(dev)
-        for _ in range(2):
-            pa.copy_blocks(pools, host, p_out)
-            pa.copy_blocks(host, pools, p_in)
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        torch.cuda.synchronize()
-        e[0].record(stream)
-        for _ in range(reps):
-            pa.copy_blocks(pools, host, p_out)
-        e[1].record(stream)
-        for _ in range(reps):
-            pa.copy_blocks(host, pools, p_in)
-        e[2].record(stream)
-        torch.cuda.synchronize()
-        t_out = e[0].elapsed_time(e[1]) / reps
-        t_in = e[1].elapsed_time(e[2]) / reps
-        payload = n * B * kappa
-        out[f"{n}_block"] = {"bytes_each_way": payload, "out_ms": round(t_out, 4), "in_ms": round(t_in, 4),
-                             "roundtrip_ms": round(t_out + t_in, 4),
-                             "out_gbs": round(payload / t_out / 1e6, 1), "in_gbs": round(payload / t_in / 1e6, 1)}
+    res = {}
+    for path in ("engines", "kernel"):
+        out = {}
+        for n in (1, 64):
+            g = np.random.default_rng(n)
+            src = g.choice(nb, n, replace=False).astype(np.int32)
+            dst = g.choice(hb, n, replace=False).astype(np.int32)
+            h_out, h_in = np.stack([src, dst], 1), np.stack([dst, src], 1)
+            p_out, p_in = torch.from_numpy(h_out).to(dev), torch.from_numpy(h_in).to(dev)
+
+            def go(direction):
+                if path == "engines":
+                    if direction == "out":
+                        pa.swap_blocks(pools, host, h_out)
+                    else:
+                        pa.swap_blocks(host, pools, h_in)
+                else:
+                    if direction == "out":
+                        pa.copy_blocks(pools, host, p_out)
+                    else:
+                        pa.copy_blocks(host, pools, p_in)
+            for _ in range(2):
+                go("out")
+                go("in")
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            torch.cuda.synchronize()
+            e[0].record(stream)
+            for _ in range(reps):
+                go("out")
+            e[1].record(stream)
+            for _ in range(reps):
+                go("in")
+            e[2].record(stream)
+            torch.cuda.synchronize()
+            t_out = e[0].elapsed_time(e[1]) / reps
+            t_in = e[1].elapsed_time(e[2]) / reps
+            payload = n * B * kappa
+            out[f"{n}_block"] = {"bytes_each_way": payload, "out_ms": round(t_out, 4), "in_ms": round(t_in, 4),
+                                 "roundtrip_ms": round(t_out + t_in, 4),
+                                 "out_gbs": round(payload / t_out / 1e6, 1), "in_gbs": round(payload / t_in / 1e6, 1)}
+        res[path] = out
+    out = res["engines"]
     beta = 2 * out["64_block"]["bytes_each_way"] / (out["64_block"]["roundtrip_ms"] * 1e6)   # GB/s
     tokens = 7
     out["pages_example"] = {
@@ -345,7 +429,225 @@ def swap_measurement(dev, reps: int = 10):
         "measured_ms_one_block": out["1_block"]["roundtrip_ms"],
         "note": "the pool moves whole blocks: 7 tokens occupy one 16-token block column (16 * kappa bytes each way)",
     }
+    out["path"] = "pa_swap_blocks: copy engines, one 2-D copy per run of consecutive block columns"
+    out["copy_kernel"] = res["kernel"]
+    del pools, host
+    torch.cuda.empty_cache()
     return out
+
+
+def pool_rotation(d, rotate_bytes=MALL_ROTATE_BYTES):
+    """Pool copies so that consecutive steps touch >= rotate_bytes apart (the
+    256 MB last-level cache must not serve a step's reads from the previous
+    step); the first copy is the step's own pools."""
+    pool_bytes = 2 * d["key_cache"].numel() * d["key_cache"].element_size()
+    n = 1 if pool_bytes >= rotate_bytes else min(8, -(-rotate_bytes // pool_bytes))
+    return [(d["key_cache"], d["value_cache"])] + \
+        [(d["key_cache"].clone(), d["value_cache"].clone()) for _ in range(n - 1)]
+
+
+def decode_workload(name: str, dev, steps: int, warmup: int):
+    """One of the decode-only configurations (C2, C4) timed like the main
+    step: write_kv + attention per step over rotated pool copies, HIP events
+    recorded by the library between its launches; returns the split-K and
+    merge times and the decode roofline (algorithmic bytes / time)."""
+    import numpy as np
+    import torch
+    import paged_kv_attention_reshape_amd as pa
+    from workloads import configs
+    spec = configs.BUILDERS[name]()
+    d = spec.device_inputs(device=dev)
+    pools = pool_rotation(d)
+    out = torch.empty_like(d["query"])
+    ws = pa.alloc_workspace(pa.attention_workspace_size(spec.query_start_loc, spec.seq_lens, spec.Hq, spec.Hkv,
+                                                        spec.D, spec.B, pa.PA_BF16), dev)
+    slots = torch.from_numpy(pa.build_step_metadata(spec.query_lens, spec.num_computed, spec.block_table,
+                                                    spec.B, spec.num_blocks)[2]).to(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    stream = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def one(i, events=None):
+        kc, vc = pools[i % len(pools)]
+        pa.write_kv(d["key"], d["value"], kc, vc, slots)
+        if events is not None:
+            pa.set_profiling_events(events)
+        pa.attention(out, d["query"], kc, vc, d["block_table"], d["query_start_loc"], d["seq_lens"],
+                     d["num_computed"], spec.query_start_loc, spec.seq_lens, spec.scale, ws)
+        if events is not None:
+            pa.set_profiling_events(None)
+
+    for i in range(warmup):
+        one(i)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(steps):
+        one(i)
+    t1.record(stream)
+    for i in range(steps):
+        one(i, ev[i])
+    torch.cuda.synchronize()
+    rw = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e3
+    mg = float(np.mean([e[3].elapsed_time(e[4]) for e in ev])) * 1e3
+    pl = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
+    db = spec.decode_bytes()
+    rw_gbs = db / (rw * 1e-6) / 1e9
+    val = db / ((rw + mg) * 1e-6) / 1e9
+    return {"workload": configs.WORKLOADS[name], "requests": spec.R, "decode_bytes_per_step": db,
+            "pool_copies": len(pools), "ms_per_step": round(t0.elapsed_time(t1) / steps, 4),
+            "kernel_us": {"plan": round(pl, 2), "rowwise": round(rw, 2), "merge": round(mg, 2)},
+            "decode_gbs": round(val, 1), "decode_frac_hbm": round(val / HBM_PEAK_GBS, 4),
+            "roofline": {"kernel": "rowwise split-K decode", "bound": "hbm", "achieved": round(rw_gbs, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(rw_gbs / HBM_PEAK_GBS, 4)}}
+
+
+def swap_beside_steps(dev, step, n_steps: int, stream, path: str = "engines"):
+    """The step run n_steps times on the current stream, first alone and then
+    while a swap-out (64 block columns: every layer's K and V block, 32 layers
+    x 32 kv heads x 128 x bf16, 16 tokens a block; 512 MiB) runs repeatedly
+    on a second stream of default priority, ordered after the inputs with an
+    event.  path "engines": pa_swap_blocks (copy engines); "kernel":
+    pa_copy_blocks (the copy kernel).  Reports the step time in both cases and
+    the swap's bandwidth beside the steps and alone."""
+    import numpy as np
+    import torch
+    import paged_kv_attention_reshape_amd as pa
+    L, HKV, D, B = 32, 32, 128, 16
+    nb, hb = 96, 64
+    pools = torch.zeros((2 * L, nb, B, HKV, D), dtype=torch.bfloat16, device=dev)
+    host = torch.empty((2 * L, hb, B, HKV, D), dtype=torch.bfloat16, pin_memory=True)
+    g = np.random.default_rng(64)
+    h_pairs = np.stack([g.choice(nb, 64, replace=False), np.arange(64)], 1).astype(np.int32)
+    pairs = torch.from_numpy(h_pairs).to(dev)
+    swap_bytes = 64 * 2 * L * B * HKV * D * 2
+    side = torch.cuda.Stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def swap(s=None):
+        if path == "engines":
+            pa.swap_blocks(pools, host, h_pairs, stream=s)
+        else:
+            pa.copy_blocks(pools, host, pairs, stream=s)
+    # swap alone (after two untimed ones)
+    swap()
+    swap()
+    torch.cuda.synchronize()
+    a0, a1 = ev(), ev()
+    a0.record(stream)
+    swap()
+    a1.record(stream)
+    torch.cuda.synchronize()
+    swap_alone_ms = a0.elapsed_time(a1)
+    # steps alone
+    s0, s1 = ev(), ev()
+    s0.record(stream)
+    for _ in range(n_steps):
+        step()
+    s1.record(stream)
+    torch.cuda.synchronize()
+    alone_ms = s0.elapsed_time(s1) / n_steps
+    reps = max(1, int(np.ceil(alone_ms * n_steps / swap_alone_ms)))
+    # steps beside the swap
+    ready = torch.cuda.Event()
+    ready.record(stream)
+    side.wait_event(ready)
+    w0, w1 = ev(), ev()
+    with torch.cuda.stream(side):
+        w0.record(side)
+        for _ in range(reps):
+            swap(side)
+        w1.record(side)
+    b0, b1 = ev(), ev()
+    b0.record(stream)
+    for _ in range(n_steps):
+        step()
+    b1.record(stream)
+    done = torch.cuda.Event()
+    done.record(side)
+    stream.wait_event(done)
+    torch.cuda.synchronize()
+    beside_ms = b0.elapsed_time(b1) / n_steps
+    swap_ms = w0.elapsed_time(w1)
+    del pools, host
+    torch.cuda.empty_cache()
+    return {"step_ms_alone": round(alone_ms, 4), "step_ms_beside_swap": round(beside_ms, 4),
+            "step_slowdown": round(beside_ms / alone_ms, 4), "swap_bytes_each": swap_bytes, "swap_reps": reps,
+            "swap_gbs_beside_steps": round(reps * swap_bytes / (swap_ms * 1e6), 1),
+            "swap_gbs_alone": round(swap_bytes / (swap_alone_ms * 1e6), 1),
+            "path": "pa_swap_blocks (copy engines, one 2-D copy per block column)" if path == "engines"
+                    else "pa_copy_blocks (copy kernel, 64 workgroups)",
+            "note": "swap-out of 64 block columns (512 MiB) repeated on a second default-priority stream, "
+                    "event-ordered after the inputs, while the step runs on the current stream"}
+
+
+def oracle_configs(dev, budget_s: float):
+    """The fp64 oracle timed on the other configurations (bounded samples):
+    C1 whole; every decode of C2 and of C4 (within budget_s each); a sample of
+    the serving trace (the decode rows and one chunk of two planned steps, one
+    layer).  Inputs are the generator's device-filled pools and rows copied to
+    the host per request (C1, C2, C4), or host random values of the same
+    shapes (C5 sample).  Returns per-configuration time and the metric's
+    units."""
+    import numpy as np
+    import oracle
+    from workloads import configs
+    res = {}
+
+    import torch
+    for name in ("c1", "c2", "c4"):
+        spec = configs.BUILDERS[name]()
+        d = spec.device_inputs(device=dev)
+        torch.cuda.synchronize()
+        sec, n = 0.0, 0
+        for r in range(spec.R):
+            if sec > budget_s:
+                break
+            sec += oracle_request_seconds(spec, d, r)
+            n += 1
+        del d
+        torch.cuda.empty_cache()
+        done = np.zeros(spec.R, bool)
+        done[:n] = True
+        dec = (spec.query_lens == 1) & done
+        L = spec.seq_lens[dec].astype(np.int64)
+        dbytes = int(np.sum(L) * spec.Hkv * spec.D * 2 * spec.esize + 2 * dec.sum() * spec.Hq * spec.D * spec.esize
+                     + 4 * np.sum(-(-L // spec.B)) + 12 * dec.sum())
+        res[name] = {"sample": f"{n} of {spec.R} requests", "oracle_s": round(sec, 3),
+                     "decode_gbs_equiv": round(dbytes / sec / 1e9, 4) if sec > 0 and dbytes else None}
+        if name == "c1":
+            res[name]["step_ms"] = round(sec * 1e3, 2)
+    # serving-trace sample: two planned steps, one layer, every decode row and one chunk
+    from workloads import serving_trace as st
+    import paged_kv_attention_reshape_amd as pa
+    cfg = st.TraceConfig()
+    plans = st.drive(pa.Scheduler(**st.scheduler_args(cfg)), cfg)
+    g = np.random.default_rng(9)
+    HQ, HKV, D = 32, 8, 128
+    sec, dbytes, flops, rows = 0.0, 0, 0, 0
+    for p in (plans[45],):
+        ql, cp, _, _, _ = st.step_arrays(p, cfg.block_size)
+        idx = [i for i in range(len(ql)) if ql[i] == 1] + [i for i in range(len(ql)) if ql[i] > 1][:1]
+        for i in idx:
+            q, c = int(ql[i]), int(cp[i])
+            L = q + c
+            Q = g.standard_normal((q, HQ, D)).astype(np.float32)
+            K = g.standard_normal((L, HKV, D)).astype(np.float32)
+            V = g.standard_normal((L, HKV, D)).astype(np.float32)
+            t0 = time.perf_counter()
+            oracle.attention_rows(Q, K, V, c + np.arange(q), 1 / np.sqrt(D), "f32")
+            sec += time.perf_counter() - t0
+            rows += q
+            if q == 1:
+                dbytes += L * HKV * D * 2 * 2 + 2 * HQ * D * 2
+            else:
+                flops += 4 * D * HQ * (q * c + q * (q + 1) // 2)
+    res["c5_sample"] = {"sample": f"step 45 of the serving trace, one layer: every decode row and the first "
+                                  f"chunk ({rows} query rows)", "oracle_s": round(sec, 3),
+                        "decode_gbs_equiv": round(dbytes / sec / 1e9, 4) if sec > 0 else None,
+                        "chunk_flops": flops,
+                        "note": "one (step, layer) sample of 200 steps x 32 layers; extrapolating this time to the "
+                                "whole trace (x 6400) is an estimate, not a measurement"}
+    return res
 
 
 def load_traffic(kernel: str):
@@ -374,6 +676,13 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
+    if args.serving_only:
+        import torch
+        import paged_kv_attention_reshape_amd as pa
+        torch.cuda.set_device(0)
+        pa.lib()
+        print(json.dumps({"serving_trace": serving_measurement(torch.device("cuda:0"))}), flush=True)
+        return
 
     import numpy as np
     import torch
@@ -393,14 +702,14 @@ def main():
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(spec, d, args.cpu_seconds)
+        if args.extra:
+            cpu["configs"] = oracle_configs(dev, max(1.0, args.cpu_seconds / 4))
 
     # The 256 MB last-level (Infinity) cache must not serve a step's cache
     # reads from the previous step: when one layer's pools are small, steps
     # rotate over copies so that consecutive steps touch >= 1 GiB apart.
-    pool_bytes = 2 * d["key_cache"].numel() * d["key_cache"].element_size()
-    n_copies = 1 if pool_bytes >= MALL_ROTATE_BYTES else min(8, -(-MALL_ROTATE_BYTES // pool_bytes))
-    pools = [(d["key_cache"], d["value_cache"])] + \
-            [(d["key_cache"].clone(), d["value_cache"].clone()) for _ in range(n_copies - 1)]
+    pools = pool_rotation(d)
+    n_copies = len(pools)
     torch.cuda.synchronize()
 
     qsl_h, sl_h = spec.query_start_loc, spec.seq_lens
@@ -539,7 +848,13 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(rope_gbs / HBM_PEAK_GBS, 4)}
 
     swap = swap_measurement(dev) if args.swap else None
+    if swap is not None:
+        swap["beside_step"] = swap_beside_steps(dev, step, args.steps, stream, "engines")
+        swap["beside_step_copy_kernel"] = swap_beside_steps(dev, step, args.steps, stream, "kernel")
     serving = serving_measurement(dev) if args.serving else None
+    extra = None
+    if args.extra and args.workload == "c3":
+        extra = {n: decode_workload(n, dev, args.steps, args.warmup) for n in ("c2", "c4")}
 
     # host scheduler / block allocator (C++) on the serving trace
     sched_t = scheduler_timing(product=True)
@@ -608,6 +923,7 @@ def main():
         "scheduler": sched_t,
         "swap_roundtrip": swap,
         "serving_trace": serving,
+        "decode_configs": extra,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -218,9 +218,51 @@ pa_status pa_rope_write_kv(void* query, const void* key, const void* value, void
  *                         head_dim * element size), a multiple of 16
  * Destination blocks must be distinct and must not be a source of the same
  * call (else the result is undefined).  The copy is exact.  Enqueued on
- * stream; a plan's copies must be enqueued before its cache write.
+ * stream; a plan's copies must be enqueued before its cache write.  A copy
+ * that crosses the host link (either side pinned host memory, as
+ * hipPointerGetAttributes reports it) runs on at most 64 workgroups; it still
+ * occupies the memory path of the compute units for the whole transfer, so
+ * swaps beside a running step belong on the copy engines (pa_swap_blocks).
+ * Returns PA_ERR_BAD_SHAPE for a pool pointer that is neither device memory
+ * nor pinned host memory.
  */
 pa_status pa_copy_blocks(const void* src_pools, void* dst_pools, const int32_t* block_pairs,
+                         int32_t num_pairs, int32_t num_pools, int64_t src_pool_stride,
+                         int64_t dst_pool_stride, int32_t src_num_blocks, int32_t dst_num_blocks,
+                         int64_t block_bytes, void* stream);
+
+/*
+ * pa_swap_blocks -- swap-out / swap-in of whole cache blocks on the GPU's
+ * copy engines.
+ *
+ * [P2] "vLLM 抢占机制源码精读", section "Swap 模式": a preempted request's
+ * blocks are moved to host memory and back asynchronously by the cache
+ * engine, before the model's kernels run; [P4] "Chunked Prefill 与
+ * Preemption": the swap round trip moves the payload out and back, bounded
+ * by twice the payload over the host-link bandwidth.
+ *
+ *   src_pools, dst_pools  num_pools pools each, pool k at base + k * stride
+ *                         bytes (the 2L per-layer K and V caches of a model);
+ *                         device memory or pinned host memory (any pairing)
+ *   h_block_pairs         HOST int32 [num_pairs, 2]: (source block,
+ *                         destination block); pair i copies block_bytes bytes
+ *                         from the source block of every source pool to the
+ *                         destination block of the matching destination pool
+ *   block_bytes           bytes of one block of one pool
+ * Each run of consecutive pairs whose source and destination blocks both
+ * advance by one becomes one 2-D asynchronous copy (width = run * block_bytes,
+ * height = num_pools, pitches = the pool strides), enqueued on stream in pair
+ * order: the copy engines move the data, so the compute units and their memory
+ * path stay with the kernels of a step running on another stream (order the
+ * two with events: the step must not write blocks being swapped out nor read
+ * blocks being swapped in).  The copy is exact; nothing is allocated.
+ * Checked on the host before anything is enqueued: pointers, sizes, strides
+ * (>= a pool when num_pools > 1), every block id within its pool
+ * (PA_ERR_OUT_OF_RANGE) and distinct destination blocks
+ * (PA_ERR_DUPLICATE_SLOT).  A HIP error while enqueueing returns PA_ERR_HIP;
+ * the copies enqueued before it stay enqueued.
+ */
+pa_status pa_swap_blocks(const void* src_pools, void* dst_pools, const int32_t* h_block_pairs,
                          int32_t num_pairs, int32_t num_pools, int64_t src_pool_stride,
                          int64_t dst_pool_stride, int32_t src_num_blocks, int32_t dst_num_blocks,
                          int64_t block_bytes, void* stream);

@@ -10,7 +10,7 @@ from ._lib import (  # noqa: F401
     NOALLOC_SCRATCH_BYTES, attention, attention_noalloc, attention_plan, attention_run,
     attention_workspace_bound, attention_workspace_size,
     build_step_metadata, compute_slot_mapping, copy_blocks, get_tuning, last_error, lib,
-    rope_write_kv, set_profiling_events, set_tuning, status_str, tuning, validate_metadata,
-    write_kv,
+    rope_write_kv, set_profiling_events, set_tuning, status_str, swap_blocks, tuning,
+    validate_metadata, write_kv,
 )
 from ._sched import SCHED_EXPORTS, SCHED_LIB_PATH, Scheduler, sched_lib  # noqa: F401,E402

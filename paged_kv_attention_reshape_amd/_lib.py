@@ -32,7 +32,7 @@ EXPORTS = [
     "pa_attention_workspace_bound", "pa_attention", "pa_attention_plan", "pa_attention_run",
     "pa_attention_noalloc",
     "pa_set_tuning", "pa_get_tuning", "pa_set_profiling_events", "pa_validate_metadata",
-    "pa_rope_write_kv", "pa_copy_blocks",
+    "pa_rope_write_kv", "pa_copy_blocks", "pa_swap_blocks",
 ]
 
 # pa_tuning_knob
@@ -97,6 +97,9 @@ def lib():
                                    ctypes.c_int, _vp]
     L.pa_copy_blocks.restype = ctypes.c_int
     L.pa_copy_blocks.argtypes = [_vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                 ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, _vp]
+    L.pa_swap_blocks.restype = ctypes.c_int
+    L.pa_swap_blocks.argtypes = [_vp, _vp, _i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                  ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, _vp]
     L.pa_attention_workspace_size.restype = ctypes.c_size_t
     L.pa_attention_workspace_size.argtypes = [_i32p, _i32p, ctypes.c_int32, ctypes.c_int32,
@@ -284,6 +287,22 @@ def copy_blocks(src_pools, dst_pools, block_pairs, stream=None) -> None:
                                 src.stride(0) * src.element_size(), dst.stride(0) * dst.element_size(),
                                 Ns, Nd, block_bytes, ctypes.c_void_p(_stream(stream))),
            "pa_copy_blocks")
+
+
+def swap_blocks(src_pools, dst_pools, block_pairs, stream=None) -> None:
+    """Swap whole blocks between pools on the copy engines (pa_swap_blocks).
+    src_pools / dst_pools: tensors [P, N, B, Hkv, D] (or [N, B, Hkv, D]),
+    device or pinned host; block_pairs: HOST int32 [n, 2] (numpy)."""
+    src = src_pools if src_pools.dim() == 5 else src_pools.unsqueeze(0)
+    dst = dst_pools if dst_pools.dim() == 5 else dst_pools.unsqueeze(0)
+    if src.shape[0] != dst.shape[0] or src.shape[2:] != dst.shape[2:] or src.dtype != dst.dtype:
+        raise ValueError("source and destination pools must have the same count, block layout and dtype")
+    pairs = np.ascontiguousarray(np.asarray(block_pairs, dtype=np.int32).reshape(-1, 2))
+    block_bytes = src[0, 0].numel() * src.element_size()
+    _check(lib().pa_swap_blocks(_ptr(src), _ptr(dst), _p32(pairs), pairs.shape[0], src.shape[0],
+                                src.stride(0) * src.element_size(), dst.stride(0) * dst.element_size(),
+                                src.shape[1], dst.shape[1], block_bytes, ctypes.c_void_p(_stream(stream))),
+           "pa_swap_blocks")
 
 
 def attention_workspace_size(h_query_start_loc, h_seq_lens, num_heads: int, num_kv_heads: int,

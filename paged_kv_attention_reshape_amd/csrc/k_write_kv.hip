@@ -22,6 +22,7 @@ namespace pa {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int64_t kHostLinkGroups = 64;  // copy workgroups for host-link transfers
 
 __global__ void __launch_bounds__(kThreads)
 write_kv_kernel(const uint4* __restrict__ key, const uint4* __restrict__ value,
@@ -72,33 +73,41 @@ slot_mapping_kernel(int64_t* __restrict__ slots, const int32_t* __restrict__ blo
 
 // Block copies between pools of the same block layout: pair i moves block
 // pairs[i].src of every source pool to block pairs[i].dst of the matching
-// destination pool (pool k at base + k * stride).  One workgroup per (pair,
-// pool); each thread moves 16-byte chunks, eight loads in flight before the
-// stores.  Serves copy-on-write (same pool) and swap between the device
-// cache and a pinned host pool (the kernel reads or writes host memory over
-// the host link directly, one launch for any scattered block list).
+// destination pool (pool k at base + k * stride).  A unit is one (pair,
+// pool) block; the grid's workgroups stride over the units (pool-fastest, so
+// consecutive units of one pair touch the pools in address order); each
+// thread moves 16-byte chunks, eight loads in flight before the stores.
+// Serves copy-on-write (same pool) and swap between the device cache and a
+// pinned host pool: the kernel reads or writes host memory over the host
+// link directly, one launch for any scattered block list, and for such
+// transfers the grid is a few dozen workgroups (the link, not the compute
+// units, bounds the copy), so a swap running beside a step leaves the compute
+// units to attention.
 __global__ void __launch_bounds__(kThreads)
 copy_blocks_kernel(const char* src, char* dst,
                    const int32_t* __restrict__ pairs, int64_t src_stride, int64_t dst_stride,
-                   int32_t src_blocks, int32_t dst_blocks, int64_t chunks) {
-  const int64_t i = blockIdx.x;
-  const int64_t k = blockIdx.y;
-  const int32_t sb = pairs[2 * i];
-  const int32_t db = pairs[2 * i + 1];
-  if (sb < 0 || sb >= src_blocks || db < 0 || db >= dst_blocks) return;
-  // source and destination may be the same pool (distinct blocks)
-  const uint4* sp = reinterpret_cast<const uint4*>(src + k * src_stride) + (int64_t)sb * chunks;
-  uint4* dp = reinterpret_cast<uint4*>(dst + k * dst_stride) + (int64_t)db * chunks;
-  constexpr int U = 8;
-  int64_t c = threadIdx.x;
-  for (; c + (U - 1) * kThreads < chunks; c += U * kThreads) {
-    uint4 v[U];
+                   int32_t src_blocks, int32_t dst_blocks, int64_t chunks, int64_t units,
+                   int32_t num_pools) {
+  for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+    const int64_t i = unit / num_pools;
+    const int64_t k = unit - i * num_pools;
+    const int32_t sb = pairs[2 * i];
+    const int32_t db = pairs[2 * i + 1];
+    if (sb < 0 || sb >= src_blocks || db < 0 || db >= dst_blocks) continue;
+    // source and destination may be the same pool (distinct blocks)
+    const uint4* sp = reinterpret_cast<const uint4*>(src + k * src_stride) + (int64_t)sb * chunks;
+    uint4* dp = reinterpret_cast<uint4*>(dst + k * dst_stride) + (int64_t)db * chunks;
+    constexpr int U = 8;
+    int64_t c = threadIdx.x;
+    for (; c + (U - 1) * kThreads < chunks; c += U * kThreads) {
+      uint4 v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = sp[c + u * kThreads];
+      for (int u = 0; u < U; ++u) v[u] = sp[c + u * kThreads];
 #pragma unroll
-    for (int u = 0; u < U; ++u) dp[c + u * kThreads] = v[u];
+      for (int u = 0; u < U; ++u) dp[c + u * kThreads] = v[u];
+    }
+    for (; c < chunks; c += kThreads) dp[c] = sp[c];
   }
-  for (; c < chunks; c += kThreads) dp[c] = sp[c];
 }
 
 }  // namespace
@@ -128,11 +137,16 @@ hipError_t launch_write_kv(const void* key, const void* value, void* key_cache, 
 hipError_t launch_copy_blocks(const void* src, void* dst, const int32_t* pairs, int32_t n,
                               int32_t num_pools, int64_t src_stride, int64_t dst_stride,
                               int32_t src_blocks, int32_t dst_blocks, int64_t block_bytes,
-                              hipStream_t s) {
+                              bool host_link, hipStream_t s) {
   if (n == 0 || num_pools == 0) return hipSuccess;
-  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)n, (unsigned)num_pools), dim3(kThreads), 0, s,
+  const int64_t units = (int64_t)n * num_pools;
+  // host-link transfers: a few dozen workgroups keep about 2 MiB in flight,
+  // enough for the link; device copies: up to eight workgroups per compute unit
+  const int64_t cap = host_link ? kHostLinkGroups : 2048;
+  const int64_t grid = units < cap ? units : cap;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s,
                      static_cast<const char*>(src), static_cast<char*>(dst), pairs, src_stride,
-                     dst_stride, src_blocks, dst_blocks, block_bytes / 16);
+                     dst_stride, src_blocks, dst_blocks, block_bytes / 16, units, num_pools);
   return hipGetLastError();
 }
 

@@ -686,10 +686,65 @@ pa_status pa_copy_blocks(const void* src_pools, void* dst_pools, const int32_t* 
     return fail(PA_ERR_BAD_SHAPE, "pool strides smaller than a pool");
   if ((src_pool_stride | dst_pool_stride) % 16 != 0 || (((uintptr_t)src_pools | (uintptr_t)dst_pools) & 15))
     return fail(PA_ERR_BAD_SHAPE, "pools and strides must be 16-byte aligned");
+  // does the copy cross the host link (either side pinned host memory)?
+  bool host_link = false;
+  for (const void* p : {src_pools, static_cast<const void*>(dst_pools)}) {
+    hipPointerAttribute_t at;
+    if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(PA_ERR_BAD_SHAPE, "pool %p is neither device memory nor pinned host memory", p);
+    }
+    if (at.type == hipMemoryTypeHost) host_link = true;
+  }
   hipError_t e = pa::launch_copy_blocks(src_pools, dst_pools, block_pairs, num_pairs, num_pools,
                                         src_pool_stride, dst_pool_stride, src_num_blocks,
-                                        dst_num_blocks, block_bytes, reinterpret_cast<hipStream_t>(stream));
+                                        dst_num_blocks, block_bytes, host_link,
+                                        reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "copy_blocks launch");
+  return PA_OK;
+}
+
+pa_status pa_swap_blocks(const void* src_pools, void* dst_pools, const int32_t* h_block_pairs,
+                         int32_t num_pairs, int32_t num_pools, int64_t src_pool_stride,
+                         int64_t dst_pool_stride, int32_t src_num_blocks, int32_t dst_num_blocks,
+                         int64_t block_bytes, void* stream) {
+  g_err.clear();
+  if (num_pairs < 0 || num_pools < 0) return fail(PA_ERR_BAD_SHAPE, "negative count");
+  if (num_pairs == 0 || num_pools == 0) return PA_OK;
+  if (!src_pools || !dst_pools || !h_block_pairs) return fail(PA_ERR_NULL_PTR, "NULL pointer argument");
+  if (block_bytes <= 0) return fail(PA_ERR_BAD_SHAPE, "block_bytes %lld must be positive", (long long)block_bytes);
+  if (src_num_blocks <= 0 || dst_num_blocks <= 0) return fail(PA_ERR_BAD_SHAPE, "pool sizes must be positive");
+  if (num_pools > 1 && (src_pool_stride < (int64_t)src_num_blocks * block_bytes ||
+                        dst_pool_stride < (int64_t)dst_num_blocks * block_bytes))
+    return fail(PA_ERR_BAD_SHAPE, "pool strides smaller than a pool");
+  std::vector<int32_t> dsts((size_t)num_pairs);
+  for (int32_t i = 0; i < num_pairs; ++i) {
+    const int32_t sb = h_block_pairs[2 * i], db = h_block_pairs[2 * i + 1];
+    if (sb < 0 || sb >= src_num_blocks || db < 0 || db >= dst_num_blocks)
+      return fail(PA_ERR_OUT_OF_RANGE, "pair %d = (%d, %d) outside the pools (%d, %d blocks)", i, sb, db,
+                  src_num_blocks, dst_num_blocks);
+    dsts[(size_t)i] = db;
+  }
+  std::sort(dsts.begin(), dsts.end());
+  for (size_t i = 1; i < dsts.size(); ++i)
+    if (dsts[i] == dsts[i - 1]) return fail(PA_ERR_DUPLICATE_SLOT, "destination block %d named twice", dsts[i]);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const char* src = static_cast<const char*>(src_pools);
+  char* dst = static_cast<char*>(dst_pools);
+  for (int32_t i = 0; i < num_pairs;) {
+    int32_t run = 1;   // consecutive source and destination blocks copy as one row
+    while (i + run < num_pairs && h_block_pairs[2 * (i + run)] == h_block_pairs[2 * i] + run &&
+           h_block_pairs[2 * (i + run) + 1] == h_block_pairs[2 * i + 1] + run)
+      ++run;
+    const size_t width = (size_t)run * (size_t)block_bytes;
+    const size_t spitch = num_pools > 1 ? (size_t)src_pool_stride : width;
+    const size_t dpitch = num_pools > 1 ? (size_t)dst_pool_stride : width;
+    const hipError_t e = hipMemcpy2DAsync(dst + (int64_t)h_block_pairs[2 * i + 1] * block_bytes, dpitch,
+                                          src + (int64_t)h_block_pairs[2 * i] * block_bytes, spitch, width,
+                                          (size_t)num_pools, hipMemcpyDefault, s);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpy2DAsync");
+    i += run;
+  }
   return PA_OK;
 }
 

@@ -310,7 +310,7 @@ struct AttnArgs {
 hipError_t launch_copy_blocks(const void* src, void* dst, const int32_t* pairs, int32_t n,
                               int32_t num_pools, int64_t src_stride, int64_t dst_stride,
                               int32_t src_blocks, int32_t dst_blocks, int64_t block_bytes,
-                              hipStream_t s);
+                              bool host_link, hipStream_t s);
 
 // Fused rotary embedding + cache write (one workgroup per token).
 struct RopeArgs {

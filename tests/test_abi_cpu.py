@@ -263,3 +263,21 @@ def test_noalloc_scratch_size_matches_header():
     txt = open(os.path.join(ROOT, "include", "pa.h")).read()
     m = re.search(r"#define PA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", txt)
     assert m and int(m.group(1)) << int(m.group(2)) == pa.NOALLOC_SCRATCH_BYTES
+
+
+def test_swap_blocks_host_checks():
+    """pa_swap_blocks checks its host-side block list before enqueueing
+    anything (dummy pool pointers, never touched)."""
+    L = pa.lib()
+
+    def rc(pairs, n_src=8, n_dst=8, pools=4, bb=1024, sstride=8 * 1024, dstride=8 * 1024, src=4096, dst=8192):
+        a = np.ascontiguousarray(np.asarray(pairs, np.int32).reshape(-1, 2))
+        return pa.status_str(L.pa_swap_blocks(src, dst, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                              a.shape[0], pools, sstride, dstride, n_src, n_dst, bb, None))
+    assert rc([[0, 1], [9, 2]]) == "PA_ERR_OUT_OF_RANGE"
+    assert rc([[0, 1], [2, -1]]) == "PA_ERR_OUT_OF_RANGE"
+    assert rc([[0, 3], [1, 3]]) == "PA_ERR_DUPLICATE_SLOT"
+    assert rc([[0, 1]], sstride=1024) == "PA_ERR_BAD_SHAPE"
+    assert rc([[0, 1]], bb=0) == "PA_ERR_BAD_SHAPE"
+    assert rc([[0, 1]], src=0) == "PA_ERR_NULL_PTR"
+    assert rc(np.zeros((0, 2))) == "PA_OK"

@@ -148,3 +148,96 @@ def test_swap_out_and_in_round_trip_bit_exact():
     assert np.array_equal(bits(after[:, in_dst]), bits(before[:, out_src])), "swap-in copy differs"
     untouched = np.setdiff1d(np.arange(nb), np.concatenate([out_src, in_dst]))
     assert np.array_equal(bits(after[:, untouched]), bits(before[:, untouched]))
+
+
+def test_swap_beside_a_step_on_a_second_stream():
+    """A swap-out of blocks the step does not use (every layer's K and V block,
+    to a pinned host pool, on the copy engines: pa_swap_blocks) on a second
+    stream of default priority, ordered
+    after the inputs with an event and joined afterwards, runs while a step
+    (cache write + attention) runs on the current stream: the swapped bytes are
+    exact, the step's outputs and caches equal the same step run alone bit for
+    bit, and the swap-in onto other free blocks is exact."""
+    from workloads import configs
+    from helpers import run_step
+    spec = configs.custom("swap-step", "bf16", HQ, HKV, D, B, [1, 1, 200, 1, 1], [3000, 900, 700, 4000, 60], 51,
+                          pool_factor=1.6)
+    used = np.unique(np.concatenate([spec.block_table[r, :-(-int(spec.seq_lens[r]) // B)]
+                                     for r in range(spec.R)]))
+    free = np.setdiff1d(np.arange(spec.num_blocks), used).astype(np.int32)
+    assert len(free) >= 64
+    swap_src, swap_back = free[:32], free[32:64]
+    base = spec.device_inputs()
+    # step alone
+    alone = {k: (v.clone() if hasattr(v, "clone") else v) for k, v in base.items()}
+    _, out_alone, _ = run_step(spec, pa, dev_inputs=alone)
+    torch.cuda.synchronize()
+    # more layers' pools beside layer 0, so the swap is long enough to overlap the step
+    layers = 16
+    extra = torch.empty((2 * layers, spec.num_blocks, B, HKV, D), dtype=torch.bfloat16, device="cuda")
+    keys = np.arange(extra.numel() // (HKV * D), dtype=np.uint64) * np.uint64(0x9E3779B1) + np.uint64(5)
+    _fill(extra.view(-1, HKV, D), keys)
+    host = torch.empty((2 * layers, 64, B, HKV, D), dtype=torch.bfloat16, pin_memory=True)
+    host.view(torch.int16).fill_(0x7FC0)
+    before = storage_np(extra[:, torch.from_numpy(swap_src.astype(np.int64)).cuda()])
+    pairs_out = np.stack([swap_src, np.arange(32, dtype=np.int32)], 1)
+    d = {k: (v.clone() if hasattr(v, "clone") else v) for k, v in base.items()}
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()                 # default priority
+    ready = torch.cuda.Event()
+    ready.record(main)                         # inputs and pools are in place
+    side.wait_event(ready)
+    with torch.cuda.stream(side):
+        for _ in range(4):                     # a few hundred MB over the host link, on the copy engines
+            pa.swap_blocks(extra, host, pairs_out, stream=side)
+    _, out, _ = run_step(spec, pa, dev_inputs=d)   # the step, on the current stream
+    done = torch.cuda.Event()
+    done.record(side)
+    main.wait_event(done)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out_alone.view(torch.int16)), "step output differs beside the swap"
+    assert torch.equal(d["key_cache"].view(torch.int16), alone["key_cache"].view(torch.int16))
+    assert torch.equal(d["value_cache"].view(torch.int16), alone["value_cache"].view(torch.int16))
+    assert np.array_equal(bits(storage_np(host[:, :32])), bits(before)), "swapped-out blocks differ"
+    # swap back in, onto other free blocks, beside another run of the step
+    pairs_in = np.stack([np.arange(32, dtype=np.int32), swap_back], 1)
+    ready.record(main)
+    side.wait_event(ready)
+    with torch.cuda.stream(side):
+        pa.swap_blocks(host, extra, pairs_in, stream=side)
+    d2 = {k: (v.clone() if hasattr(v, "clone") else v) for k, v in base.items()}
+    _, out2, _ = run_step(spec, pa, dev_inputs=d2)
+    done.record(side)
+    main.wait_event(done)
+    torch.cuda.synchronize()
+    assert torch.equal(out2.view(torch.int16), out_alone.view(torch.int16))
+    back = storage_np(extra[:, torch.from_numpy(swap_back.astype(np.int64)).cuda()])
+    assert np.array_equal(bits(back), bits(before)), "swapped-in blocks differ"
+
+
+def test_swap_blocks_copy_engines_round_trip():
+    """pa_swap_blocks: runs of consecutive blocks (one 2-D copy each) and
+    scattered blocks go out to a pinned host pool and come back exactly;
+    nothing else changes."""
+    layers, nb, hb = 6, 80, 48
+    pools = torch.empty((2 * layers, nb, B, HKV, D), dtype=torch.bfloat16, device="cuda")
+    keys = np.arange(2 * layers * nb * B, dtype=np.uint64) * np.uint64(0x2545F491) + np.uint64(3)
+    _fill(pools.view(-1, HKV, D), keys)
+    host = torch.empty((2 * layers, hb, B, HKV, D), dtype=torch.bfloat16, pin_memory=True)
+    host.view(torch.int16).fill_(0x7FC0)
+    g = np.random.default_rng(12)
+    src = np.concatenate([np.arange(10, 20), g.choice(np.arange(30, nb), 14, replace=False)]).astype(np.int32)
+    dst = np.concatenate([np.arange(5, 15), g.choice(np.arange(20, hb), 14, replace=False)]).astype(np.int32)
+    before = storage_np(pools)
+    pa.swap_blocks(pools, host, np.stack([src, dst], 1))
+    torch.cuda.synchronize()
+    hs = storage_np(host)
+    assert np.array_equal(bits(hs[:, dst]), bits(before[:, src])), "swap-out differs"
+    assert np.all(hs[:, np.setdiff1d(np.arange(hb), dst)] == 0x7FC0)
+    back = np.setdiff1d(np.arange(nb), src)[:24].astype(np.int32)
+    pa.swap_blocks(host, pools, np.stack([dst, back], 1))
+    torch.cuda.synchronize()
+    after = storage_np(pools)
+    assert np.array_equal(bits(after[:, back]), bits(before[:, src])), "swap-in differs"
+    rest = np.setdiff1d(np.arange(nb), back)
+    assert np.array_equal(bits(after[:, rest]), bits(before[:, rest]))
