@@ -413,6 +413,13 @@ pa_status pa_attention_run(const pa_step_plan* plan, void* out, const void* quer
  *   PA_TUNE_CHUNK_PATH          1: every multi-token request takes the
  *                               split-K path instead of the matrix-core
  *                               chunk kernel
+ *   PA_TUNE_DECODE_STAGING      1: the vector split-K kernel with one
+ *                               wavefront per kv head streaming its own rows
+ *                               through registers, instead of the default
+ *                               (bf16, head_dim 128, up to 4 q heads per kv
+ *                               head, 1/2/4/8 kv heads) of one workgroup per
+ *                               item staging whole 16-token slabs of all kv
+ *                               heads in LDS
  * pa_set_tuning returns PA_ERR_BAD_SHAPE for an unknown knob or a negative
  * value; pa_get_tuning returns -1 for an unknown knob.
  */
@@ -423,7 +430,8 @@ typedef enum pa_tuning_knob {
   PA_TUNE_SPLIT_RULE = 3,
   PA_TUNE_CHUNK_SEGMENT = 4,
   PA_TUNE_CHUNK_PATH = 5,
-  PA_TUNE_COUNT = 6
+  PA_TUNE_DECODE_STAGING = 6,
+  PA_TUNE_COUNT = 7
 } pa_tuning_knob;
 
 pa_status pa_set_tuning(int32_t knob, int32_t value);

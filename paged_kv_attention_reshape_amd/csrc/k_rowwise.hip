@@ -9,8 +9,12 @@
 // absolute position p is key p ("Chunked Prefill 与 Preemption", equation
 // M_{i,j}); the plan gives each item its key range [kb, ke).
 //
-// MI355X design (one wavefront per item x kv head; no atomics, so results are
-// deterministic):
+// MI355X design (no atomics, so results are deterministic).  Two kernels share
+// one sub-tile of math.  The whole-block kernel (bf16, head_dim 128, GQA
+// groups up to 4: the default there) gives an item one workgroup of Hkv
+// waves and stages each 16-token slab of all kv heads in LDS by DMA; the
+// per-head kernel (every other case) gives each (item, kv head) one
+// wavefront that loads its rows itself.  In both, per wave and kv head:
 //   * the G query heads that share kv head g are processed together, so every
 //     K/V byte is read from HBM exactly once per item;
 //   * q.k: lanes are (token j, quarter c) pairs, 16 tokens per sub-tile; each
@@ -27,9 +31,10 @@
 //   * the next sub-tile's K and V are loaded before the current one is used;
 //     they are read with the nontemporal hint: each K/V byte is used once per
 //     step, and streaming it past the caches keeps the split-K partials and
-//     this step's freshly written rows resident (measured: the paged read
-//     pattern goes from about 5.8 to 6.2 TB/s with the hint).
-// fp32 caches use the same structure with plain FMAs.
+//     this step's freshly written rows resident (measured: the per-head read
+//     pattern goes from about 5.8 to 6.2 TB/s with the hint, the whole-block
+//     one from 5.9 to 6.4).
+// fp32 caches use the per-head structure with plain FMAs.
 #include <stdlib.h>
 
 #include <algorithm>
@@ -66,6 +71,9 @@ __device__ __forceinline__ uint4 load_once(const char* p) {
   return make_uint4(x[0], x[1], x[2], x[3]);
 }
 
+// cache-policy operand of global_load_lds: the nontemporal bit (nt)
+constexpr int kDmaNontemporal = 2;
+
 __device__ __forceinline__ uint16_t to_bf16(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
@@ -90,14 +98,250 @@ struct Geo {
   static_assert(NL >= 1 && RPL >= 2 && RPL % 2 == 0, "unsupported geometry");
 };
 
+// One wave's online-softmax state for its G query heads: running max and sum
+// (one head per lane in the softmax layout) and the unnormalised output slice
+// of every head (p.v layout).
+template <bool BF16, int D, int G>
+struct WaveAcc {
+  using Gm = Geo<BF16, D, G>;
+  float m_run[Gm::HPL], l_run[Gm::HPL];
+  float o[G][Gm::EPC];
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int k = 0; k < Gm::HPL; ++k) { m_run[k] = kNegInf; l_run[k] = 0.f; }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < Gm::EPC; ++e) o[h][e] = 0.f;
+  }
+};
+
+// Lane roles: (token j, quarter c) in the q.k layout, (first V row rsub,
+// 16-byte chunk cv) in the p.v layout.
+struct DecodeLanes {
+  int lane, j, c, rsub, cv;
+};
+template <int LPRV>
+__device__ __forceinline__ DecodeLanes decode_lanes(int lane) {
+  return DecodeLanes{lane, lane >> 2, lane & 3, lane / LPRV, lane % LPRV};
+}
+
+// The probabilities and rescale factors handed from the q.k to the p.v lane
+// layout through LDS are only exchanged among the lanes of one wave.  A
+// workgroup of one wave orders the hand-off with its barrier; a wave of a
+// larger workgroup needs no barrier with the other waves (the LDS accesses
+// of one wave complete in order), only the compiler must keep the accesses
+// on their side of the fences.
+template <bool WAVE_ONLY>
+__device__ __forceinline__ void lds_handoff() {
+  if constexpr (WAVE_ONLY) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  } else {
+    __syncthreads();
+  }
+}
+
+// One 16-token sub-tile of one kv head: q.k for the G heads, online softmax,
+// p.v.  kc holds the lane's K chunks (q.k layout), vc its V rows (p.v
+// layout); tokens at or past ke are masked.  The query rows come from q_lds
+// (QLDS) or qv.
+template <bool BF16, int D, int G, bool QLDS, bool WAVE_ONLY>
+__device__ __forceinline__ void decode_subtile(WaveAcc<BF16, D, G>& acc,
+                                               const uint4 (&kc)[Geo<BF16, D, G>::NL],
+                                               uint4 (&vc)[Geo<BF16, D, G>::RPL], const char* q_lds,
+                                               const uint4 (&qv)[QLDS ? 1 : G][QLDS ? 1 : Geo<BF16, D, G>::NL],
+                                               float* p_lds, float* a_lds, int start, int ke,
+                                               float scale_log2, const DecodeLanes& ln) {
+  using Gm = Geo<BF16, D, G>;
+  constexpr int ROWB = Gm::ROWB, LPR = Gm::LPR, NL = Gm::NL, EPC = Gm::EPC;
+  constexpr int RPI = Gm::RPI, RPL = Gm::RPL, HPL = Gm::HPL;
+  const int j = ln.j, c = ln.c, rsub = ln.rsub;
+
+  // ---- q.k for the G heads ------------------------------------------------
+  float s[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      uint4 qq;
+      if constexpr (QLDS)
+        qq = *reinterpret_cast<const uint4*>(q_lds + h * ROWB + (i * LPR + c) * 16);
+      else
+        qq = qv[h][i];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        if constexpr (BF16) {
+          sum = dot2(comp(kc[i], w), comp(qq, w), sum);
+        } else {
+          sum = __builtin_fmaf(__uint_as_float(comp(kc[i], w)), __uint_as_float(comp(qq, w)), sum);
+        }
+      }
+    }
+    sum += dpp<kQuadXor1>(sum);
+    sum += dpp<kQuadXor2>(sum);
+    s[h] = sum;
+  }
+
+  // ---- online softmax: each lane owns heads c, c+4 of token j --------------
+  const bool tok_ok = start + j < ke;
+  bool rescale = false;
+#pragma unroll
+  for (int k = 0; k < HPL; ++k) {
+    const int h = c + 4 * k;
+    const bool hv = h < G;
+    float sv = s[0];
+#pragma unroll
+    for (int hh = 1; hh < G; ++hh) sv = (h == hh) ? s[hh] : sv;
+    const float s2 = (hv && tok_ok) ? sv * scale_log2 : kNegInf;
+    float mx = s2;
+    mx = fmaxf(mx, dpp<kRowRor4>(mx));
+    mx = fmaxf(mx, dpp<kRowRor8>(mx));
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    const float m_new = fmaxf(acc.m_run[k], mx);
+    const bool live = m_new != kNegInf;
+    const float alpha = live ? __builtin_amdgcn_exp2f(acc.m_run[k] - m_new) : 1.f;
+    const float p = live ? __builtin_amdgcn_exp2f(s2 - m_new) : 0.f;
+    acc.l_run[k] = acc.l_run[k] * alpha + p;
+    acc.m_run[k] = m_new;
+    rescale |= alpha != 1.f;
+    if (hv) {
+      if constexpr (BF16) {
+        const int rs = j % RPI, kk = j / RPI;
+        const int pi = (kk >> 1) * RPI + rs;
+        reinterpret_cast<uint16_t*>(p_lds)[(pi * G + h) * 2 + (kk & 1)] = to_bf16(p);
+      } else {
+        p_lds[j * G + h] = p;
+      }
+      if (j == 0) a_lds[h] = alpha;
+    }
+  }
+  const bool any_rescale = __builtin_amdgcn_ballot_w64(rescale) != 0;
+  lds_handoff<WAVE_ONLY>();
+
+  // ---- p.v ------------------------------------------------------------------
+  if (start + 16 > ke) {  // tail sub-tile: rows past the key range may hold NaN
+#pragma unroll
+    for (int k = 0; k < RPL; ++k)
+      if (start + rsub + RPI * k >= ke) vc[k] = make_uint4(0, 0, 0, 0);
+  }
+  if (any_rescale) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float al = a_lds[h];
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc.o[h][e] *= al;
+    }
+  }
+  if constexpr (BF16) {
+#pragma unroll
+    for (int kk = 0; kk < RPL / 2; ++kk) {
+      const uint32_t* pp = reinterpret_cast<const uint32_t*>(p_lds) + (kk * RPI + rsub) * G;
+      uint32_t pr[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) pr[h] = pp[h];
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        const uint32_t lo = comp(vc[2 * kk], e >> 1);
+        const uint32_t hi = comp(vc[2 * kk + 1], e >> 1);
+        const uint32_t vp = __builtin_amdgcn_perm(hi, lo, (e & 1) ? 0x07060302u : 0x05040100u);
+#pragma unroll
+        for (int h = 0; h < G; ++h) acc.o[h][e] = dot2(vp, pr[h], acc.o[h][e]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < RPL; ++k) {
+      const int row = rsub + RPI * k;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float p = p_lds[row * G + h];
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc.o[h][e] = __builtin_fmaf(p, __uint_as_float(comp(vc[k], e)), acc.o[h][e]);
+      }
+    }
+  }
+  lds_handoff<WAVE_ONLY>();
+}
+
+// End of an item: sums over tokens and over V-row groups, then the G heads'
+// rows of token t, kv head g, either normalised into the output (the item
+// covers the whole row) or as a partial (m, l, o) in partition slot `slot`.
+template <bool BF16, int D, int G, bool WAVE_ONLY>
+__device__ __forceinline__ void decode_finish(WaveAcc<BF16, D, G>& acc, float* m_lds, float* l_lds,
+                                              const AttnArgs& a, int t, int g, bool direct, int slot,
+                                              const DecodeLanes& ln) {
+  using Gm = Geo<BF16, D, G>;
+  constexpr int ROWB = Gm::ROWB, EPC = Gm::EPC, LPRV = Gm::LPRV, HPL = Gm::HPL;
+#pragma unroll
+  for (int k = 0; k < HPL; ++k) {
+    float l = acc.l_run[k];
+    l += dpp<kRowRor4>(l);
+    l += dpp<kRowRor8>(l);
+    l += shfl_xor(l, 16);
+    l += shfl_xor(l, 32);
+    const int h = ln.c + 4 * k;
+    if (ln.j == 0 && h < G) {
+      m_lds[h] = acc.m_run[k];
+      l_lds[h] = l;
+    }
+  }
+#pragma unroll
+  for (int off = LPRV; off < 64; off <<= 1)
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc.o[h][e] += shfl_xor(acc.o[h][e], off);
+  lds_handoff<WAVE_ONLY>();
+
+  if (ln.rsub == 0) {
+    const int hq0 = g * G;
+    if (direct) {
+      char* ob = static_cast<char*>(a.out) + ((int64_t)t * a.Hq + hq0) * ROWB + ln.cv * 16;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float inv = 1.f / l_lds[h];
+        if constexpr (BF16) {
+          uint32_t w[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            w[e] = (uint32_t)to_bf16(acc.o[h][2 * e] * inv) | ((uint32_t)to_bf16(acc.o[h][2 * e + 1] * inv) << 16);
+          *reinterpret_cast<uint4*>(ob + h * ROWB) = make_uint4(w[0], w[1], w[2], w[3]);
+        } else {
+          *reinterpret_cast<float4*>(ob + h * ROWB) =
+              make_float4(acc.o[h][0] * inv, acc.o[h][1] * inv, acc.o[h][2] * inv, acc.o[h][3] * inv);
+        }
+      }
+    } else {
+      float* op = a.o_part + ((int64_t)slot * a.Hq + hq0) * D + ln.cv * EPC;
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < EPC; e += 4)
+          *reinterpret_cast<float4*>(op + h * D + e) =
+              make_float4(acc.o[h][e], acc.o[h][e + 1], acc.o[h][e + 2], acc.o[h][e + 3]);
+    }
+  }
+  if (!direct && ln.lane < G) {
+    float* mp = a.ml_part + ((int64_t)slot * a.Hq + g * G + ln.lane) * 2;
+    mp[0] = m_lds[ln.lane];
+    mp[1] = l_lds[ln.lane];
+  }
+}
+
+// Per-head kernel: one wavefront per (item, kv head); its K/V rows stream
+// through registers.
 // QLDS: keep the G query rows in LDS (read with broadcast ds_read_b128 in the
 // q.k loop) instead of registers: G * D / 4 fewer VGPRs per lane, which buys
 // occupancy (more waves, more loads in flight) for the large GQA groups.
 template <bool BF16, int D, int G, bool QLDS>
 __global__ void __launch_bounds__(64) rowwise_kernel(AttnArgs a) {
   using Gm = Geo<BF16, D, G>;
-  constexpr int ROWB = Gm::ROWB, LPR = Gm::LPR, NL = Gm::NL, EPC = Gm::EPC;
-  constexpr int LPRV = Gm::LPRV, RPI = Gm::RPI, RPL = Gm::RPL, HPL = Gm::HPL;
+  constexpr int ROWB = Gm::ROWB, LPR = Gm::LPR, NL = Gm::NL;
+  constexpr int LPRV = Gm::LPRV, RPI = Gm::RPI, RPL = Gm::RPL;
 
   __shared__ __attribute__((aligned(16))) char q_lds[QLDS ? G * ROWB : 16];
   __shared__ float p_lds[16 * G];   // bf16: 8 token pairs x G dwords; fp32: 16 x G
@@ -105,7 +349,7 @@ __global__ void __launch_bounds__(64) rowwise_kernel(AttnArgs a) {
   __shared__ float m_lds[G];
   __shared__ float l_lds[G];
 
-  const int lane = threadIdx.x;
+  const DecodeLanes ln = decode_lanes<LPRV>(threadIdx.x);
   const int4 it = a.items_rw[blockIdx.x];
   const int r = it.x;
   if (r < 0 || r >= a.R) return;
@@ -116,18 +360,13 @@ __global__ void __launch_bounds__(64) rowwise_kernel(AttnArgs a) {
   const bool direct = (it.w & kDirect) != 0;
   const int slot = direct ? 0 : a.rw_slot[blockIdx.x];   // partial slot (plan order)
 
-  const int j = lane >> 2;           // token of the sub-tile (q.k layout)
-  const int c = lane & 3;            // quarter of the head dimension
-  const int rsub = lane / LPRV;      // first V row of this lane (p.v layout)
-  const int cv = lane % LPRV;        // 16-byte chunk of the V row
-
   // query rows of the G heads, in the q.k lane layout (16-byte chunk
   // i * LPR + c of each row); with QLDS the G rows are staged contiguously in
   // LDS, which is the same byte order
   const char* qb = static_cast<const char*>(a.query) + ((int64_t)t * a.Hq + g * G) * ROWB;
   uint4 qv[QLDS ? 1 : G][QLDS ? 1 : NL];
   if constexpr (QLDS) {
-    for (int o = lane * 16; o < G * ROWB; o += 64 * 16)
+    for (int o = ln.lane * 16; o < G * ROWB; o += 64 * 16)
       *reinterpret_cast<uint4*>(q_lds + o) = *reinterpret_cast<const uint4*>(qb + o);
     __syncthreads();
   } else {
@@ -135,15 +374,15 @@ __global__ void __launch_bounds__(64) rowwise_kernel(AttnArgs a) {
     for (int h = 0; h < G; ++h)
 #pragma unroll
       for (int i = 0; i < NL; ++i)
-        qv[h][i] = *reinterpret_cast<const uint4*>(qb + h * ROWB + (i * LPR + c) * 16);
+        qv[h][i] = *reinterpret_cast<const uint4*>(qb + h * ROWB + (i * LPR + ln.c) * 16);
   }
 
   // physical block ids of the partition: lane i holds block kb/B + i
   const int blk0 = kb / a.B;
   const int nblk = (ke - 1) / a.B - blk0 + 1;
   int myblk = 0;
-  if (lane < nblk) {
-    myblk = a.block_table[(int64_t)r * a.M + blk0 + lane];
+  if (ln.lane < nblk) {
+    myblk = a.block_table[(int64_t)r * a.M + blk0 + ln.lane];
     myblk = myblk < 0 ? 0 : (myblk >= a.num_blocks ? a.num_blocks - 1 : myblk);
   }
 
@@ -154,24 +393,17 @@ __global__ void __launch_bounds__(64) rowwise_kernel(AttnArgs a) {
   auto load_tile = [&](int start, uint4 (&kr)[NL], uint4 (&vr)[RPL]) {
     const int blk = __builtin_amdgcn_readlane(myblk, start / a.B - blk0);
     const int64_t slot0 = (int64_t)blk * a.B + (start % a.B);
-    const char* kbp = kcache + (slot0 + j) * slot_stride + (int64_t)g * ROWB;
+    const char* kbp = kcache + (slot0 + ln.j) * slot_stride + (int64_t)g * ROWB;
 #pragma unroll
-    for (int i = 0; i < NL; ++i) kr[i] = load_once(kbp + (i * LPR + c) * 16);
-    const char* vbp = vcache + slot0 * slot_stride + (int64_t)g * ROWB + cv * 16;
+    for (int i = 0; i < NL; ++i) kr[i] = load_once(kbp + (i * LPR + ln.c) * 16);
+    const char* vbp = vcache + slot0 * slot_stride + (int64_t)g * ROWB + ln.cv * 16;
 #pragma unroll
     for (int k = 0; k < RPL; ++k)
-      vr[k] = load_once(vbp + (int64_t)(rsub + RPI * k) * slot_stride);
+      vr[k] = load_once(vbp + (int64_t)(ln.rsub + RPI * k) * slot_stride);
   };
 
-  float m_run[HPL], l_run[HPL];
-#pragma unroll
-  for (int k = 0; k < HPL; ++k) { m_run[k] = kNegInf; l_run[k] = 0.f; }
-  float o[G][EPC];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) o[h][e] = 0.f;
-
+  WaveAcc<BF16, D, G> acc;
+  acc.init();
   const int n_tiles = (ke - kb + 15) >> 4;
   uint4 kc[NL], vc[RPL];
   load_tile(kb, kc, vc);
@@ -180,114 +412,8 @@ __global__ void __launch_bounds__(64) rowwise_kernel(AttnArgs a) {
     const int start = kb + (tile << 4);
     uint4 kn[NL], vn[RPL];
     if (tile + 1 < n_tiles) load_tile(start + 16, kn, vn);
-
-    // ---- q.k for the G heads ----------------------------------------------
-    float s[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float acc = 0.f;
-#pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        uint4 qq;
-        if constexpr (QLDS)
-          qq = *reinterpret_cast<const uint4*>(q_lds + h * ROWB + (i * LPR + c) * 16);
-        else
-          qq = qv[h][i];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          if constexpr (BF16) {
-            acc = dot2(comp(kc[i], w), comp(qq, w), acc);
-          } else {
-            acc = __builtin_fmaf(__uint_as_float(comp(kc[i], w)), __uint_as_float(comp(qq, w)), acc);
-          }
-        }
-      }
-      acc += dpp<kQuadXor1>(acc);
-      acc += dpp<kQuadXor2>(acc);
-      s[h] = acc;
-    }
-
-    // ---- online softmax: each lane owns heads c, c+4 of token j ------------
-    const bool tok_ok = start + j < ke;
-    bool rescale = false;
-#pragma unroll
-    for (int k = 0; k < HPL; ++k) {
-      const int h = c + 4 * k;
-      const bool hv = h < G;
-      float sv = s[0];
-#pragma unroll
-      for (int hh = 1; hh < G; ++hh) sv = (h == hh) ? s[hh] : sv;
-      const float s2 = (hv && tok_ok) ? sv * a.scale_log2 : kNegInf;
-      float mx = s2;
-      mx = fmaxf(mx, dpp<kRowRor4>(mx));
-      mx = fmaxf(mx, dpp<kRowRor8>(mx));
-      mx = fmaxf(mx, shfl_xor(mx, 16));
-      mx = fmaxf(mx, shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[k], mx);
-      const bool live = m_new != kNegInf;
-      const float alpha = live ? __builtin_amdgcn_exp2f(m_run[k] - m_new) : 1.f;
-      const float p = live ? __builtin_amdgcn_exp2f(s2 - m_new) : 0.f;
-      l_run[k] = l_run[k] * alpha + p;
-      m_run[k] = m_new;
-      rescale |= alpha != 1.f;
-      if (hv) {
-        if constexpr (BF16) {
-          const int rs = j % RPI, kk = j / RPI;
-          const int pi = (kk >> 1) * RPI + rs;
-          reinterpret_cast<uint16_t*>(p_lds)[(pi * G + h) * 2 + (kk & 1)] = to_bf16(p);
-        } else {
-          p_lds[j * G + h] = p;
-        }
-        if (j == 0) a_lds[h] = alpha;
-      }
-    }
-    const bool any_rescale = __builtin_amdgcn_ballot_w64(rescale) != 0;
-    __syncthreads();
-
-    // ---- p.v ----------------------------------------------------------------
-    if (start + 16 > ke) {  // tail sub-tile: rows past the key range may hold NaN
-#pragma unroll
-      for (int k = 0; k < RPL; ++k)
-        if (start + rsub + RPI * k >= ke) vc[k] = make_uint4(0, 0, 0, 0);
-    }
-    if (any_rescale) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float al = a_lds[h];
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) o[h][e] *= al;
-      }
-    }
-    if constexpr (BF16) {
-#pragma unroll
-      for (int kk = 0; kk < RPL / 2; ++kk) {
-        const uint32_t* pp = reinterpret_cast<const uint32_t*>(p_lds) + (kk * RPI + rsub) * G;
-        uint32_t pr[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) pr[h] = pp[h];
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-          const uint32_t lo = comp(vc[2 * kk], e >> 1);
-          const uint32_t hi = comp(vc[2 * kk + 1], e >> 1);
-          const uint32_t vp = __builtin_amdgcn_perm(hi, lo, (e & 1) ? 0x07060302u : 0x05040100u);
-#pragma unroll
-          for (int h = 0; h < G; ++h) o[h][e] = dot2(vp, pr[h], o[h][e]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < RPL; ++k) {
-        const int row = rsub + RPI * k;
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float p = p_lds[row * G + h];
-#pragma unroll
-          for (int e = 0; e < EPC; ++e) o[h][e] = __builtin_fmaf(p, __uint_as_float(comp(vc[k], e)), o[h][e]);
-        }
-      }
-    }
-    __syncthreads();
-
+    decode_subtile<BF16, D, G, QLDS, false>(acc, kc, vc, q_lds, qv, p_lds, a_lds, start, ke,
+                                            a.scale_log2, ln);
     if (tile + 1 < n_tiles) {
 #pragma unroll
       for (int i = 0; i < NL; ++i) kc[i] = kn[i];
@@ -295,61 +421,150 @@ __global__ void __launch_bounds__(64) rowwise_kernel(AttnArgs a) {
       for (int k = 0; k < RPL; ++k) vc[k] = vn[k];
     }
   }
+  decode_finish<BF16, D, G, false>(acc, m_lds, l_lds, a, t, g, direct, slot, ln);
+}
 
-  // ---- finish: sums over tokens and over V-row groups ----------------------
+// Whole-block kernel (bf16, head_dim 128, GQA groups of 1, 2 or 4): one
+// workgroup of HKV waves per item, wave g computing kv head g.  The item's
+// keys are read 16 tokens at a time as one contiguous slab of all kv heads
+// (16 * HKV * 256 bytes of K and of V; with 16-token blocks, the whole block)
+// by global -> LDS DMA (global_load_lds_dwordx4, nontemporal) into a double
+// buffer; every wave issues its share of the slab's 1-KB DMA instructions
+// for the next sub-tile, then takes its head's K and V rows from LDS into the
+// same register layouts the per-head kernel loads from memory.  Reading each
+// block whole, rather than as HKV separate 256-byte rows per token fetched by
+// HKV unrelated waves, is what raises the stream (measured on MI355X: the C3
+// split-K pass from 6.08 to 6.37 TB/s, 256 x 4K-token decodes from 6.10 to
+// 6.82 TB/s).
+// LDS layout: slab row (token j, head h) holds its 16 chunks of 16 bytes at
+// positions chunk ^ swz(j), swz(j) = 4 (j mod 4) + (j / 4) mod 4, so that the
+// q.k reads of any 16 consecutive lanes (tokens j..j+3, chunks 4i + c) fall on
+// 16 distinct 16-byte bank groups; each DMA lane fetches the logical chunk
+// that belongs at its physical position.
+__device__ __forceinline__ int slab_swz(int j) { return ((j & 3) << 2) | ((j >> 2) & 3); }
+
+constexpr int kSlabTokens = 16;
+
+template <int G, int HKV>
+__global__ void __launch_bounds__(64 * HKV) rowwise_block_kernel(AttnArgs a) {
+  constexpr int D = 128;
+  using Gm = Geo<true, D, G>;
+  constexpr int ROWB = Gm::ROWB, LPR = Gm::LPR, NL = Gm::NL;
+  constexpr int LPRV = Gm::LPRV, RPI = Gm::RPI, RPL = Gm::RPL;
+  constexpr int CPR = ROWB / 16;                       // 16-byte chunks per head row
+  constexpr int SLAB = kSlabTokens * HKV * ROWB;       // bytes of K (or V) per sub-tile
+  constexpr int DMA_PER_WAVE = SLAB / 1024 / HKV;      // 1-KB DMA instructions per wave
+  static_assert(CPR == 16 && DMA_PER_WAVE * 1024 * HKV == SLAB, "slab geometry");
+  __shared__ __attribute__((aligned(1024))) char k_lds0[SLAB];
+  __shared__ __attribute__((aligned(1024))) char k_lds1[SLAB];
+  __shared__ __attribute__((aligned(1024))) char v_lds0[SLAB];
+  __shared__ __attribute__((aligned(1024))) char v_lds1[SLAB];
+  __shared__ __attribute__((aligned(16))) char q_lds[HKV * G * ROWB];
+  __shared__ float p_lds[HKV * 16 * G];
+  __shared__ float a_lds[HKV * G];
+  __shared__ float m_lds[HKV * G];
+  __shared__ float l_lds[HKV * G];
+  typedef __attribute__((address_space(3))) void* lds_vptr;
+  typedef __attribute__((address_space(1))) void* glb_vptr;
+
+  const DecodeLanes ln = decode_lanes<LPRV>(threadIdx.x & 63);
+  const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int4 it = a.items_rw[blockIdx.x];
+  const int r = it.x;
+  if (r < 0 || r >= a.R) return;
+  const int t = it.y;
+  const int kb = it.z;
+  const int ke = it.w & 0x7FFFFFFF;
+  const bool direct = (it.w & kDirect) != 0;
+  const int slot = direct ? 0 : a.rw_slot[blockIdx.x];
+
+  // this wave's query rows and hand-off areas
+  char* qw = q_lds + g * G * ROWB;
+  float* pw = p_lds + g * 16 * G;
+  float* aw = a_lds + g * G;
+  const char* qb = static_cast<const char*>(a.query) + ((int64_t)t * a.Hq + g * G) * ROWB;
+  for (int o = ln.lane * 16; o < G * ROWB; o += 64 * 16)
+    *reinterpret_cast<uint4*>(qw + o) = *reinterpret_cast<const uint4*>(qb + o);
+
+  const int blk0 = kb / a.B;
+  const int nblk = (ke - 1) / a.B - blk0 + 1;
+  int myblk = 0;
+  if (ln.lane < nblk) {
+    myblk = a.block_table[(int64_t)r * a.M + blk0 + ln.lane];
+    myblk = myblk < 0 ? 0 : (myblk >= a.num_blocks ? a.num_blocks - 1 : myblk);
+  }
+  const char* kcache = static_cast<const char*>(a.kcache);
+  const char* vcache = static_cast<const char*>(a.vcache);
+
+  // DMA lane offsets within a slab: physical chunk q of the slab (wave g's
+  // instruction i, lane l: q = (g * DMA_PER_WAVE + i) * 64 + l) belongs to
+  // token q / (HKV * CPR) and takes that row's logical chunk (q mod CPR) ^ swz
+  uint32_t dma_off[DMA_PER_WAVE];
 #pragma unroll
-  for (int k = 0; k < HPL; ++k) {
-    float l = l_run[k];
-    l += dpp<kRowRor4>(l);
-    l += dpp<kRowRor8>(l);
-    l += shfl_xor(l, 16);
-    l += shfl_xor(l, 32);
-    const int h = c + 4 * k;
-    if (j == 0 && h < G) {
-      m_lds[h] = m_run[k];
-      l_lds[h] = l;
+  for (int i = 0; i < DMA_PER_WAVE; ++i) {
+    const int q = (g * DMA_PER_WAVE + i) * 64 + ln.lane;
+    const int tok = q / (HKV * CPR);
+    dma_off[i] = (uint32_t)(((q & ~(CPR - 1)) | ((q & (CPR - 1)) ^ slab_swz(tok))) * 16);
+  }
+  // The 16 tokens of a sub-tile lie in one cache block (block sizes are
+  // multiples of 16 and sub-tiles start at multiples of 16), contiguous.
+#define PA_SLAB_DMA(START, KD, VD)                                                              \
+  {                                                                                            \
+    const int st_ = (START);                                                                   \
+    const int blk_ = __builtin_amdgcn_readlane(myblk, st_ / a.B - blk0);                       \
+    const uint64_t base_ = ((uint64_t)blk_ * a.B + (st_ % a.B)) * (uint64_t)(HKV * ROWB);     \
+    __builtin_amdgcn_sched_barrier(0);                                                         \
+    _Pragma("unroll") for (int i = 0; i < DMA_PER_WAVE; ++i) {                                 \
+      __builtin_amdgcn_global_load_lds((glb_vptr)(kcache + base_ + dma_off[i]),                \
+                                       (lds_vptr)((KD) + (g * DMA_PER_WAVE + i) * 1024), 16, 0, \
+                                       kDmaNontemporal);                                       \
+      __builtin_amdgcn_global_load_lds((glb_vptr)(vcache + base_ + dma_off[i]),                \
+                                       (lds_vptr)((VD) + (g * DMA_PER_WAVE + i) * 1024), 16, 0, \
+                                       kDmaNontemporal);                                       \
+    }                                                                                          \
+  }
+
+  const int sj = slab_swz(ln.j);
+  int vrow_off[RPL];
+#pragma unroll
+  for (int k = 0; k < RPL; ++k) {
+    const int row = ln.rsub + RPI * k;
+    vrow_off[k] = (row * HKV + g) * ROWB + ((ln.cv ^ slab_swz(row)) << 4);
+  }
+  const uint4 no_qv[1][1] = {};
+  WaveAcc<true, D, G> acc;
+  acc.init();
+  auto subtile = [&](const char* kbuf, const char* vbuf, int start) __attribute__((always_inline)) {
+    uint4 kc[NL], vc[RPL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+      kc[i] = *reinterpret_cast<const uint4*>(kbuf + (ln.j * HKV + g) * ROWB + (((i * LPR + ln.c) ^ sj) << 4));
+#pragma unroll
+    for (int k = 0; k < RPL; ++k) vc[k] = *reinterpret_cast<const uint4*>(vbuf + vrow_off[k]);
+    decode_subtile<true, D, G, true, true>(acc, kc, vc, qw, no_qv, pw, aw, start, ke, a.scale_log2, ln);
+  };
+
+  // vmcnt(0), expcnt/lgkmcnt unconstrained: this wave's DMA into LDS is done
+  constexpr int kWaitDma = 0x0F70;
+  const int n_tiles = (ke - kb + 15) >> 4;
+  PA_SLAB_DMA(kb, k_lds0, v_lds0)
+  for (int tile = 0; tile < n_tiles; tile += 2) {
+    // even sub-tile: buffer 0.  Wait for this wave's part of its DMA, then a
+    // barrier makes every wave's part visible and guarantees buffer 1 is no
+    // longer being read; the next sub-tile's DMA goes out before the math.
+    __builtin_amdgcn_s_waitcnt(kWaitDma);
+    __syncthreads();
+    if (tile + 1 < n_tiles) PA_SLAB_DMA(kb + 16 * (tile + 1), k_lds1, v_lds1)
+    subtile(k_lds0, v_lds0, kb + 16 * tile);
+    if (tile + 1 < n_tiles) {  // odd sub-tile: buffer 1
+      __builtin_amdgcn_s_waitcnt(kWaitDma);
+      __syncthreads();
+      if (tile + 2 < n_tiles) PA_SLAB_DMA(kb + 16 * (tile + 2), k_lds0, v_lds0)
+      subtile(k_lds1, v_lds1, kb + 16 * (tile + 1));
     }
   }
-#pragma unroll
-  for (int off = LPRV; off < 64; off <<= 1)
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) o[h][e] += shfl_xor(o[h][e], off);
-  __syncthreads();
-
-  if (rsub == 0) {
-    const int hq0 = g * G;
-    if (direct) {
-      char* ob = static_cast<char*>(a.out) + ((int64_t)t * a.Hq + hq0) * ROWB + cv * 16;
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float inv = 1.f / l_lds[h];
-        if constexpr (BF16) {
-          uint32_t w[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            w[e] = (uint32_t)to_bf16(o[h][2 * e] * inv) | ((uint32_t)to_bf16(o[h][2 * e + 1] * inv) << 16);
-          *reinterpret_cast<uint4*>(ob + h * ROWB) = make_uint4(w[0], w[1], w[2], w[3]);
-        } else {
-          *reinterpret_cast<float4*>(ob + h * ROWB) =
-              make_float4(o[h][0] * inv, o[h][1] * inv, o[h][2] * inv, o[h][3] * inv);
-        }
-      }
-    } else {
-      float* op = a.o_part + ((int64_t)slot * a.Hq + hq0) * D + cv * EPC;
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < EPC; e += 4)
-          *reinterpret_cast<float4*>(op + h * D + e) = make_float4(o[h][e], o[h][e + 1], o[h][e + 2], o[h][e + 3]);
-    }
-  }
-  if (!direct && lane < G) {
-    float* mp = a.ml_part + ((int64_t)slot * a.Hq + g * G + lane) * 2;
-    mp[0] = m_lds[lane];
-    mp[1] = l_lds[lane];
-  }
+#undef PA_SLAB_DMA
+  decode_finish<true, D, G, true>(acc, m_lds + g * G, l_lds + g * G, a, t, g, direct, slot, ln);
 }
 
 // Merge pass: combine the partial (m, l, o) of one query row's partitions,
@@ -552,6 +767,34 @@ static bool use_mfma(bool bf16, int32_t D, int32_t G) {
   return G >= 8;
 }
 
+// The whole-block kernel where it has an instance (bf16, head_dim 128, GQA
+// groups 1, 2 and 4 on the vector path, 1..8 kv heads); measured faster than
+// the per-head kernel on every decode mix tried (C3's split-K pass 4.5 %,
+// 64 contexts of 512..4096 keys 2 %, 256 contexts of 4K keys 12 %).
+// PA_TUNE_DECODE_STAGING 1 keeps the per-head kernel.
+static const void* block_kernel_for(int32_t G, int32_t Hkv) {
+#define PA_BLOCK_G(HK)                                                   \
+  switch (G) {                                                           \
+    case 1: return (const void*)rowwise_block_kernel<1, HK>;             \
+    case 2: return (const void*)rowwise_block_kernel<2, HK>;             \
+    case 4: return (const void*)rowwise_block_kernel<4, HK>;             \
+    default: return nullptr;                                             \
+  }
+  switch (Hkv) {
+    case 1: PA_BLOCK_G(1)
+    case 2: PA_BLOCK_G(2)
+    case 4: PA_BLOCK_G(4)
+    case 8: PA_BLOCK_G(8)
+    default: return nullptr;
+  }
+#undef PA_BLOCK_G
+}
+
+static bool use_block(bool bf16, int32_t D, int32_t G, int32_t Hkv) {
+  if (!bf16 || D != 128 || use_mfma(bf16, D, G) || block_kernel_for(G, Hkv) == nullptr) return false;
+  return tuning(PA_TUNE_DECODE_STAGING) != 1;
+}
+
 static hipError_t rowwise_kernel_for(bool bf16, int32_t D, int32_t G, const void** out) {
   if (use_mfma(bf16, D, G)) {
     *out = rowwise_mfma_kernel_for(D, G);
@@ -574,35 +817,47 @@ static hipError_t rowwise_kernel_for(bool bf16, int32_t D, int32_t G, const void
 
 hipError_t launch_rowwise(const AttnArgs& a, hipStream_t s) {
   if (a.ps.n_rw == 0) return hipSuccess;
-  const void* kern = nullptr;
-  const hipError_t e = rowwise_kernel_for(a.bf16, a.D, a.Hq / a.Hkv, &kern);
-  if (e != hipSuccess) return e;
   AttnArgs args = a;
   void* params[] = {&args};
+  const int32_t G = a.Hq / a.Hkv;
+  if (use_block(a.bf16, a.D, G, a.Hkv))
+    return hipLaunchKernel(block_kernel_for(G, a.Hkv), dim3(a.ps.n_rw), dim3(64 * a.Hkv), params, 0, s);
+  const void* kern = nullptr;
+  const hipError_t e = rowwise_kernel_for(a.bf16, a.D, G, &kern);
+  if (e != hipSuccess) return e;
   return hipLaunchKernel(kern, dim3(a.ps.n_rw, a.Hkv), dim3(64), params, 0, s);
 }
 
-int64_t rowwise_round_slots(bool bf16, int32_t D, int32_t G) {
+int64_t rowwise_round_slots(bool bf16, int32_t D, int32_t G, int32_t Hkv) {
   // wave slots of one round of the split-K grid: the kernel's occupancy per
-  // compute unit, at most 8 (two per SIMD), times the compute units; cached
-  // per configuration.  A grid that fits in one round streams faster with
-  // about 8 waves per compute unit than with the 12 the vector kernel could
-  // hold (measured on 64 contexts of 512..4096 keys: 107 against 116 us;
-  // fewer concurrent K/V streams per HBM channel)
-  static thread_local int64_t cache[2][2][9][3] = {};
-  const int qi = use_mfma(bf16, D, G) ? 2 : (use_qlds(G) ? 1 : 0);
-  const int di = D == 128 ? 1 : 0;
-  if (G < 1 || G > 8) return 0;
-  int64_t& c = cache[bf16 ? 1 : 0][di][G][qi];
+  // compute unit in waves (workgroups times their waves: Hkv for the
+  // whole-block kernel, one otherwise), at most 8 (two per SIMD), times the
+  // compute units; cached per configuration.  A grid that fits in one round
+  // streams faster with about 8 waves per compute unit than with the 12 the
+  // per-head kernel could hold (measured on 64 contexts of 512..4096 keys:
+  // 107 against 116 us; fewer concurrent K/V streams per HBM channel)
+  static thread_local int64_t cache[2][2][9][4][4] = {};
+  if (G < 1 || G > 8 || Hkv < 1) return 0;
+  const bool blk = use_block(bf16, D, G, Hkv);
+  const int ki = blk ? 3 : (use_mfma(bf16, D, G) ? 2 : (use_qlds(G) ? 1 : 0));
+  const int hi = blk ? 31 - __builtin_clz((unsigned)Hkv) : 0;   // Hkv in {1, 2, 4, 8} there
+  int64_t& c = cache[bf16 ? 1 : 0][D == 128 ? 1 : 0][G][ki][hi];
   if (c == 0) {
     const void* kern = nullptr;
+    int threads = 64;
+    if (blk) {
+      kern = block_kernel_for(G, Hkv);
+      threads = 64 * Hkv;
+    } else if (rowwise_kernel_for(bf16, D, G, &kern) != hipSuccess) {
+      return 0;
+    }
     int dev = 0, cus = 0, per_cu = 0;
-    if (rowwise_kernel_for(bf16, D, G, &kern) != hipSuccess || hipGetDevice(&dev) != hipSuccess ||
+    if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64, 0) != hipSuccess || cus <= 0 ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, 0) != hipSuccess || cus <= 0 ||
         per_cu <= 0)
       return 0;
-    c = (int64_t)cus * std::min(per_cu, 8);
+    c = (int64_t)cus * std::min(per_cu * (threads / 64), 8);
   }
   return c;
 }

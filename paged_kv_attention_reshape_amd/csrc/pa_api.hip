@@ -253,7 +253,7 @@ pa_status make_plan(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R, 
       rowwise_keys += q * (c + 1) + (int64_t)q * (q - 1) / 2;
     }
   }
-  const int64_t resident = rowwise_keys > 0 ? pa::rowwise_round_slots(bf16, D, G) : 0;
+  const int64_t resident = rowwise_keys > 0 ? pa::rowwise_round_slots(bf16, D, G, Hkv) : 0;
   ps.S = choose_split(h_qsl, h_seq_lens, R, M, rowwise_keys, Hkv, resident, ps);
   ps.SEG = choose_segment(h_qsl, h_seq_lens, R, M, B, Hkv, ps);
   int64_t n_rw = 0, n_ck = 0, n_mg = 0, n_parts = 0;
@@ -320,7 +320,7 @@ PlanBound plan_bound(int64_t R_max, int64_t T_max, int64_t L_max, int32_t Hq, in
   if (forced > 0) {
     k_over_s = cdiv64(K, forced);
   } else {
-    const int64_t resident = pa::rowwise_round_slots(bf16, D, G);
+    const int64_t resident = pa::rowwise_round_slots(bf16, D, G, Hkv);
     if (resident > 0 && pa::tuning(PA_TUNE_SPLIT_RULE) != 1)
       k_over_s = std::max(3 * cdiv64(resident, Hkv), cdiv64(K, sl.longest));
     else

@@ -336,7 +336,7 @@ hipError_t launch_rowwise(const AttnArgs& a, hipStream_t s);
 const void* rowwise_mfma_kernel_for(int32_t D, int32_t G);
 // Wave slots of one round of the split-K grid on the current device for this
 // configuration (0 when the device cannot be queried).
-int64_t rowwise_round_slots(bool bf16, int32_t D, int32_t G);
+int64_t rowwise_round_slots(bool bf16, int32_t D, int32_t G, int32_t Hkv);
 hipError_t launch_chunk(const AttnArgs& a, hipStream_t s);
 hipError_t launch_merge(const AttnArgs& a, hipStream_t s);
 bool chunk_kernel_supports(bool bf16, int32_t D, int32_t G, int32_t B);

@@ -6,8 +6,9 @@
   oracle (caches bit-exact, outputs within the dtype's tolerance).
 * A wider seeded sweep: up to 12 requests with histories up to 20 000 keys
   and chunks up to 700 tokens, with the decode kernel (matrix-core or
-  vector) and the partition length (64, 128 or 512 keys, or the automatic
-  rule) drawn per case.
+  vector), the vector kernel's staging (whole-block or per-head) and the
+  partition length (64, 128 or 512 keys, or the automatic rule) drawn per
+  case.
 * Rows with more than 64 split-K partitions (the merge pass then makes
   several passes over the partitions): forced 64-key partitions over
   contexts of thousands of keys, and genuinely long contexts (70 000 keys)
@@ -77,7 +78,8 @@ def _wide_case(i):
                                   int(g.integers(5000, 20000))], p=[0.1, 0.2, 0.5, 0.2])))
     mfma = ["0", "1", None][int(g.integers(0, 3))]
     split = [None, "64", "128", "512"][int(g.integers(0, 4))]
-    return dtype, G * Hkv, Hkv, D, B, qlens, comp, mfma, split
+    staging = int(np.random.default_rng(30000 + i).integers(0, 2))   # 0 auto, 1 per-head
+    return dtype, G * Hkv, Hkv, D, B, qlens, comp, mfma, split, staging
 
 
 WIDE = [_wide_case(i) for i in range(64)]
@@ -85,11 +87,12 @@ WIDE = [_wide_case(i) for i in range(64)]
 
 @pytest.mark.parametrize("i", range(len(WIDE)), ids=[f"wide{i}" for i in range(len(WIDE))])
 def test_wide_random_steps_match_oracle(i):
-    dtype, Hq, Hkv, D, B, qlens, comp, mfma, split = WIDE[i]
+    dtype, Hq, Hkv, D, B, qlens, comp, mfma, split, staging = WIDE[i]
     say(f"\n[gpu-test] wide random step {i}: {WIDE[i]}")
     spec = configs.custom(f"wide{i}", dtype, Hq, Hkv, D, B, qlens, comp, seed=20000 + i, pool_factor=1.3)
     knobs = {"decode_kernel": None if mfma is None else (2 if mfma == "1" else 1),
-             "split_keys": None if split is None else int(split)}
+             "split_keys": None if split is None else int(split),
+             "decode_staging": staging or None}
     with pa.tuning(**knobs):
         d, out, _ = run_step(spec, pa)
     torch.cuda.synchronize()
@@ -98,19 +101,24 @@ def test_wide_random_steps_match_oracle(i):
     say(f"wide random step {i}: worst abs err {err:.2e}")
 
 
-@pytest.mark.parametrize("kernel", ["matrix", "vector"])
+_KERNELS = {"matrix": dict(decode_kernel=2), "vector": dict(decode_kernel=1),
+            "per-head": dict(decode_kernel=1, decode_staging=1)}
+
+
+@pytest.mark.parametrize("kernel", list(_KERNELS))
 @pytest.mark.parametrize("shape", [(32, 8, 128, 16), (64, 8, 128, 32), (16, 8, 64, 16)],
                          ids=["g4-d128-b16", "g8-d128-b32", "g2-d64-b16"])
 def test_more_than_64_partitions_forced(kernel, shape):
     """64-key partitions over up to 9000 keys: up to 141 partials per row.
-    (With 2 q heads per kv head both settings run the vector kernel, the only
-    one with that instance.)"""
+    (A setting without an instance for the shape runs the kernel that has
+    one: with 2 q heads per kv head and head_dim 64, the per-head vector
+    kernel.)"""
     Hq, Hkv, D, B = shape
     qlens = [1, 1, 1, 1]
     comp = [4095, 4096 + 63, 8999, 130]
     spec = configs.custom(f"p64-{kernel}-{Hq}", "bf16", Hq, Hkv, D, B, qlens, comp,
                           seed=71 + Hq, pool_factor=1.2)
-    with pa.tuning(decode_kernel=2 if kernel == "matrix" else 1, split_keys=64):
+    with pa.tuning(split_keys=64, **_KERNELS[kernel]):
         d, out, _ = run_step(spec, pa)
     torch.cuda.synchronize()
     err = check_requests(spec, out, d["key_cache"], d["value_cache"], range(spec.R),
