@@ -130,18 +130,72 @@ int64_t rowwise_waves(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R
   return n * Hkv;
 }
 
+// Keys of every row that takes the split-K path (decode rows; with
+// rowwise_all, every query row), or false when there are more than `limit`.
+bool rowwise_row_keys(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R, int32_t M,
+                      const pa::PlanShape& ps, size_t limit, std::vector<int64_t>* keys) {
+  keys->clear();
+  for (int32_t r = 0; r < R; ++r) {
+    int32_t q = h_qsl[r + 1] - h_qsl[r];
+    int32_t L = h_seq_lens[r];
+    pa::sanitize(q, L, M, ps.B);
+    if (q <= 0 || !pa::goes_rowwise(q, ps)) continue;
+    if (keys->size() + (size_t)q > limit) return false;
+    for (int32_t i = 0; i < q; ++i) keys->push_back((int64_t)(L - q) + i + 1);
+  }
+  return true;
+}
+
+// Per-item cost of a split-K work item beyond its keys, in keys: prologue,
+// pipeline fill, partial write and its share of the merge (fitted to the
+// measured partition-length sweeps below).
+constexpr int64_t kItemOverheadKeys = 128;
+
+// Makespan (in keys) of longest-processing-time list scheduling of the split-K
+// items at partition length S on P item slots: the hardware dispatches the
+// workgroups in launch order, which the planner sorts longest first, onto
+// whichever slot frees first.  A row of k keys makes floor((k-1)/S) full
+// items and one remainder; the full items, the longest, are dealt first and
+// spread evenly (the slots are then loaded q or q + 1 times), the remainders
+// follow longest first, each onto the least-loaded slot.
+int64_t lpt_makespan(const std::vector<int64_t>& row_keys, int64_t S, int64_t P, std::vector<int64_t>* rem,
+                     std::vector<int64_t>* heap) {
+  rem->clear();
+  int64_t full = 0;
+  for (const int64_t k : row_keys) {
+    const int64_t n = (k + S - 1) / S;
+    full += n - 1;
+    rem->push_back(k - (n - 1) * S + kItemOverheadKeys);
+  }
+  std::sort(rem->begin(), rem->end(), std::greater<int64_t>());
+  const int64_t cost = S + kItemOverheadKeys;
+  heap->assign((size_t)P, (full / P) * cost);
+  for (int64_t i = 0; i < full % P; ++i) (*heap)[(size_t)i] += cost;
+  std::make_heap(heap->begin(), heap->end(), std::greater<int64_t>());
+  for (const int64_t c : *rem) {
+    std::pop_heap(heap->begin(), heap->end(), std::greater<int64_t>());
+    heap->back() += c;
+    std::push_heap(heap->begin(), heap->end(), std::greater<int64_t>());
+  }
+  return *std::max_element(heap->begin(), heap->end());
+}
+
 // Row-wise partition length: a multiple of lcm(64, B), at most 64 blocks (one
 // block id per lane of the wavefront) and 2048 keys.  With the round's wave
 // slots known (resident = min(occupancy, 8) waves per compute unit x compute
-// units; 0 if unknown):
+// units, so P = resident / Hkv item slots; 0 if unknown):
 //  * when the whole split-K grid fits in one round at some length, the
 //    shortest such length (any multiple of the unit: the grid then fills
 //    nearly every slot, each wave as short as that allows);
-//  * otherwise several rounds run, and longest-first list scheduling ends
-//    near max(keys per slot, longest item): every length up to the keys per
-//    slot is as good by that bound, and the longest of them makes the fewest
-//    items, partial results and merges (measured on 16 x 32K + 240 short
-//    contexts: 2048-key partitions 651 us, 1024 674 us, 512 729 us).
+//  * otherwise several rounds run: the length, among the multiples of the
+//    unit from a quarter of the keys per slot (K / P) up to the longest, whose
+//    simulated longest-first makespan is shortest (ties: the longer length,
+//    fewer partials).  Measured on MI355X, best length against the old
+//    choice of the keys per slot rounded down: 125 decode rows of about 2 K
+//    keys 640 keys (226 us; 1024 keys 276 us); 16 x 32K + 240 short contexts
+//    2048 (651 us; 1024 672 us, 512 727 us); C3's 512 decode rows 1024
+//    (1107 us; 512 1179 us) -- the simulation picks each of these.  Steps
+//    with more than 65536 split-K rows keep the keys per slot rounded down.
 // Without the slot count: a power-of-two multiple of the unit (<= 1024 keys)
 // that gives the grid roughly 32 wavefronts per compute unit.
 int32_t choose_split(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R, int32_t M,
@@ -163,7 +217,19 @@ int32_t choose_split(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R,
       }
       return (int32_t)(lo * unit);
     }
+    const int64_t P = std::max<int64_t>(1, resident / Hkv);
     const int64_t per_slot = rowwise_keys * Hkv / resident;
+    // at least a quarter of the keys per slot, so K / S <= 4 P (the workspace bound)
+    const int64_t s_min = std::max(unit, cdiv64(cdiv64(rowwise_keys * Hkv, 4 * resident), unit) * unit);
+    std::vector<int64_t> keys, rem, heap;
+    if (s_min < longest && rowwise_row_keys(h_qsl, h_seq_lens, R, M, ps, 65536, &keys)) {
+      int64_t best = longest, best_t = lpt_makespan(keys, longest, P, &rem, &heap);
+      for (int64_t S = longest - unit; S >= s_min; S -= unit) {
+        const int64_t t = lpt_makespan(keys, S, P, &rem, &heap);
+        if (t < best_t) { best = S; best_t = t; }
+      }
+      return (int32_t)best;
+    }
     return (int32_t)std::min(longest, std::max(unit, per_slot / unit * unit));
   }
   const int64_t target_waves = 256 * 32;
@@ -286,10 +352,11 @@ pa_status make_plan(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R, 
 //    n_rw <= K/S + N with N <= Nmax (decode rows: min(R, T); every row when
 //    multi-token requests go row-wise too) and K <= Nmax L_max.  K/S:
 //    forced S: K/S directly.  Occupancy rule with R slots of waves: a
-//    one-round grid has n_rw Hkv <= R; otherwise S = unit when the keys per
-//    slot K Hkv / R are below a unit (then K/S < R/Hkv), S = floor(keys per
-//    slot to the unit) >= half the keys per slot (K/S <= 2 R/Hkv * 64/63 <
-//    3 R/Hkv), or S = longest (K/S <= K/longest).  Device-independent rule:
+//    one-round grid has n_rw Hkv <= R; otherwise S >= a quarter of the keys
+//    per slot K Hkv / R (K/S <= 4 R/Hkv), or S = the unit when that quarter
+//    is below it (K/S < 4 R/Hkv too), or S = floor(keys per slot to the unit)
+//    >= half the keys per slot (K/S < 3 R/Hkv), or S = longest (K/S <=
+//    K/longest).  Device-independent rule:
 //    S >= want = floor(K Hkv / 8192) gives K/S < 16384/Hkv, else S = top.
 //  * chunk q-tiles: Nqt <= floor(T/TQ) + Rck with Rck <= min(R, T/2) chunk
 //    requests; a tile has cdiv(kmax, SEG) <= cdiv(L_max, SEG) segments and
@@ -322,7 +389,7 @@ PlanBound plan_bound(int64_t R_max, int64_t T_max, int64_t L_max, int32_t Hq, in
   } else {
     const int64_t resident = pa::rowwise_round_slots(bf16, D, G, Hkv);
     if (resident > 0 && pa::tuning(PA_TUNE_SPLIT_RULE) != 1)
-      k_over_s = std::max(3 * cdiv64(resident, Hkv), cdiv64(K, sl.longest));
+      k_over_s = std::max(4 * cdiv64(resident, Hkv), cdiv64(K, sl.longest));
     else
       k_over_s = std::max(cdiv64(16384, Hkv), cdiv64(K, sl.top));
   }

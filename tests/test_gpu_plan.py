@@ -113,3 +113,38 @@ def test_device_metadata_shorter_than_mirrors_leaves_other_rows_intact():
     t0 = int(spec.query_start_loc[1])
     assert torch.equal(out[t0:].view(torch.int16), ref[t0:].view(torch.int16))
     assert bool(torch.isfinite(out[0].float()).all())
+
+
+def test_stale_merge_records_in_the_workspace_never_run():
+    """The workspace is filled with merge records that, if executed, would
+    rewrite the step's last row from partial slot 0.  A step whose device
+    seq_lens give one merge record fewer than the host mirrors sized (request
+    0 cut from 3000 keys to 16 on the device) leaves one such record in the
+    table's tail unless the planner fills the tail with sentinels; the last
+    row must equal the consistent step's bit for bit."""
+    spec = configs.custom("stale-mg", "bf16", 32, 8, 128, 16, [1, 1, 64, 1, 1, 40, 1],
+                          [2999, 1500, 700, 2500, 60, 1200, 3100], 44)
+    d = spec.device_inputs()
+    qsl, sl, sm = pa.build_step_metadata(spec.query_lens, spec.num_computed, spec.block_table,
+                                         spec.B, spec.num_blocks)
+    pa.write_kv(d["key"], d["value"], d["key_cache"], d["value_cache"], torch.from_numpy(sm).cuda())
+    short = d["seq_lens"].clone()
+    short[0] = 16
+    T = spec.T
+    with pa.tuning(split_keys=256):
+        size = pa.attention_workspace_size(qsl, sl, spec.Hq, spec.Hkv, spec.D, spec.B, pa.PA_BF16)
+        ref = torch.empty_like(d["query"])
+        pa.attention(ref, d["query"], d["key_cache"], d["value_cache"], d["block_table"], d["query_start_loc"],
+                     d["seq_lens"], d["num_computed"], qsl, sl, spec.scale, pa.alloc_workspace(size))
+        ws = pa.alloc_workspace(size)
+        assert ws.numel() % 16 == 0
+        # (t_first, first partial, partitions, n_tok << 16 | stride): a valid-looking record
+        rec = torch.tensor([T - 1, 0, 1, (1 << 16) | 1], dtype=torch.int32, device=ws.device)
+        ws.view(torch.int32).view(-1, 4)[:] = rec
+        out = torch.empty_like(d["query"])
+        pa.attention(out, d["query"], d["key_cache"], d["value_cache"], d["block_table"], d["query_start_loc"],
+                     short, d["num_computed"], qsl, sl, spec.scale, ws)
+    torch.cuda.synchronize()
+    t0 = int(spec.query_start_loc[1])
+    assert torch.equal(out[t0:].view(torch.int16), ref[t0:].view(torch.int16)), \
+        "a stale merge record rewrote rows of other requests"
