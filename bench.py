@@ -44,6 +44,8 @@ def decode_kernel_name(spec) -> str:
     tuning (its own rule, restated here as a label for the report)."""
     G = spec.Hq // spec.Hkv
     if spec.dtype == "bf16" and G == 8:
+        if spec.D == 128 and spec.Hkv in (1, 2, 4, 8):
+            return "rowwise_mfma_block_kernel (whole-block split-K decode on the matrix cores)"
         return "rowwise_mfma_kernel (split-K decode on the matrix cores)"
     if spec.dtype == "bf16" and spec.D == 128 and G in (1, 2, 4) and spec.Hkv in (1, 2, 4, 8):
         return "rowwise_block_kernel (whole-block split-K decode)"
@@ -285,6 +287,7 @@ def serving_measurement(dev, first: int = 40, steps: int = 20, layers: int = 32)
     gen = torch.Generator(device=dev).manual_seed(5)
     scale = 1.0 / np.sqrt(D)
     total_ms, total_tok, n_dec, n_chunk_tok = 0.0, 0, 0, 0
+    host_plan_s = 0.0
     dec_bytes, chunk_flops = 0, 0
     acc = {"plan": 0.0, "write_kv": 0.0, "rowwise": 0.0, "chunk": 0.0, "merge": 0.0}
     per_step = []
@@ -309,7 +312,9 @@ def serving_measurement(dev, first: int = 40, steps: int = 20, layers: int = 32)
         e0, e1 = ev(), ev()
         e0.record(stream)
         # planned once per step (the metadata has no layer dimension), run per layer
+        h0 = time.perf_counter()
         plan = pa.attention_plan(d["bt"], d["qsl"], d["sl"], d["nc"], qsl, sl, HQ, kc.shape[1:], pa.PA_BF16, ws)
+        host_plan_s += time.perf_counter() - h0
         for layer in range(layers):
             pa.write_kv(k, v, kc[layer], vc[layer], d["sm"])
             pa.attention_run(plan, out, q, kc[layer], vc[layer], scale)
@@ -365,6 +370,7 @@ def serving_measurement(dev, first: int = 40, steps: int = 20, layers: int = 32)
             "chunk_tflops": round(ck_tf, 1) if ck_tf else None,
             "chunk_frac_mfma": round(ck_tf / MFMA_BF16_PEAK_TFLOPS, 4) if ck_tf else None,
             "workspace_bytes": ws_bytes,
+            "host_plan_us_per_step": round(1e6 * host_plan_s / n, 1),
             "trace": "2048 requests at step 0, prompts lognormal median 1500, outputs geometric mean 256, "
                      "chunk 512, budget 8192, 16384 blocks of 16; Hq 32, Hkv 8, D 128",
             "includes": "write_kv + attention (slot mapping built on the host) for every layer of the step; "

@@ -413,13 +413,12 @@ pa_status pa_attention_run(const pa_step_plan* plan, void* out, const void* quer
  *   PA_TUNE_CHUNK_PATH          1: every multi-token request takes the
  *                               split-K path instead of the matrix-core
  *                               chunk kernel
- *   PA_TUNE_DECODE_STAGING      1: the vector split-K kernel with one
+ *   PA_TUNE_DECODE_STAGING      1: the split-K kernels' per-head form (one
  *                               wavefront per kv head streaming its own rows
- *                               through registers, instead of the default
- *                               (bf16, head_dim 128, up to 4 q heads per kv
- *                               head, 1/2/4/8 kv heads) of one workgroup per
- *                               item staging whole 16-token slabs of all kv
- *                               heads in LDS
+ *                               through registers) instead of the default
+ *                               whole-block form (bf16, head_dim 128, 1/2/4/8
+ *                               kv heads: one workgroup per item staging whole
+ *                               16-token slabs of all kv heads in LDS)
  * pa_set_tuning returns PA_ERR_BAD_SHAPE for an unknown knob or a negative
  * value; pa_get_tuning returns -1 for an unknown knob.
  */

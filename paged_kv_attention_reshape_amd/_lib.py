@@ -43,7 +43,7 @@ TUNING = {
     "split_rule": 3,           # 1 device-independent partition rule
     "chunk_segment": 4,        # n > 0: chunk key-segment length
     "chunk_path": 5,           # 1 multi-token requests on the split-K path
-    "decode_staging": 6,       # 1 per-head vector split-K kernel, not the whole-block one
+    "decode_staging": 6,       # 1 per-head split-K kernels, not the whole-block ones
 }
 
 

@@ -71,9 +71,6 @@ __device__ __forceinline__ uint4 load_once(const char* p) {
   return make_uint4(x[0], x[1], x[2], x[3]);
 }
 
-// cache-policy operand of global_load_lds: the nontemporal bit (nt)
-constexpr int kDmaNontemporal = 2;
-
 __device__ __forceinline__ uint16_t to_bf16(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
@@ -425,26 +422,14 @@ __global__ void __launch_bounds__(64) rowwise_kernel(AttnArgs a) {
 }
 
 // Whole-block kernel (bf16, head_dim 128, GQA groups of 1, 2 or 4): one
-// workgroup of HKV waves per item, wave g computing kv head g.  The item's
-// keys are read 16 tokens at a time as one contiguous slab of all kv heads
-// (16 * HKV * 256 bytes of K and of V; with 16-token blocks, the whole block)
-// by global -> LDS DMA (global_load_lds_dwordx4, nontemporal) into a double
-// buffer; every wave issues its share of the slab's 1-KB DMA instructions
-// for the next sub-tile, then takes its head's K and V rows from LDS into the
-// same register layouts the per-head kernel loads from memory.  Reading each
-// block whole, rather than as HKV separate 256-byte rows per token fetched by
-// HKV unrelated waves, is what raises the stream (measured on MI355X: the C3
-// split-K pass from 6.08 to 6.37 TB/s, 256 x 4K-token decodes from 6.10 to
-// 6.82 TB/s).
-// LDS layout: slab row (token j, head h) holds its 16 chunks of 16 bytes at
-// positions chunk ^ swz(j), swz(j) = 4 (j mod 4) + (j / 4) mod 4, so that the
-// q.k reads of any 16 consecutive lanes (tokens j..j+3, chunks 4i + c) fall on
-// 16 distinct 16-byte bank groups; each DMA lane fetches the logical chunk
-// that belongs at its physical position.
-__device__ __forceinline__ int slab_swz(int j) { return ((j & 3) << 2) | ((j >> 2) & 3); }
-
-constexpr int kSlabTokens = 16;
-
+// workgroup of HKV waves per item, wave g computing kv head g from slabs of
+// all kv heads staged in LDS (see slab_dma) in a double buffer; every wave
+// issues its share of the next slab's DMA, then takes its head's K and V
+// rows from LDS into the same register layouts the per-head kernel loads from
+// memory.  Reading each block whole, rather than as HKV separate 256-byte
+// rows per token fetched by HKV unrelated waves, is what raises the stream
+// (measured on MI355X: the C3 split-K pass from 6.08 to 6.37 TB/s, 256 x
+// 4K-token decodes from 6.10 to 6.82 TB/s).
 template <int G, int HKV>
 __global__ void __launch_bounds__(64 * HKV) rowwise_block_kernel(AttnArgs a) {
   constexpr int D = 128;
@@ -464,9 +449,6 @@ __global__ void __launch_bounds__(64 * HKV) rowwise_block_kernel(AttnArgs a) {
   __shared__ float a_lds[HKV * G];
   __shared__ float m_lds[HKV * G];
   __shared__ float l_lds[HKV * G];
-  typedef __attribute__((address_space(3))) void* lds_vptr;
-  typedef __attribute__((address_space(1))) void* glb_vptr;
-
   const DecodeLanes ln = decode_lanes<LPRV>(threadIdx.x & 63);
   const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int4 it = a.items_rw[blockIdx.x];
@@ -496,33 +478,16 @@ __global__ void __launch_bounds__(64 * HKV) rowwise_block_kernel(AttnArgs a) {
   const char* kcache = static_cast<const char*>(a.kcache);
   const char* vcache = static_cast<const char*>(a.vcache);
 
-  // DMA lane offsets within a slab: physical chunk q of the slab (wave g's
-  // instruction i, lane l: q = (g * DMA_PER_WAVE + i) * 64 + l) belongs to
-  // token q / (HKV * CPR) and takes that row's logical chunk (q mod CPR) ^ swz
+  // DMA lane offsets within a slab (wave g's instruction i, lane l: physical
+  // chunk (g * DMA_PER_WAVE + i) * 64 + l)
   uint32_t dma_off[DMA_PER_WAVE];
 #pragma unroll
-  for (int i = 0; i < DMA_PER_WAVE; ++i) {
-    const int q = (g * DMA_PER_WAVE + i) * 64 + ln.lane;
-    const int tok = q / (HKV * CPR);
-    dma_off[i] = (uint32_t)(((q & ~(CPR - 1)) | ((q & (CPR - 1)) ^ slab_swz(tok))) * 16);
-  }
-  // The 16 tokens of a sub-tile lie in one cache block (block sizes are
-  // multiples of 16 and sub-tiles start at multiples of 16), contiguous.
-#define PA_SLAB_DMA(START, KD, VD)                                                              \
-  {                                                                                            \
-    const int st_ = (START);                                                                   \
-    const int blk_ = __builtin_amdgcn_readlane(myblk, st_ / a.B - blk0);                       \
-    const uint64_t base_ = ((uint64_t)blk_ * a.B + (st_ % a.B)) * (uint64_t)(HKV * ROWB);     \
-    __builtin_amdgcn_sched_barrier(0);                                                         \
-    _Pragma("unroll") for (int i = 0; i < DMA_PER_WAVE; ++i) {                                 \
-      __builtin_amdgcn_global_load_lds((glb_vptr)(kcache + base_ + dma_off[i]),                \
-                                       (lds_vptr)((KD) + (g * DMA_PER_WAVE + i) * 1024), 16, 0, \
-                                       kDmaNontemporal);                                       \
-      __builtin_amdgcn_global_load_lds((glb_vptr)(vcache + base_ + dma_off[i]),                \
-                                       (lds_vptr)((VD) + (g * DMA_PER_WAVE + i) * 1024), 16, 0, \
-                                       kDmaNontemporal);                                       \
-    }                                                                                          \
-  }
+  for (int i = 0; i < DMA_PER_WAVE; ++i)
+    dma_off[i] = slab_source_offset<HKV, CPR>((g * DMA_PER_WAVE + i) * 64 + ln.lane);
+  auto slab_base = [&](int start) -> uint64_t {
+    const int blk = __builtin_amdgcn_readlane(myblk, start / a.B - blk0);
+    return ((uint64_t)blk * a.B + (start % a.B)) * (uint64_t)(HKV * ROWB);
+  };
 
   const int sj = slab_swz(ln.j);
   int vrow_off[RPL];
@@ -544,26 +509,23 @@ __global__ void __launch_bounds__(64 * HKV) rowwise_block_kernel(AttnArgs a) {
     decode_subtile<true, D, G, true, true>(acc, kc, vc, qw, no_qv, pw, aw, start, ke, a.scale_log2, ln);
   };
 
-  // vmcnt(0), expcnt/lgkmcnt unconstrained: this wave's DMA into LDS is done
-  constexpr int kWaitDma = 0x0F70;
   const int n_tiles = (ke - kb + 15) >> 4;
-  PA_SLAB_DMA(kb, k_lds0, v_lds0)
+  slab_dma(kcache, vcache, slab_base(kb), dma_off, k_lds0, v_lds0, g);
   for (int tile = 0; tile < n_tiles; tile += 2) {
     // even sub-tile: buffer 0.  Wait for this wave's part of its DMA, then a
     // barrier makes every wave's part visible and guarantees buffer 1 is no
     // longer being read; the next sub-tile's DMA goes out before the math.
     __builtin_amdgcn_s_waitcnt(kWaitDma);
     __syncthreads();
-    if (tile + 1 < n_tiles) PA_SLAB_DMA(kb + 16 * (tile + 1), k_lds1, v_lds1)
+    if (tile + 1 < n_tiles) slab_dma(kcache, vcache, slab_base(kb + 16 * (tile + 1)), dma_off, k_lds1, v_lds1, g);
     subtile(k_lds0, v_lds0, kb + 16 * tile);
     if (tile + 1 < n_tiles) {  // odd sub-tile: buffer 1
       __builtin_amdgcn_s_waitcnt(kWaitDma);
       __syncthreads();
-      if (tile + 2 < n_tiles) PA_SLAB_DMA(kb + 16 * (tile + 2), k_lds0, v_lds0)
+      if (tile + 2 < n_tiles) slab_dma(kcache, vcache, slab_base(kb + 16 * (tile + 2)), dma_off, k_lds0, v_lds0, g);
       subtile(k_lds1, v_lds1, kb + 16 * (tile + 1));
     }
   }
-#undef PA_SLAB_DMA
   decode_finish<true, D, G, true>(acc, m_lds + g * G, l_lds + g * G, a, t, g, direct, slot, ln);
 }
 
@@ -767,11 +729,8 @@ static bool use_mfma(bool bf16, int32_t D, int32_t G) {
   return G >= 8;
 }
 
-// The whole-block kernel where it has an instance (bf16, head_dim 128, GQA
-// groups 1, 2 and 4 on the vector path, 1..8 kv heads); measured faster than
-// the per-head kernel on every decode mix tried (C3's split-K pass 4.5 %,
-// 64 contexts of 512..4096 keys 2 %, 256 contexts of 4K keys 12 %).
-// PA_TUNE_DECODE_STAGING 1 keeps the per-head kernel.
+// The whole-block vector kernel's instances (bf16, head_dim 128, GQA groups
+// 1, 2 and 4, 1..8 kv heads); nullptr elsewhere.
 static const void* block_kernel_for(int32_t G, int32_t Hkv) {
 #define PA_BLOCK_G(HK)                                                   \
   switch (G) {                                                           \
@@ -790,15 +749,33 @@ static const void* block_kernel_for(int32_t G, int32_t Hkv) {
 #undef PA_BLOCK_G
 }
 
-static bool use_block(bool bf16, int32_t D, int32_t G, int32_t Hkv) {
-  if (!bf16 || D != 128 || use_mfma(bf16, D, G) || block_kernel_for(G, Hkv) == nullptr) return false;
-  return tuning(PA_TUNE_DECODE_STAGING) != 1;
-}
+// The split-K kernel of a configuration and its launch shape: whole-block
+// kernels run one workgroup of Hkv waves per item (grid n_rw), per-head
+// kernels one wavefront per (item, kv head) (grid n_rw x Hkv).  The
+// whole-block forms are the default wherever they have an instance: measured
+// faster than the per-head kernels on every decode mix tried (C3's split-K
+// pass 4.5 %, 64 contexts of 512..4096 keys 2 %, 256 contexts of 4K keys
+// 12 %).  PA_TUNE_DECODE_STAGING 1 keeps the per-head kernels.
+struct DecodeLaunch {
+  const void* kern;
+  int threads;      // per workgroup
+  bool per_item;    // one workgroup per item (whole-block) or per (item, kv head)
+  int kind;         // 0/1 per-head vector (q in registers / LDS), 2 per-head matrix-core,
+                    // 3 whole-block vector, 4 whole-block matrix-core
+};
 
-static hipError_t rowwise_kernel_for(bool bf16, int32_t D, int32_t G, const void** out) {
+static hipError_t decode_launch(bool bf16, int32_t D, int32_t G, int32_t Hkv, DecodeLaunch* out) {
+  const bool staged = tuning(PA_TUNE_DECODE_STAGING) != 1;
   if (use_mfma(bf16, D, G)) {
-    *out = rowwise_mfma_kernel_for(D, G);
+    const void* wb = staged ? rowwise_mfma_block_kernel_for(D, G, Hkv) : nullptr;
+    *out = wb ? DecodeLaunch{wb, 64 * Hkv, true, 4} : DecodeLaunch{rowwise_mfma_kernel_for(D, G), 64, false, 2};
     return hipSuccess;
+  }
+  if (bf16 && D == 128 && staged) {
+    if (const void* bk = block_kernel_for(G, Hkv)) {
+      *out = DecodeLaunch{bk, 64 * Hkv, true, 3};
+      return hipSuccess;
+    }
   }
   AttnArgs a{};
   a.bf16 = bf16;
@@ -806,58 +783,49 @@ static hipError_t rowwise_kernel_for(bool bf16, int32_t D, int32_t G, const void
   a.Hkv = 1;
   a.Hq = G;
   const void* kern = nullptr;
-  if (use_qlds(G)) {
+  const bool qlds = use_qlds(G);
+  if (qlds) {
     PA_SELECT_Q(rowwise_kernel, true)
   } else {
     PA_SELECT_Q(rowwise_kernel, false)
   }
-  *out = kern;
+  *out = DecodeLaunch{kern, 64, false, qlds ? 1 : 0};
   return hipSuccess;
 }
 
 hipError_t launch_rowwise(const AttnArgs& a, hipStream_t s) {
   if (a.ps.n_rw == 0) return hipSuccess;
+  DecodeLaunch dl{};
+  const hipError_t e = decode_launch(a.bf16, a.D, a.Hq / a.Hkv, a.Hkv, &dl);
+  if (e != hipSuccess) return e;
   AttnArgs args = a;
   void* params[] = {&args};
-  const int32_t G = a.Hq / a.Hkv;
-  if (use_block(a.bf16, a.D, G, a.Hkv))
-    return hipLaunchKernel(block_kernel_for(G, a.Hkv), dim3(a.ps.n_rw), dim3(64 * a.Hkv), params, 0, s);
-  const void* kern = nullptr;
-  const hipError_t e = rowwise_kernel_for(a.bf16, a.D, G, &kern);
-  if (e != hipSuccess) return e;
-  return hipLaunchKernel(kern, dim3(a.ps.n_rw, a.Hkv), dim3(64), params, 0, s);
+  const dim3 grid = dl.per_item ? dim3(a.ps.n_rw) : dim3(a.ps.n_rw, a.Hkv);
+  return hipLaunchKernel(dl.kern, grid, dim3(dl.threads), params, 0, s);
 }
 
 int64_t rowwise_round_slots(bool bf16, int32_t D, int32_t G, int32_t Hkv) {
   // wave slots of one round of the split-K grid: the kernel's occupancy per
   // compute unit in waves (workgroups times their waves: Hkv for the
-  // whole-block kernel, one otherwise), at most 8 (two per SIMD), times the
+  // whole-block kernels, one otherwise), at most 8 (two per SIMD), times the
   // compute units; cached per configuration.  A grid that fits in one round
   // streams faster with about 8 waves per compute unit than with the 12 the
   // per-head kernel could hold (measured on 64 contexts of 512..4096 keys:
   // 107 against 116 us; fewer concurrent K/V streams per HBM channel)
-  static thread_local int64_t cache[2][2][9][4][4] = {};
+  static thread_local int64_t cache[2][2][9][5][4] = {};
   if (G < 1 || G > 8 || Hkv < 1) return 0;
-  const bool blk = use_block(bf16, D, G, Hkv);
-  const int ki = blk ? 3 : (use_mfma(bf16, D, G) ? 2 : (use_qlds(G) ? 1 : 0));
-  const int hi = blk ? 31 - __builtin_clz((unsigned)Hkv) : 0;   // Hkv in {1, 2, 4, 8} there
-  int64_t& c = cache[bf16 ? 1 : 0][D == 128 ? 1 : 0][G][ki][hi];
+  DecodeLaunch dl{};
+  if (decode_launch(bf16, D, G, Hkv, &dl) != hipSuccess || dl.kern == nullptr) return 0;
+  const int hi = dl.per_item ? 31 - __builtin_clz((unsigned)Hkv) : 0;   // Hkv in {1, 2, 4, 8} there
+  int64_t& c = cache[bf16 ? 1 : 0][D == 128 ? 1 : 0][G][dl.kind][hi];
   if (c == 0) {
-    const void* kern = nullptr;
-    int threads = 64;
-    if (blk) {
-      kern = block_kernel_for(G, Hkv);
-      threads = 64 * Hkv;
-    } else if (rowwise_kernel_for(bf16, D, G, &kern) != hipSuccess) {
-      return 0;
-    }
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, 0) != hipSuccess || cus <= 0 ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, dl.kern, dl.threads, 0) != hipSuccess || cus <= 0 ||
         per_cu <= 0)
       return 0;
-    c = (int64_t)cus * std::min(per_cu * (threads / 64), 8);
+    c = (int64_t)cus * std::min(per_cu * (dl.threads / 64), 8);
   }
   return c;
 }

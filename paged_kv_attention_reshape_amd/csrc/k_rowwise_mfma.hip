@@ -40,6 +40,8 @@
 // loads in flight the compiler's vmcnt waits stay exact (mixing in LDS DMA
 // makes it wait for every outstanding load).  Partial results use the same
 // layout as the vector kernel's, so the merge pass is shared.
+#include <type_traits>
+
 #include "pa_internal.h"
 
 namespace pa {
@@ -335,6 +337,194 @@ __global__ void __launch_bounds__(64, 2) rowwise_mfma_kernel(AttnArgs a) {
   }
 }
 
+
+// Whole-block form (head_dim 128): one workgroup of HKV waves per item, wave
+// g computing kv head g, with the item's keys staged 16 tokens at a time as
+// slabs of all kv heads in an LDS double buffer (see slab_dma); reading each
+// block whole is what the whole-block vector kernel showed to stream faster.
+// Per 16-key slab and wave:
+//   S^T = K Q^T : four v_mfma_f32_16x16x32_bf16, A = K rows read from the
+//                 slab (lane: key li, d 32s + 8grp .. +7, one ds_read_b128),
+//                 B = the query heads as in the per-head kernel; lane l gets
+//                 the scores of head li for keys 4grp + r, r < 4.
+//   softmax     : over those 4 keys and the 4 lane groups; lazily raised max.
+//   O^T = V^T P^T: v_mfma_f32_16x16x16_bf16 per 16-wide d block, B = the
+//                 lane's own 4 probabilities (already in the B layout: key
+//                 slots 4grp + r, head li), A = V^T by one ds_read_b64_tr_b16
+//                 per block from the slab (row 4grp + li/4, d 16n + 4(li%4)
+//                 give lane (li, grp) the values V[4grp + r][16n + li]).
+// In the last, partial slab, keys at or past the partition end get score
+// -inf and their V values are zeroed (the slab may hold NaN there).
+template <int G, int HKV>
+__global__ void __launch_bounds__(64 * HKV) rowwise_mfma_block_kernel(AttnArgs a) {
+  constexpr int D = 128;
+  using Gm = MGeo<D>;
+  constexpr int ROWB = Gm::ROWB, CPR = Gm::CPR, KSTEPS = Gm::KSTEPS, NB = Gm::NB;
+  constexpr int SLAB = kSlabTokens * HKV * ROWB;
+  constexpr int DMA_PER_WAVE = SLAB / 1024 / HKV;
+  static_assert(CPR == 16 && DMA_PER_WAVE * 1024 * HKV == SLAB, "slab geometry");
+  static_assert(G >= 1 && G <= 16, "query heads per kv head must fit 16 MFMA columns");
+  __shared__ __attribute__((aligned(1024))) char k_lds0[SLAB];
+  __shared__ __attribute__((aligned(1024))) char k_lds1[SLAB];
+  __shared__ __attribute__((aligned(1024))) char v_lds0[SLAB];
+  __shared__ __attribute__((aligned(1024))) char v_lds1[SLAB];
+
+  const int lane = threadIdx.x & 63;
+  const int li = lane & 15, grp = lane >> 4;
+  const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int4 it = a.items_rw[blockIdx.x];
+  const int r = it.x;
+  if (r < 0 || r >= a.R) return;
+  const int t = it.y;
+  const int kb = it.z;
+  const int ke = it.w & 0x7FFFFFFF;
+  const bool direct = (it.w & kDirect) != 0;
+  const int slot = direct ? 0 : a.rw_slot[blockIdx.x];
+  if (ke <= kb) return;
+
+  // Q^T fragments (B operand of S^T = K Q^T): column li = query head g*G + li
+  u32x4_t qf[KSTEPS];
+  {
+    const int hh = li < G ? li : G - 1;
+    const char* qrow = static_cast<const char*>(a.query) + ((int64_t)t * a.Hq + g * G + hh) * ROWB + grp * 16;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
+      qf[s] = li < G ? *reinterpret_cast<const u32x4_t*>(qrow + s * 64) : u32x4_t{0, 0, 0, 0};
+  }
+
+  const int blk0 = kb / a.B;
+  const int nblk = (ke - 1) / a.B - blk0 + 1;
+  int myblk = 0;
+  if (lane < nblk) {
+    myblk = a.block_table[(int64_t)r * a.M + blk0 + lane];
+    myblk = myblk < 0 ? 0 : (myblk >= a.num_blocks ? a.num_blocks - 1 : myblk);
+  }
+  const char* kcache = static_cast<const char*>(a.kcache);
+  const char* vcache = static_cast<const char*>(a.vcache);
+  uint32_t dma_off[DMA_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < DMA_PER_WAVE; ++i)
+    dma_off[i] = slab_source_offset<HKV, CPR>((g * DMA_PER_WAVE + i) * 64 + lane);
+  auto slab_base = [&](int start) -> uint64_t {
+    const int blk = __builtin_amdgcn_readlane(myblk, start / a.B - blk0);
+    return ((uint64_t)blk * a.B + (start % a.B)) * (uint64_t)(HKV * ROWB);
+  };
+
+  // LDS offsets: K row li of this head, chunk 4s + grp; V^T reads of block n
+  // at row 4grp + li/4, logical chunk 2n + (li/2) % 2, byte 8 (li % 2)
+  int koff[KSTEPS];
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) koff[s] = (li * HKV + g) * ROWB + (((4 * s + grp) ^ slab_swz(li)) << 4);
+  const int vrow = 4 * grp + (li >> 2);
+  const int vbase = (vrow * HKV + g) * ROWB + (li & 1) * 8;
+  const int vsw = slab_swz(vrow);
+  const int vhalf = (li >> 1) & 1;
+
+  const float sl = a.scale_log2;
+  float m_run = kNegInf, l_run = 0.f;
+  f32x4_t o[NB];
+#pragma unroll
+  for (int n = 0; n < NB; ++n) o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto subtile = [&](const char* kbuf, const char* vbuf, int start) __attribute__((always_inline)) {
+    f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(kbuf + koff[s]);
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf),
+                                                   __builtin_bit_cast(bf16x8_t, qf[s]), sc, 0, 0, 0);
+    }
+    const int lim = ke - start - 4 * grp;   // element e is key 4grp + e of the slab
+    const bool tail = start + kSlabTokens > ke;
+    if (tail) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sc[e] = e < lim ? sc[e] : kNegInf;
+    }
+    float mx = max3f(sc[0], sc[1], fmaxf(sc[2], sc[3]));
+    mx = fmaxf(mx, xor16(mx));
+    mx = fmaxf(mx, xor32(mx)) * sl;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kSlack)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int n = 0; n < NB; ++n) o[n] *= alpha;
+    }
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
+    uint32_t pk[2];
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; e += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], sl, -m_use));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e + 1], sl, -m_use));
+      pk[e >> 1] = pack_bf16(p0, p1);
+      // the sum takes the bf16-rounded probabilities that p.v uses
+      psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[e >> 1]),
+                                             __builtin_bit_cast(bf16x2_t, 0x3F803F80u), psum, false);
+    }
+    l_run += psum;
+    const s16x4_t pf = __builtin_bit_cast(s16x4_t, make_uint2(pk[0], pk[1]));
+    lds_cptr vb = (lds_cptr)vbuf;
+    auto pv = [&](auto masked) __attribute__((always_inline)) {
+#pragma unroll
+      for (int n = 0; n < NB; ++n) {
+        s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t*)(vb + vbase + (((2 * n + vhalf) ^ vsw) << 4)));
+        if constexpr (decltype(masked)::value) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = e < lim ? v[e] : (short)0;
+        }
+        o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v, pf, o[n], 0, 0, 0);
+      }
+    };
+    if (tail) pv(std::true_type{});
+    else pv(std::false_type{});
+  };
+
+  const int n_tiles = (ke - kb + kSlabTokens - 1) / kSlabTokens;
+  slab_dma(kcache, vcache, slab_base(kb), dma_off, k_lds0, v_lds0, g);
+  for (int tile = 0; tile < n_tiles; tile += 2) {
+    // even slab: buffer 0 (its DMA done by every wave; buffer 1 no longer read)
+    __builtin_amdgcn_s_waitcnt(kWaitDma);
+    __syncthreads();
+    if (tile + 1 < n_tiles) slab_dma(kcache, vcache, slab_base(kb + 16 * (tile + 1)), dma_off, k_lds1, v_lds1, g);
+    subtile(k_lds0, v_lds0, kb + 16 * tile);
+    if (tile + 1 < n_tiles) {  // odd slab: buffer 1
+      __builtin_amdgcn_s_waitcnt(kWaitDma);
+      __syncthreads();
+      if (tile + 2 < n_tiles) slab_dma(kcache, vcache, slab_base(kb + 16 * (tile + 2)), dma_off, k_lds0, v_lds0, g);
+      subtile(k_lds1, v_lds1, kb + 16 * (tile + 1));
+    }
+  }
+
+  // ---- finish ------------------------------------------------------------------
+  float l_tot = l_run + xor16(l_run);
+  l_tot += xor32(l_tot);
+  if (li >= G) return;
+  const int hq = g * G + li;
+  if (direct) {
+    const float inv = 1.f / l_tot;
+    char* orow = static_cast<char*>(a.out) + ((int64_t)t * a.Hq + hq) * ROWB;
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      const int d = 16 * n + 4 * grp;
+      *reinterpret_cast<uint2*>(orow + d * 2) =
+          make_uint2(pack_bf16(o[n][0] * inv, o[n][1] * inv), pack_bf16(o[n][2] * inv, o[n][3] * inv));
+    }
+  } else {
+    float* op = a.o_part + ((int64_t)slot * a.Hq + hq) * D;
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+      *reinterpret_cast<float4*>(op + 16 * n + 4 * grp) = make_float4(o[n][0], o[n][1], o[n][2], o[n][3]);
+    if (grp == 0) {
+      float* mp = a.ml_part + ((int64_t)slot * a.Hq + hq) * 2;
+      mp[0] = m_run;
+      mp[1] = l_tot;
+    }
+  }
+}
+
 }  // namespace
 
 const void* rowwise_mfma_kernel_for(int32_t D, int32_t G) {
@@ -343,6 +533,21 @@ const void* rowwise_mfma_kernel_for(int32_t D, int32_t G) {
   if (D == 128 && G == 4) return (const void*)rowwise_mfma_kernel<128, 4>;
   if (D == 128 && G == 8) return (const void*)rowwise_mfma_kernel<128, 8>;
   return nullptr;
+}
+
+const void* rowwise_mfma_block_kernel_for(int32_t D, int32_t G, int32_t Hkv) {
+  if (D != 128 || (G != 4 && G != 8)) return nullptr;
+#define PA_MFMA_BLOCK_H(GG)                                                  \
+  switch (Hkv) {                                                             \
+    case 1: return (const void*)rowwise_mfma_block_kernel<GG, 1>;            \
+    case 2: return (const void*)rowwise_mfma_block_kernel<GG, 2>;            \
+    case 4: return (const void*)rowwise_mfma_block_kernel<GG, 4>;            \
+    case 8: return (const void*)rowwise_mfma_block_kernel<GG, 8>;            \
+    default: return nullptr;                                                 \
+  }
+  if (G == 4) { PA_MFMA_BLOCK_H(4) }
+  PA_MFMA_BLOCK_H(8)
+#undef PA_MFMA_BLOCK_H
 }
 
 }  // namespace pa

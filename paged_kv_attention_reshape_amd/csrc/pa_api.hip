@@ -146,6 +146,10 @@ bool rowwise_row_keys(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R
   return true;
 }
 
+// Steps with more split-K rows than this keep the keys-per-slot rule (the
+// simulation's host time grows with rows x candidate lengths).
+constexpr size_t kLptMaxRows = 4096;
+
 // Per-item cost of a split-K work item beyond its keys, in keys: prologue,
 // pipeline fill, partial write and its share of the merge (fitted to the
 // measured partition-length sweeps below).
@@ -195,7 +199,8 @@ int64_t lpt_makespan(const std::vector<int64_t>& row_keys, int64_t S, int64_t P,
 //    keys 640 keys (226 us; 1024 keys 276 us); 16 x 32K + 240 short contexts
 //    2048 (651 us; 1024 672 us, 512 727 us); C3's 512 decode rows 1024
 //    (1107 us; 512 1179 us) -- the simulation picks each of these.  Steps
-//    with more than 65536 split-K rows keep the keys per slot rounded down.
+//    with more than kLptMaxRows split-K rows keep the keys per slot rounded
+//    down.
 // Without the slot count: a power-of-two multiple of the unit (<= 1024 keys)
 // that gives the grid roughly 32 wavefronts per compute unit.
 int32_t choose_split(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R, int32_t M,
@@ -222,7 +227,7 @@ int32_t choose_split(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R,
     // at least a quarter of the keys per slot, so K / S <= 4 P (the workspace bound)
     const int64_t s_min = std::max(unit, cdiv64(cdiv64(rowwise_keys * Hkv, 4 * resident), unit) * unit);
     std::vector<int64_t> keys, rem, heap;
-    if (s_min < longest && rowwise_row_keys(h_qsl, h_seq_lens, R, M, ps, 65536, &keys)) {
+    if (s_min < longest && rowwise_row_keys(h_qsl, h_seq_lens, R, M, ps, kLptMaxRows, &keys)) {
       int64_t best = longest, best_t = lpt_makespan(keys, longest, P, &rem, &heap);
       for (int64_t S = longest - unit; S >= s_min; S -= unit) {
         const int64_t t = lpt_makespan(keys, S, P, &rem, &heap);

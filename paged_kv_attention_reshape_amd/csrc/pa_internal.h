@@ -330,10 +330,56 @@ struct RopeArgs {
 };
 hipError_t launch_rope_write_kv(const RopeArgs& a, bool bf16, int32_t D, bool neox, hipStream_t s);
 
+// ---- whole-block staging shared by the split-K kernels ----------------------
+// A 16-token sub-tile of a partition is one contiguous slab of the cache: 16
+// slots x Hkv kv heads x head row (block sizes are multiples of 16 and
+// sub-tiles start at multiples of 16, so the slab never crosses a block).  One
+// workgroup of Hkv waves stages it in LDS with 1-KB global -> LDS DMA
+// instructions (lane l of an instruction lands at LDS base + 16 l), and wave
+// g reads kv head g's rows from there.  Slab row (token j, head h) keeps its
+// 16-byte chunk c at position c ^ slab_swz(j), which spreads the rows of four
+// consecutive tokens over distinct bank groups; each DMA lane fetches the
+// logical chunk that belongs at its physical position.
+constexpr int kSlabTokens = 16;
+// cache-policy operand of global_load_lds: the nontemporal bit (nt)
+constexpr int kDmaNontemporal = 2;
+__device__ __forceinline__ int slab_swz(int j) { return ((j & 3) << 2) | ((j >> 2) & 3); }
+
+// Byte offset within a slab of the logical chunk that belongs at physical
+// 16-byte position q of the slab (CPR chunks per head row).
+template <int HKV, int CPR>
+__device__ __forceinline__ uint32_t slab_source_offset(int q) {
+  const int tok = q / (HKV * CPR);
+  return (uint32_t)(((q & ~(CPR - 1)) | ((q & (CPR - 1)) ^ slab_swz(tok))) * 16);
+}
+
+// Wave g's share of one slab's DMA, K and V: PER_WAVE instructions each,
+// source base (bytes from the cache start) `base`, lane offsets `off`.
+template <int PER_WAVE>
+__device__ __forceinline__ void slab_dma(const char* kcache, const char* vcache, uint64_t base,
+                                         const uint32_t (&off)[PER_WAVE], char* kd, char* vd, int g) {
+  typedef __attribute__((address_space(3))) void* lds_vptr;
+  typedef __attribute__((address_space(1))) void* glb_vptr;
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    __builtin_amdgcn_global_load_lds((glb_vptr)(kcache + base + off[i]), (lds_vptr)(kd + (g * PER_WAVE + i) * 1024),
+                                     16, 0, kDmaNontemporal);
+    __builtin_amdgcn_global_load_lds((glb_vptr)(vcache + base + off[i]), (lds_vptr)(vd + (g * PER_WAVE + i) * 1024),
+                                     16, 0, kDmaNontemporal);
+  }
+}
+
+// vmcnt(0), expcnt / lgkmcnt unconstrained: this wave's DMA into LDS is done
+constexpr int kWaitDma = 0x0F70;
+
 hipError_t launch_rowwise(const AttnArgs& a, hipStream_t s);
 // Matrix-core split-K kernel for bf16 caches (same items, partials and
 // launch shape as the vector kernel); nullptr where it has no instance.
 const void* rowwise_mfma_kernel_for(int32_t D, int32_t G);
+// Its whole-block form (one workgroup of Hkv waves per item, slabs of all kv
+// heads staged in LDS); nullptr where it has no instance.
+const void* rowwise_mfma_block_kernel_for(int32_t D, int32_t G, int32_t Hkv);
 // Wave slots of one round of the split-K grid on the current device for this
 // configuration (0 when the device cannot be queried).
 int64_t rowwise_round_slots(bool bf16, int32_t D, int32_t G, int32_t Hkv);

@@ -1,11 +1,12 @@
 """GPU parity of the split-K decode kernels against the fp64 oracle.
 
-bf16 caches with 8 query heads per kv head run the matrix-core kernel by
-default; bf16 with head_dim 128 and up to 4 query heads per kv head the
-whole-block vector kernel (one workgroup of Hkv waves per item, slabs of all
-kv heads staged in LDS); every other case the per-head vector kernel.  The
-decode_kernel and decode_staging tuning knobs select each of them where it
-has an instance.  All are checked on context lengths around every tile and
+bf16 caches with 8 query heads per kv head run a matrix-core kernel by
+default, bf16 with up to 4 query heads per kv head a vector kernel; with
+head_dim 128 both come in a whole-block form (one workgroup of Hkv waves per
+item, slabs of all kv heads staged in LDS), the default, and a per-head form
+(one wavefront per item and kv head); every other case runs the per-head
+vector kernel.  The decode_kernel and decode_staging tuning knobs select
+each of the four where it has an instance.  All are checked on context lengths around every tile and
 partition edge (1, 15..17, 31..33, partition lengths +-1), with head_dim 64
 and 128, 1, 2, 4 and 8 kv heads, block sizes 16, 32 and 48 (a size that is
 not a power of two: 16-key halves of a 32-key tile fall in different
@@ -40,10 +41,9 @@ SHAPES = [
     (8, 8, 128, 16),
 ]
 
-# kernel name -> tuning: matrix-core; vector (whole-block where it has an
-# instance, else per-head); per-head vector
-KERNELS = {"matrix": dict(decode_kernel=2), "vector": dict(decode_kernel=1),
-           "per-head": dict(decode_kernel=1, decode_staging=1)}
+# kernel name -> tuning (whole-block where it has an instance, else per-head)
+KERNELS = {"matrix": dict(decode_kernel=2), "matrix-per-head": dict(decode_kernel=2, decode_staging=1),
+           "vector": dict(decode_kernel=1), "per-head": dict(decode_kernel=1, decode_staging=1)}
 
 
 @pytest.mark.parametrize("kernel", list(KERNELS))

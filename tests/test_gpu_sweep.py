@@ -101,8 +101,8 @@ def test_wide_random_steps_match_oracle(i):
     say(f"wide random step {i}: worst abs err {err:.2e}")
 
 
-_KERNELS = {"matrix": dict(decode_kernel=2), "vector": dict(decode_kernel=1),
-            "per-head": dict(decode_kernel=1, decode_staging=1)}
+_KERNELS = {"matrix": dict(decode_kernel=2), "matrix-per-head": dict(decode_kernel=2, decode_staging=1),
+            "vector": dict(decode_kernel=1), "per-head": dict(decode_kernel=1, decode_staging=1)}
 
 
 @pytest.mark.parametrize("kernel", list(_KERNELS))
