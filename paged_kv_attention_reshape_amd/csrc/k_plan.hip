@@ -220,10 +220,14 @@ plan_kernel(const int32_t* __restrict__ qsl, const int32_t* __restrict__ seq_len
       return v;
     };
     auto excl = [&](int k, int rl) { return rl > 0 ? scan[k][rl - 1] : 0; };
-    // row-wise items
+    // row-wise items: staged for the longest-first sort, or (one-round grid,
+    // where the launch order does not matter) straight into the launch table
+    // with the plan-order index as partial slot
     for (int32_t idx = tid; idx < scan[0][n_here - 1]; idx += kPlanThreads) {
       const int rl = upper_bound(scan[0], n_here, idx);
-      emit_rowwise(view(rl), idx - excl(0, rl), carry[0] + idx, ps, rw_stage);
+      const int32_t k = carry[0] + idx;
+      emit_rowwise(view(rl), idx - excl(0, rl), k, ps, ps.sort_rw ? rw_stage : items_rw);
+      if (!ps.sort_rw && k < ps.n_rw) rw_slot[k] = k;
     }
     // chunk items
     for (int32_t idx = tid; idx < scan[1][n_here - 1]; idx += kPlanThreads) {
@@ -257,7 +261,7 @@ plan_kernel(const int32_t* __restrict__ qsl, const int32_t* __restrict__ seq_len
   // by this workgroup: the barrier makes them visible to all its threads.
   __syncthreads();
   const int32_t n_rw_items = min32(carry[0], ps.n_rw);
-  if (n_rw_items > 0) {
+  if (n_rw_items > 0 && ps.sort_rw) {
     auto rw_key = [&](const int4 it) {
       const int32_t keys = (it.w & 0x7FFFFFFF) - it.z;
       return kPlanThreads - 1 - min32(keys < 0 ? 0 : keys, kPlanThreads - 1);

@@ -341,6 +341,9 @@ pa_status make_plan(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R, 
   if (n_rw + n_parts > INT32_MAX / 2 || n_ck > INT32_MAX / 2 || n_mg > INT32_MAX / 2)
     return fail(PA_ERR_BAD_SHAPE, "step too large for one call");
   ps.n_rw = (int32_t)n_rw;
+  // the longest-first launch order only matters when the grid takes more
+  // than one round of the resident workgroups
+  ps.sort_rw = resident > 0 && n_rw * Hkv <= resident ? 0 : 1;
   ps.n_ck = (int32_t)n_ck;
   ps.n_mg = (int32_t)n_mg;
   ps.n_ck_parts = (int32_t)n_parts;

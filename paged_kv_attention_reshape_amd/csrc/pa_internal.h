@@ -59,6 +59,8 @@ struct PlanShape {
   int32_t TQ;            // chunk tile tokens
   int32_t MT;            // tokens per chunk merge record
   int32_t SEG;           // chunk key-segment length, multiple of 64
+  int32_t sort_rw;       // 1: row-wise items go to the launch order longest first
+                         // (0 when the split-K grid fits in one round)
   // exact totals for this step (host mirrors); capacities of the tables
   int32_t n_rw;          // row-wise items (= row-wise partial slots)
   int32_t n_ck;          // chunk items
