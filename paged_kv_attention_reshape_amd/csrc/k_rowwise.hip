@@ -812,16 +812,24 @@ int64_t rowwise_round_slots(bool bf16, int32_t D, int32_t G, int32_t Hkv) {
   // streams faster with about 8 waves per compute unit than with the 12 the
   // per-head kernel could hold (measured on 64 contexts of 512..4096 keys:
   // 107 against 116 us; fewer concurrent K/V streams per HBM channel)
+  // (per thread: the current device of the calling thread, the last device
+  // seen and its entries; another device clears them)
   static thread_local int64_t cache[2][2][9][5][4] = {};
+  static thread_local int cache_dev = -1;
   if (G < 1 || G > 8 || Hkv < 1) return 0;
   DecodeLaunch dl{};
   if (decode_launch(bf16, D, G, Hkv, &dl) != hipSuccess || dl.kern == nullptr) return 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev != cache_dev) {
+    std::fill(&cache[0][0][0][0][0], &cache[0][0][0][0][0] + sizeof(cache) / sizeof(int64_t), int64_t{0});
+    cache_dev = dev;
+  }
   const int hi = dl.per_item ? 31 - __builtin_clz((unsigned)Hkv) : 0;   // Hkv in {1, 2, 4, 8} there
   int64_t& c = cache[bf16 ? 1 : 0][D == 128 ? 1 : 0][G][dl.kind][hi];
   if (c == 0) {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, dl.kern, dl.threads, 0) != hipSuccess || cus <= 0 ||
         per_cu <= 0)
       return 0;

@@ -150,40 +150,6 @@ bool rowwise_row_keys(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R
 // simulation's host time grows with rows x candidate lengths).
 constexpr size_t kLptMaxRows = 4096;
 
-// Per-item cost of a split-K work item beyond its keys, in keys: prologue,
-// pipeline fill, partial write and its share of the merge (fitted to the
-// measured partition-length sweeps below).
-constexpr int64_t kItemOverheadKeys = 128;
-
-// Makespan (in keys) of longest-processing-time list scheduling of the split-K
-// items at partition length S on P item slots: the hardware dispatches the
-// workgroups in launch order, which the planner sorts longest first, onto
-// whichever slot frees first.  A row of k keys makes floor((k-1)/S) full
-// items and one remainder; the full items, the longest, are dealt first and
-// spread evenly (the slots are then loaded q or q + 1 times), the remainders
-// follow longest first, each onto the least-loaded slot.
-int64_t lpt_makespan(const std::vector<int64_t>& row_keys, int64_t S, int64_t P, std::vector<int64_t>* rem,
-                     std::vector<int64_t>* heap) {
-  rem->clear();
-  int64_t full = 0;
-  for (const int64_t k : row_keys) {
-    const int64_t n = (k + S - 1) / S;
-    full += n - 1;
-    rem->push_back(k - (n - 1) * S + kItemOverheadKeys);
-  }
-  std::sort(rem->begin(), rem->end(), std::greater<int64_t>());
-  const int64_t cost = S + kItemOverheadKeys;
-  heap->assign((size_t)P, (full / P) * cost);
-  for (int64_t i = 0; i < full % P; ++i) (*heap)[(size_t)i] += cost;
-  std::make_heap(heap->begin(), heap->end(), std::greater<int64_t>());
-  for (const int64_t c : *rem) {
-    std::pop_heap(heap->begin(), heap->end(), std::greater<int64_t>());
-    heap->back() += c;
-    std::push_heap(heap->begin(), heap->end(), std::greater<int64_t>());
-  }
-  return *std::max_element(heap->begin(), heap->end());
-}
-
 // Row-wise partition length: a multiple of lcm(64, B), at most 64 blocks (one
 // block id per lane of the wavefront) and 2048 keys.  With the round's wave
 // slots known (resident = min(occupancy, 8) waves per compute unit x compute
@@ -228,9 +194,9 @@ int32_t choose_split(const int32_t* h_qsl, const int32_t* h_seq_lens, int32_t R,
     const int64_t s_min = std::max(unit, cdiv64(cdiv64(rowwise_keys * Hkv, 4 * resident), unit) * unit);
     std::vector<int64_t> keys, rem, heap;
     if (s_min < longest && rowwise_row_keys(h_qsl, h_seq_lens, R, M, ps, kLptMaxRows, &keys)) {
-      int64_t best = longest, best_t = lpt_makespan(keys, longest, P, &rem, &heap);
+      int64_t best = longest, best_t = pa::lpt_makespan(keys, longest, P, &rem, &heap);
       for (int64_t S = longest - unit; S >= s_min; S -= unit) {
-        const int64_t t = lpt_makespan(keys, S, P, &rem, &heap);
+        const int64_t t = pa::lpt_makespan(keys, S, P, &rem, &heap);
         if (t < best_t) { best = S; best_t = t; }
       }
       return (int32_t)best;

@@ -4,6 +4,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <functional>
+#include <vector>
+
 #include "pa.h"
 
 namespace pa {
@@ -236,6 +240,42 @@ __host__ __device__ inline ReqCounts request_counts(int32_t q, int32_t L, const 
     }
   }
   return n;
+}
+
+// ---- split-K partition length: simulated launch schedule (host) ------------
+// Per-item cost of a split-K work item beyond its keys, in keys: prologue,
+// pipeline fill, partial write and its share of the merge (fitted to measured
+// partition-length sweeps on MI355X).
+constexpr int64_t kItemOverheadKeys = 128;
+
+// Makespan (in keys) of longest-processing-time list scheduling of the split-K
+// items at partition length S on P item slots: the hardware dispatches the
+// workgroups in launch order, which the planner sorts longest first, onto
+// whichever slot frees first.  A row of k keys makes ceil(k / S) - 1 full
+// items and one remainder; the full items, the longest, are dealt first and
+// spread evenly (the slots are then loaded q or q + 1 times), the remainders
+// follow longest first, each onto the least-loaded slot.  rem and heap are
+// scratch vectors.
+inline int64_t lpt_makespan(const std::vector<int64_t>& row_keys, int64_t S, int64_t P,
+                            std::vector<int64_t>* rem, std::vector<int64_t>* heap) {
+  rem->clear();
+  int64_t full = 0;
+  for (const int64_t k : row_keys) {
+    const int64_t n = (k + S - 1) / S;
+    full += n - 1;
+    rem->push_back(k - (n - 1) * S + kItemOverheadKeys);
+  }
+  std::sort(rem->begin(), rem->end(), std::greater<int64_t>());
+  const int64_t cost = S + kItemOverheadKeys;
+  heap->assign((size_t)P, (full / P) * cost);
+  for (int64_t i = 0; i < full % P; ++i) (*heap)[(size_t)i] += cost;
+  std::make_heap(heap->begin(), heap->end(), std::greater<int64_t>());
+  for (const int64_t c : *rem) {
+    std::pop_heap(heap->begin(), heap->end(), std::greater<int64_t>());
+    heap->back() += c;
+    std::push_heap(heap->begin(), heap->end(), std::greater<int64_t>());
+  }
+  return *std::max_element(heap->begin(), heap->end());
 }
 
 struct WorkspaceLayout {

@@ -11,9 +11,15 @@
 // than one segment takes nseg * TQ partial slots, in tile order, and one
 // merge record per MT tokens.
 //
+// It also checks lpt_makespan (the simulated longest-first schedule behind
+// the split-K partition rule) against the same schedule written out item by
+// item.
+//
 // Prints "ok <cases>" and exits 0, or prints the first mismatch and exits 1.
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
+#include <functional>
 #include <vector>
 
 #include "pa_internal.h"
@@ -149,8 +155,39 @@ static bool check_chunk(int32_t c, int32_t q, int32_t TQ, int32_t SEG, int32_t M
   return true;
 }
 
+// Longest-processing-time list scheduling written out: every item of every
+// row (full items of S keys, one remainder) sorted longest first, each placed
+// on the least-loaded of P slots; each costs its keys + kItemOverheadKeys.
+static int64_t lpt_brute(const std::vector<int64_t>& rows, int64_t S, int64_t P) {
+  std::vector<int64_t> items;
+  for (const int64_t k : rows)
+    for (int64_t kb = 0; kb < k; kb += S) items.push_back((k - kb < S ? k - kb : S) + kItemOverheadKeys);
+  std::sort(items.begin(), items.end(), std::greater<int64_t>());
+  std::vector<int64_t> load((size_t)P, 0);
+  for (const int64_t c : items) *std::min_element(load.begin(), load.end()) += c;
+  return *std::max_element(load.begin(), load.end());
+}
+
 int main() {
   long cases = 0;
+  // simulated launch schedule of the split-K partition rule
+  {
+    srand(777);
+    std::vector<int64_t> rem, heap;
+    for (int k = 0; k < 400; ++k) {
+      const int64_t P = 1 + rand() % 300;
+      const int64_t S = 64 * (1 + rand() % 32);
+      std::vector<int64_t> rows((size_t)(1 + rand() % 200));
+      for (auto& r : rows) r = 1 + rand() % (k % 2 ? 5000 : 40000);
+      const int64_t want = lpt_brute(rows, S, P), got = lpt_makespan(rows, S, P, &rem, &heap);
+      if (want != got) {
+        std::printf("lpt mismatch: P=%lld S=%lld rows=%zu: %lld vs %lld\n", (long long)P, (long long)S,
+                    rows.size(), (long long)got, (long long)want);
+        return 1;
+      }
+      ++cases;
+    }
+  }
   // exhaustive small ranges
   for (int32_t S : {64, 128, 192, 1024})
     for (int32_t c = 0; c <= 300; c += 7)
