@@ -463,11 +463,13 @@ def pool_rotation(d, rotate_bytes=MALL_ROTATE_BYTES):
         [(d["key_cache"].clone(), d["value_cache"].clone()) for _ in range(n - 1)]
 
 
-def decode_workload(name: str, dev, steps: int, warmup: int):
-    """One of the decode-only configurations (C2, C4) timed like the main
-    step: write_kv + attention per step over rotated pool copies, HIP events
-    recorded by the library between its launches; returns the split-K and
-    merge times and the decode roofline (algorithmic bytes / time)."""
+def config_workload(name: str, dev, steps: int, warmup: int):
+    """Another configuration (C1, C2, C4) timed like the main step: write_kv
+    + attention per step over rotated pool copies, HIP events recorded by the
+    library between its launches.  For the bf16 decode configurations (C2,
+    C4): the split-K and merge times and the decode roofline (algorithmic
+    bytes / time); C1 (fp32, a correctness configuration) reports its times
+    only."""
     import numpy as np
     import torch
     import paged_kv_attention_reshape_amd as pa
@@ -476,8 +478,9 @@ def decode_workload(name: str, dev, steps: int, warmup: int):
     d = spec.device_inputs(device=dev)
     pools = pool_rotation(d)
     out = torch.empty_like(d["query"])
+    dt = pa.PA_BF16 if spec.dtype == "bf16" else pa.PA_F32
     ws = pa.alloc_workspace(pa.attention_workspace_size(spec.query_start_loc, spec.seq_lens, spec.Hq, spec.Hkv,
-                                                        spec.D, spec.B, pa.PA_BF16), dev)
+                                                        spec.D, spec.B, dt), dev)
     slots = torch.from_numpy(pa.build_step_metadata(spec.query_lens, spec.num_computed, spec.block_table,
                                                     spec.B, spec.num_blocks)[2]).to(dev)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
@@ -505,17 +508,22 @@ def decode_workload(name: str, dev, steps: int, warmup: int):
         one(i, ev[i])
     torch.cuda.synchronize()
     rw = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e3
+    ck = float(np.mean([e[2].elapsed_time(e[3]) for e in ev])) * 1e3
     mg = float(np.mean([e[3].elapsed_time(e[4]) for e in ev])) * 1e3
     pl = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
+    res = {"workload": configs.WORKLOADS[name], "requests": spec.R, "tokens": spec.T, "dtype": spec.dtype,
+           "pool_copies": len(pools), "ms_per_step": round(t0.elapsed_time(t1) / steps, 4),
+           "kernel_us": {"plan": round(pl, 2), "rowwise": round(rw, 2), "chunk": round(ck, 2), "merge": round(mg, 2)}}
+    if spec.dtype != "bf16":
+        res["note"] = "correctness configuration: times only, no roofline claim"
+        return res
     db = spec.decode_bytes()
     rw_gbs = db / (rw * 1e-6) / 1e9
     val = db / ((rw + mg) * 1e-6) / 1e9
-    return {"workload": configs.WORKLOADS[name], "requests": spec.R, "decode_bytes_per_step": db,
-            "pool_copies": len(pools), "ms_per_step": round(t0.elapsed_time(t1) / steps, 4),
-            "kernel_us": {"plan": round(pl, 2), "rowwise": round(rw, 2), "merge": round(mg, 2)},
-            "decode_gbs": round(val, 1), "decode_frac_hbm": round(val / HBM_PEAK_GBS, 4),
-            "roofline": {"kernel": decode_kernel_name(spec), "bound": "hbm", "achieved": round(rw_gbs, 1),
-                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(rw_gbs / HBM_PEAK_GBS, 4)}}
+    res.update({"decode_bytes_per_step": db, "decode_gbs": round(val, 1), "decode_frac_hbm": round(val / HBM_PEAK_GBS, 4),
+                "roofline": {"kernel": decode_kernel_name(spec), "bound": "hbm", "achieved": round(rw_gbs, 1),
+                             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(rw_gbs / HBM_PEAK_GBS, 4)}})
+    return res
 
 
 def swap_beside_steps(dev, step, n_steps: int, stream, path: str = "engines"):
@@ -871,7 +879,7 @@ def main():
     serving = serving_measurement(dev) if args.serving else None
     extra = None
     if args.extra and args.workload == "c3":
-        extra = {n: decode_workload(n, dev, args.steps, args.warmup) for n in ("c2", "c4")}
+        extra = {n: config_workload(n, dev, args.steps, args.warmup) for n in ("c1", "c2", "c4")}
 
     # host scheduler / block allocator (C++) on the serving trace
     sched_t = scheduler_timing(product=True)
@@ -940,7 +948,7 @@ def main():
         "scheduler": sched_t,
         "swap_roundtrip": swap,
         "serving_trace": serving,
-        "decode_configs": extra,
+        "other_configs": extra,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
