@@ -9,12 +9,15 @@
 // absolute position p is key p ("Chunked Prefill 与 Preemption", equation
 // M_{i,j}); the plan gives each item its key range [kb, ke).
 //
-// MI355X design (no atomics, so results are deterministic).  Two kernels share
-// one sub-tile of math.  The whole-block kernel (bf16, head_dim 128, GQA
-// groups up to 4: the default there) gives an item one workgroup of Hkv
-// waves and stages each 16-token slab of all kv heads in LDS by DMA; the
-// per-head kernel (every other case) gives each (item, kv head) one
-// wavefront that loads its rows itself.  In both, per wave and kv head:
+// MI355X design (no atomics, so results are deterministic).  The vector-ALU
+// split-K kernels live here and share one sub-tile of math; the matrix-core
+// ones (8 query heads per kv head) are in k_rowwise_mfma.hip, and
+// decode_launch below picks among the four.  The whole-block vector kernel
+// (bf16, head_dim 128, GQA groups up to 4: the default there) gives an item
+// one workgroup of Hkv waves and stages each 16-token slab of all kv heads in
+// LDS by DMA; the per-head kernel (every other case) gives each (item, kv
+// head) one wavefront that loads its rows itself.  In both, per wave and kv
+// head:
 //   * the G query heads that share kv head g are processed together, so every
 //     K/V byte is read from HBM exactly once per item;
 //   * q.k: lanes are (token j, quarter c) pairs, 16 tokens per sub-tile; each
@@ -35,8 +38,6 @@
 //     pattern goes from about 5.8 to 6.2 TB/s with the hint, the whole-block
 //     one from 5.9 to 6.4).
 // fp32 caches use the per-head structure with plain FMAs.
-#include <stdlib.h>
-
 #include <algorithm>
 
 #include "pa_internal.h"

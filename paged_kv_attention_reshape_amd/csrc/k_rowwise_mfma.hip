@@ -17,7 +17,11 @@
 // about 40 vector instructions of softmax per wave, far below the time the
 // tile's 16 KB take to arrive.
 //
-// One wavefront per (row, key partition, kv head); lane l = (grp = l / 16,
+// Two forms.  The whole-block form (the default with head_dim 128 and 1, 2,
+// 4 or 8 kv heads; rowwise_mfma_block_kernel below) gives an item one
+// workgroup of Hkv waves reading 16-key slabs of all kv heads from LDS.  The
+// per-head form (rowwise_mfma_kernel) gives each (row, key partition, kv head)
+// one wavefront that streams its own rows; lane l = (grp = l / 16,
 // li = l % 16):
 //   S^T = K Q^T : A = K rows of the tile straight from global memory (lane
 //                 holds key li of a 16-key half, d 32s + 8grp .. +7), B = the
