@@ -2,7 +2,8 @@
 allocate): through the C ABI, its outputs equal pa_attention's (which plans
 into a caller workspace) bit for bit on two calls in a row, the second with
 a smaller step, and a step that needs more than the static scratch is
-refused before anything runs."""
+refused before anything runs; C1-C4 and every step of the serving trace fit
+in the static scratch."""
 import numpy as np
 import pytest
 
@@ -78,3 +79,29 @@ def test_noalloc_fp32_and_oversize_refused():
         assert e.value.status_name == "PA_ERR_WORKSPACE_TOO_SMALL"
         assert "static scratch" in str(e.value)
     torch.cuda.synchronize()
+
+
+def test_static_scratch_covers_the_configurations_and_the_serving_trace():
+    """The exact workspace of C1-C4 and of every step of the 2048-request
+    serving trace, sized on this device (its occupancy sets the partition
+    lengths), fits in the static scratch, so those steps never need a
+    caller workspace.  Host sizing only; nothing is launched."""
+    import sys
+    import os
+    sys.path.insert(0, os.path.dirname(__file__))
+    import test_workspace_bound as wb
+    from workloads import serving_trace as st
+    torch.cuda.set_device(0)
+    sizes = {}
+    for name in ("c1", "c2", "c3", "c4"):
+        s = configs.BUILDERS[name]()
+        sizes[name] = wb._exact(s.query_lens, s.num_computed, s.Hq, s.Hkv, s.D, s.B, wb._dt(s.dtype))
+    cfg = st.TraceConfig()
+    worst = 0
+    for p in st.drive(pa.Scheduler(**st.scheduler_args(cfg)), cfg):
+        if p["sched"]:
+            ql, cp, _, _, _ = st.step_arrays(p, cfg.block_size)
+            worst = max(worst, wb._exact(ql, cp, 32, 8, 128, cfg.block_size, pa.PA_BF16))
+    sizes["serving trace (worst step)"] = worst
+    say("workspace MiB: " + ", ".join(f"{k} {v / 2**20:.1f}" for k, v in sizes.items()))
+    assert all(0 < v <= pa.NOALLOC_SCRATCH_BYTES for v in sizes.values()), sizes
