@@ -86,9 +86,6 @@ def test_static_scratch_covers_the_configurations_and_the_serving_trace():
     serving trace, sized on this device (its occupancy sets the partition
     lengths), fits in the static scratch, so those steps never need a
     caller workspace.  Host sizing only; nothing is launched."""
-    import sys
-    import os
-    sys.path.insert(0, os.path.dirname(__file__))
     import test_workspace_bound as wb
     from workloads import serving_trace as st
     torch.cuda.set_device(0)
